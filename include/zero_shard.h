@@ -1,0 +1,211 @@
+/* zero_shard.h -- C ABI of one data-parallel rank's partitioned mixed-precision
+ * optimizer step (ZeRO stage 1/2) on one AMD Instinct MI355X (gfx950).
+ *
+ * What the step computes (the pages on DeepSpeed ZeRO):
+ *   - model states are fp16/bf16 parameters and gradients plus fp32 master
+ *     weights, momentum and variance ("ZeRO 技术原理" section 3; "DeepSpeed ZeRO"
+ *     表格计算);
+ *   - the flattened, padded model is cut into N_d equal shards and rank r owns
+ *     and updates only shard r ("ZeRO 技术原理" 3.1.1 and 3.3.1;
+ *     "DeepSpeed ZeRO" ZeRO Stage 3 基本流程);
+ *   - the shard's gradient is the reduce-scatter of the ranks' gradients
+ *     ("DeepSpeed ZeRO" ZeRO Stage 2 基本思想); this library performs the local
+ *     reduction half on buffers already resident on the GPU;
+ *   - a nan/inf gradient skips the update entirely ("DeepSpeed ZeRO"
+ *     权重更新的触发条件);
+ *   - Adam updates the fp32 master, momentum and variance ("DeepSpeed ZeRO"
+ *     ZeRO Stage 1, 以 AdaW 为例), here with bias correction, decoupled weight
+ *     decay and global-norm clipping;
+ *   - the updated fp32 slice is written back in place into the 16-bit
+ *     parameters for the all-gather that follows ("DeepSpeed ZeRO" 具体训练步骤).
+ *
+ * Conventions
+ *   - Every call returns a zero_status_t; on failure zero_last_error() gives a
+ *     message (thread-local, valid until the next call on the same thread).
+ *   - Device memory is owned by the caller (parameters, gradients, fp32 state
+ *     and the workspace); the library owns only the host-side handle and never
+ *     frees caller memory.  All pointers given to zero_shard_init must stay
+ *     valid until zero_shard_destroy.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work
+ *     on it and return without waiting, except where a host_* output pointer is
+ *     non-NULL (the call then synchronises the stream) and for the query calls.
+ *   - One step is: zero_reduce_grads -> zero_check_overflow -> zero_grad_norm
+ *     -> zero_adam_step [-> zero_cast_params].  Calls out of that order return
+ *     ZERO_ESTATE and change nothing.
+ *   - Element counts and offsets are int64 (a 7.5e9-element model is fine).
+ *   - Calls on one handle must not overlap (one host thread, one stream at a
+ *     time); different handles are independent.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZERO_OK = 0,
+  ZERO_EINVAL = -1, /* bad argument: null pointer, size, dtype, alignment, rank count */
+  ZERO_EHIP = -3,   /* a HIP runtime call failed (message names it)                  */
+  ZERO_ESTATE = -4  /* call out of the step order                                    */
+} zero_status_t;
+
+typedef enum { ZERO_F16 = 1, ZERO_BF16 = 2 } zero_dtype_t;
+
+typedef struct zero_shard* zero_shard_t; /* opaque host handle */
+
+/* Description of the model and of this rank.  Host memory, read during the call. */
+typedef struct {
+  int32_t dp_size;            /* N_d >= 1                                                     */
+  int32_t dp_rank;            /* 0 <= dp_rank < N_d                                           */
+  int32_t dtype;              /* zero_dtype_t of the 16-bit parameters and gradients         */
+  int32_t align;              /* shard length is a multiple of this many elements; 0 -> 64;  */
+                              /* must be a multiple of 8                                      */
+  int64_t num_tensors;        /* T >= 1 tensors, flattened in this order                     */
+  const int64_t* numel;       /* host [T], each >= 0; psi = sum                               */
+  void* const* param16;       /* host [T] of device pointers, one per tensor, or NULL         */
+  void* flat_param16;         /* device [psi] flat 16-bit parameters, or NULL                 */
+                              /* (exactly one of param16 / flat_param16)                      */
+  const void* const* grad16;  /* host [T] of device pointers: the already-reduced 16-bit      */
+                              /* gradient per tensor, or NULL                                 */
+  const void* flat_grad16;    /* device [psi] already-reduced flat gradient, or NULL          */
+                              /* (at most one of grad16 / flat_grad16; used by                */
+                              /* zero_reduce_grads with n_ranks == 0)                         */
+} zero_shard_desc_t;
+
+/* Sizes of this rank's shard (zero_shard_plan / zero_shard_info). */
+typedef struct {
+  int64_t psi;               /* total parameters                                              */
+  int64_t shard_elems;       /* S: every rank's shard length (multiple of align)             */
+  int64_t shard_begin;       /* r * S: flat index of this rank's first element               */
+  int64_t valid_elems;       /* elements of [r*S, r*S + S) inside [0, psi)                    */
+  int64_t state_elems;       /* floats the caller allocates for each of master, m, v (and red) */
+  int64_t num_pieces;        /* tensor pieces the shard touches                               */
+  int64_t num_chunks;        /* work items of the kernels                                     */
+  int64_t workspace_bytes;   /* device workspace the caller allocates (256-byte aligned)      */
+  int64_t model_state_bytes; /* bytes this rank keeps for the method's model states:          */
+                             /* full 16-bit params and grads + 12 * state_elems (ZeRO-1 view) */
+} zero_shard_info_t;
+
+/* Caller-allocated device buffers, each 16-byte aligned. */
+typedef struct {
+  float* master;             /* [state_capacity] fp32 master weights                          */
+  float* m;                  /* [state_capacity] fp32 first moment                            */
+  float* v;                  /* [state_capacity] fp32 second moment                           */
+  float* red;                /* [state_capacity] fp32 reduced gradient; required only for     */
+                             /* zero_reduce_grads with n_ranks >= 2, else may be NULL         */
+  void* workspace;           /* [workspace_bytes], 256-byte aligned                           */
+  int64_t state_capacity;    /* floats allocated per state buffer (>= state_elems)            */
+  int64_t workspace_capacity;/* bytes allocated for the workspace (>= workspace_bytes)        */
+} zero_shard_bufs_t;
+
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+} zero_adam_hparams_t;
+
+/* Partition and sizes only; no GPU work.  psi = sum(numel); S = align *
+ * ceil(ceil(psi / N_d) / align); this rank owns flat [r*S, r*S + S) clipped to
+ * [0, psi) -- the flatten-and-pad partition of "DeepSpeed ZeRO" ZeRO Stage 3
+ * 基本流程 with start = partition size * rank as in "ZeRO 技术原理" 3.3.1.
+ * The fp32 state is laid out in tensor pieces, each placed so that it has the
+ * same 16-byte alignment as its 16-bit parameters (a few padding floats per
+ * piece), hence state_elems >= valid_elems.  EINVAL on a bad description. */
+zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* out);
+
+/* Builds the handle: copies the work table into the workspace, zeroes the
+ * state, sets the master to master_init (device fp32 [valid_elems], this
+ * shard in logical order) or, when master_init is NULL, to the exact fp32
+ * value of this shard's 16-bit parameters (the partition_fp16.copy().float()
+ * of "DeepSpeed ZeRO" ZeRO Stage 1); m = v = 0 and no step applied yet.
+ * Synchronises the stream before returning.  EINVAL on a bad description,
+ * null or misaligned buffers, or capacities below zero_shard_plan's sizes. */
+zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
+                              const float* master_init, void* stream, zero_shard_t* out);
+
+/* Gradient intake of one step: the local reduce, the unscale, and this rank's
+ * overflow flag and sum of squares, in one pass over the gradient.
+ *   n_ranks == 0: use the already-reduced gradient registered at init
+ *                 (grad16 or flat_grad16); rank_grads is ignored.
+ *   n_ranks == 1: rank_grads[0] is an already-reduced flat 16-bit gradient
+ *                 [psi] (the ZeRO-1 all-reduce result); only this rank's slice
+ *                 is read.  It must stay unchanged until zero_adam_step.
+ *   n_ranks == N_d >= 2: rank_grads[q] is rank q's flat 16-bit gradient [psi];
+ *                 this rank's slice is summed in fp32 in rank order
+ *                 g_0 + g_1 + ... + g_{N_d-1} (the local half of the
+ *                 reduce-scatter, "DeepSpeed ZeRO" ZeRO Stage 2) and the
+ *                 unscaled sum is kept in bufs.red.  N_d <= 64.
+ * u = gradient * inv_loss_scale (fp32); flag = any u not finite; sum of
+ * squares = sum of u*u in fp64.  rank_grads is a host array of device
+ * pointers.  EINVAL on bad n_ranks or null pointers; ESTATE if the previous
+ * step's cast is still pending. */
+zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks,
+                                float inv_loss_scale, void* stream);
+
+/* This rank's local overflow flag and fp64 sum of squares from the last
+ * zero_reduce_grads, for the caller's exchange with the other ranks.
+ * Synchronises the stream.  ESTATE before a zero_reduce_grads. */
+zero_status_t zero_local_stats(zero_shard_t h, int32_t* found_inf, double* sumsq, void* stream);
+
+/* Global overflow decision: this rank's flag OR other_ranks_found_inf (the
+ * other ranks' flags, combined by the caller).  If host_found_inf is non-NULL
+ * the stream is synchronised and the global flag stored there.  A set flag
+ * makes zero_adam_step and zero_cast_params change nothing ("DeepSpeed ZeRO"
+ * 权重更新的触发条件). */
+zero_status_t zero_check_overflow(zero_shard_t h, int32_t other_ranks_found_inf, int32_t* host_found_inf,
+                                  void* stream);
+
+/* Global L2 norm and clip: norm = sqrt(local sum of squares +
+ * other_ranks_sumsq); the clip coefficient is max_norm / (norm + 1e-6) when
+ * that is below 1, else 1; max_norm <= 0 disables clipping.  If host_norm is
+ * non-NULL the stream is synchronised and the norm stored there. */
+zero_status_t zero_grad_norm(zero_shard_t h, double other_ranks_sumsq, float max_norm, double* host_norm,
+                             void* stream);
+
+/* Adam on this rank's fp32 master, m and v ("DeepSpeed ZeRO" ZeRO Stage 1,
+ * 以 AdaW 为例), with bias correction and decoupled weight decay.  Unless the
+ * step is skipped: t += 1, beta^t advance as fp64 running products,
+ * bc = 1 - beta^t rounded to fp32, and per element (fp32, each operation
+ * rounded to nearest even, no fused multiply-add):
+ *   g = u * clip; m = b1 m + (1-b1) g; v = b2 v + (1-b2) g g;
+ *   w = w - lr * ((m / bc1) / (sqrt(v / bc2) + eps) + wd * w).
+ * The skip decision is read on the device; a skipped step writes nothing.
+ * fuse_cast != 0 also writes the 16-bit parameters in the same pass (then
+ * zero_cast_params is a no-op).  EINVAL on a null hparams pointer. */
+zero_status_t zero_adam_step(zero_shard_t h, const zero_adam_hparams_t* hp, int32_t fuse_cast, void* stream);
+
+/* In-place write-back p16 = round-to-nearest-even(master) of this rank's
+ * valid elements ("DeepSpeed ZeRO" 权重更新的触发条件, step 4: fp32 copied
+ * into fp16 in place); nothing outside the shard is touched, nothing at all
+ * after a skipped step.  No-op when the step fused the cast. */
+zero_status_t zero_cast_params(zero_shard_t h, void* stream);
+
+/* Plan sizes of an initialised handle. */
+zero_status_t zero_shard_info(zero_shard_t h, zero_shard_info_t* out);
+
+/* The state layout: for each piece p < min(num_pieces, cap), out[5p .. 5p+4] =
+ * {tensor index, offset in tensor, offset in shard (logical), offset in the
+ * state buffers, length}.  Host memory. */
+zero_status_t zero_shard_pieces(zero_shard_t h, int64_t* out, int64_t cap);
+
+/* Applied steps t, whether the last zero_adam_step skipped, and the global
+ * norm and clip coefficient it used.  Synchronises the stream. */
+zero_status_t zero_shard_query(zero_shard_t h, int64_t* t, int32_t* last_skipped, double* last_norm,
+                               float* last_clip, void* stream);
+
+/* Copies state buffer `which` (0 master, 1 m, 2 v, 3 red) of this shard into
+ * dst (device fp32 [valid_elems]) in logical order. */
+zero_status_t zero_export_state(zero_shard_t h, int32_t which, float* dst, void* stream);
+
+/* Frees the host handle (never caller memory). */
+zero_status_t zero_shard_destroy(zero_shard_t h);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* zero_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

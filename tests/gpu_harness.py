@@ -1,0 +1,211 @@
+"""Test harness: run the HIP path for every simulated rank on one GPU next to
+the oracle, on the same seeded inputs, and compare element by element.
+
+The exchange between ranks (OR of flags, sum of the other ranks' sums of
+squares in rank order) is done here on the host for both sides, exactly as
+oracle.step_ranks does it.
+"""
+import numpy as np
+import torch
+
+import oracle
+from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
+
+DEV = "cuda"
+
+
+def dev16(u16):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(DEV)
+
+
+def host16(t):
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+def ordered(bits_i32):
+    b = bits_i32.astype(np.int64)
+    return np.where(b >= 0, b, -(b & 0x7FFFFFFF))
+
+
+def ulp_diff32(a, b):
+    return np.abs(ordered(a.view(np.int32)) - ordered(b.view(np.int32)))
+
+
+def ulp_diff16(a, b):
+    a = a.astype(np.int64)
+    b = b.astype(np.int64)
+    oa = np.where(a & 0x8000, -(a & 0x7FFF), a)
+    ob = np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(oa - ob)
+
+
+def assert_f32_close(got, exp, what):
+    """Within 2 ulp or 1e-6 relative, element by element (NaN matches NaN)."""
+    got = np.asarray(got, np.float32)
+    exp = np.asarray(exp, np.float32)
+    assert got.shape == exp.shape, what
+    both_nan = np.isnan(got) & np.isnan(exp)
+    ulp = ulp_diff32(got, exp)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.abs(got.astype(np.float64) - exp) / np.maximum(np.abs(exp.astype(np.float64)), 1e-300)
+    ok = both_nan | (ulp <= 2) | (rel <= 1e-6)
+    bad = np.flatnonzero(~ok)
+    assert bad.size == 0, (f"{what}: {bad.size} of {got.size} differ; first at {bad[:5]}: "
+                           f"got {got[bad[:5]]} expected {exp[bad[:5]]}")
+    return int((ulp != 0).sum() - both_nan.sum())
+
+
+def assert_16_close(got, exp, what):
+    """16-bit values within 1 ulp (bit patterns; NaN matches NaN)."""
+    got = np.asarray(got, np.uint16)
+    exp = np.asarray(exp, np.uint16)
+    d = ulp_diff16(got, exp)
+    bad = np.flatnonzero(d > 1)
+    assert bad.size == 0, f"{what}: {bad.size} differ by more than 1 ulp; first at {bad[:5]}"
+    return int((d != 0).sum())
+
+
+class Layout:
+    """Where the 16-bit parameters and the registered gradient live on the device."""
+
+    def __init__(self, numel, per_tensor, misalign=(0,)):
+        self.numel = list(numel)
+        self.per_tensor = per_tensor
+        self.misalign = misalign  # element offsets cycled over the tensors
+
+    def make(self, flat_u16):
+        """Device storage holding flat_u16 (length psi): a flat tensor, or per-tensor
+        views (at the given element misalignments) into one allocation."""
+        if not self.per_tensor:
+            return dev16(flat_u16), None
+        offs, pos = [], 0
+        for k, n in enumerate(self.numel):
+            mis = self.misalign[k % len(self.misalign)]
+            pos = (pos + 63) // 64 * 64 + mis
+            offs.append(pos)
+            pos += n
+        store = torch.zeros(pos + 64, dtype=torch.int16, device=DEV)
+        views, start = [], 0
+        for k, n in enumerate(self.numel):
+            v = store[offs[k]:offs[k] + n]
+            v.copy_(dev16(flat_u16[start:start + n]))
+            views.append(v)
+            start += n
+        return store, views
+
+    @staticmethod
+    def flat_of(views_or_flat):
+        if isinstance(views_or_flat, list):
+            return np.concatenate([host16(v) for v in views_or_flat]) if views_or_flat else np.zeros(0, np.uint16)
+        return host16(views_or_flat)
+
+
+class Sim:
+    """N_d ranks of the HIP path plus the oracle, stepped together."""
+
+    def __init__(self, numel, nd, dtype, p16_full, master_full, grad_mode, per_tensor_params=False,
+                 param_misalign=(0,), grad_misalign=(0,), ranks=None):
+        self.numel, self.nd, self.dtype, self.grad_mode = list(numel), nd, dtype, grad_mode
+        self.psi = sum(numel)
+        self.ranks = list(range(nd)) if ranks is None else ranks
+        self.plans = [oracle.plan(numel, nd, r) for r in range(nd)]
+        self.begins = [p[2] for p in self.plans]
+        # oracle side: every rank (the exchange needs all of them)
+        self.ostates = []
+        for r in range(nd):
+            _, _, b, valid = self.plans[r]
+            mst = None if master_full is None else master_full[b:b + valid]
+            self.ostates.append(oracle.RankState(dtype, p16_full[b:b + valid], mst))
+        # GPU side
+        self.player = Layout(numel, per_tensor_params, param_misalign)
+        self.glayout = Layout(numel, grad_mode == "ragged", grad_misalign)
+        self.gstore, self.gviews = None, None
+        if grad_mode in ("ragged", "registered_flat"):
+            self.gstore, self.gviews = self.glayout.make(np.zeros(self.psi, np.uint16))
+        self.params, self.shards = {}, {}
+        for r in self.ranks:
+            store, views = self.player.make(p16_full)
+            self.params[r] = (store, views)
+            _, _, b, valid = self.plans[r]
+            mi = None
+            if master_full is not None:
+                mi = torch.from_numpy(np.ascontiguousarray(master_full[b:b + valid])).to(DEV)
+            grads = None
+            if grad_mode == "ragged":
+                grads = self.gviews
+            elif grad_mode == "registered_flat":
+                grads = self.gstore
+            self.shards[r] = ZeroShard(numel, nd, r, dtype, views if views is not None else store, grads=grads,
+                                       master_init=mi, with_red=(grad_mode == "reduce"))
+
+    def step(self, grads, inv, max_norm, hp, fuse=True, extra_found_inf=False):
+        """grads: list of flat uint16 arrays (N_d for 'reduce', else one)."""
+        res = oracle.step_ranks(self.ostates, grads, self.begins, inv, max_norm, hp, extra_found_inf)
+        if self.grad_mode == "reduce":
+            dg = [dev16(g) for g in grads]
+        elif self.grad_mode == "flat":
+            dg = [dev16(grads[0])]
+        else:
+            src = dev16(grads[0])
+            if self.gviews is not None:
+                start = 0
+                for v, n in zip(self.gviews, self.numel):
+                    v.copy_(src[start:start + n])
+                    start += n
+            else:
+                self.gstore.copy_(src)
+            dg = []
+        # every simulated rank's own flag and sum (others from the oracle when not simulated on the GPU)
+        loc = {}
+        for r in self.ranks:
+            self.shards[r].zero_reduce_grads(dg, inv)
+            loc[r] = self.shards[r].zero_local_stats()
+        for r in self.ranks:
+            flag_others = any((loc[q][0] if q in loc else res[q]["flag"]) for q in range(self.nd) if q != r)
+            flag_others = flag_others or extra_found_inf
+            ss_others = 0.0
+            for q in range(self.nd):
+                if q != r:
+                    ss_others = ss_others + (loc[q][1] if q in loc else res[q]["local_sumsq"])
+            s = self.shards[r]
+            gflag = s.zero_check_overflow(flag_others, sync=True)
+            norm = s.zero_grad_norm(ss_others, max_norm, sync=True)
+            s.zero_adam_step(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, fuse_cast=fuse)
+            if not fuse:
+                s.zero_cast_params()
+            q = s.query()
+            assert gflag == res[r]["skipped"] == q["skipped"], (r, gflag, res[r], q)
+            assert loc[r][0] == res[r]["flag"], (r, loc[r], res[r])
+            rel = abs(loc[r][1] - res[r]["local_sumsq"]) / max(res[r]["local_sumsq"], 1e-300)
+            if np.isfinite(res[r]["local_sumsq"]):
+                assert rel <= 1e-9, (r, loc[r][1], res[r]["local_sumsq"])
+            if np.isfinite(res[r]["norm"]):
+                assert abs(norm - res[r]["norm"]) <= 1e-6 * res[r]["norm"]
+                if not q["skipped"]:
+                    assert q["clip"] == res[r]["clip"], (r, q, res[r])
+            assert q["t"] == self.ostates[r].counters.t
+        return res
+
+    def compare(self):
+        """Every simulated rank's master, m, v and 16-bit slice against the oracle;
+        also checks nothing outside the rank's slice of its parameters moved."""
+        nonexact = 0
+        for r in self.ranks:
+            s, o = self.shards[r], self.ostates[r]
+            _, _, b, valid = self.plans[r]
+            nonexact += assert_f32_close(s.export("master").cpu().numpy(), o.w, f"rank {r} master")
+            nonexact += assert_f32_close(s.export("m").cpu().numpy(), o.m, f"rank {r} m")
+            nonexact += assert_f32_close(s.export("v").cpu().numpy(), o.v, f"rank {r} v")
+            store, views = self.params[r]
+            flat = Layout.flat_of(views if views is not None else store)
+            nonexact += assert_16_close(flat[b:b + valid], o.p16, f"rank {r} p16 slice")
+            self.check_outside(r, flat)
+        return nonexact
+
+    def check_outside(self, r, flat):
+        _, _, b, valid = self.plans[r]
+        if not hasattr(self, "p16_initial"):
+            return
+        init = self.p16_initial
+        assert (flat[:b] == init[:b]).all() and (flat[b + valid:] == init[b + valid:]).all(), \
+            f"rank {r} wrote outside its shard"

@@ -1,0 +1,233 @@
+"""Parity of the HIP path with the oracle, element by element (MI355X).
+
+Sizes span many chunks and ragged tails; every rank of the data-parallel group
+is simulated so the shard boundaries and the exchange are exercised.
+Tolerance (stated for the method): fp32 master/m/v within 2 ulp or 1e-6
+relative, 16-bit parameters within 1 ulp, flags and skip decisions and t
+exact, norm within 1e-6 relative (local sums of squares within 1e-9).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import recipes
+from tests.gpu_harness import Sim, dev16, host16
+
+pytestmark = pytest.mark.gpu
+F16, BF16 = oracle.F16, oracle.BF16
+
+
+@pytest.fixture(autouse=True)
+def _gpu(need_gpu):
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def hp_of(d):
+    return oracle.HParams(d["lr"], d["beta1"], d["beta2"], d["eps"], d["weight_decay"])
+
+
+def grads_for(w, step, psi, nranks):
+    return [synth.normal_16(psi, w.dtype, w.seed, synth.stream_id(synth.GRAD, q, step), 0, w.grad_sigma,
+                            zero_seed=w.seed if w.zero_mod else 0, zero_mod=w.zero_mod) for q in range(nranks)]
+
+
+def master_of(w, psi):
+    m = synth.normal_f32(psi, w.seed, synth.stream_id(synth.MASTER), 0, w.master_sigma)
+    return m, synth.normal_16(psi, w.dtype, w.seed, synth.stream_id(synth.MASTER), 0, w.master_sigma)
+
+
+# --------------------------------------------------------------------------
+# the tiny workload: 4 ranks, fp16, loss scale 1024, 5 steps, inf injected at step 2
+
+
+@pytest.mark.parametrize("bad,where,at_step", [
+    (np.inf, "own", 2), (-np.inf, "own", 2), (np.nan, "own", 2), (np.inf, "other", 2), (np.inf, "own", 1)])
+def test_tiny_workload_all_ranks(bad, where, at_step):
+    w = recipes.tiny()
+    psi = w.psi
+    master, p16 = master_of(w, psi)
+    sim = Sim(w.numel, w.nd, w.dtype, p16, master, "reduce")
+    sim.p16_initial = p16.copy()
+    hp = hp_of(w.hp)
+    S = sim.plans[0][1]
+    for step in range(1, w.steps + 1):
+        g = grads_for(w, step, psi, w.nd)
+        if step == at_step:
+            r_bad = 3 if where == "own" else 1
+            g[0][r_bad * S + 777] = oracle.encode16(F16, np.array([bad], np.float32))[0]
+        res = sim.step(g, 1.0 / w.loss_scale, w.max_norm, hp)
+        assert all(x["skipped"] == (step == at_step) for x in res)
+        sim.compare()
+    assert all(st.counters.t == w.steps - 1 for st in sim.ostates)
+
+
+# --------------------------------------------------------------------------
+# ragged per-tensor list with shard cuts inside rows
+
+
+@pytest.mark.parametrize("nd", [3, 7])
+@pytest.mark.parametrize("fuse", [True, False])
+def test_ragged_mini_all_ranks(nd, fuse):
+    w = recipes.ragged_mini(nd)
+    psi = w.psi
+    master, p16 = master_of(w, psi)
+    # at least one shard boundary falls strictly inside a row of a 2-D tensor
+    starts = np.cumsum([0] + w.numel)
+    cut_mid_row = False
+    for r in range(1, nd):
+        b = oracle.plan(w.numel, nd, r)[2]
+        k = int(np.searchsorted(starts, b, side="right") - 1)
+        if w.numel[k] > 256 and (b - starts[k]) % 256 != 0:
+            cut_mid_row = True
+    assert cut_mid_row
+    sim = Sim(w.numel, nd, w.dtype, p16, None, "ragged", per_tensor_params=True)
+    sim.p16_initial = p16.copy()
+    hp = hp_of(w.hp)
+    for step in range(1, w.steps + 1):
+        sim.step(grads_for(w, step, psi, 1), 1.0, w.max_norm, hp, fuse=fuse)
+        sim.compare()
+    # the layout reported by the library is the oracle's partition
+    for r in sim.ranks:
+        pieces = sim.shards[r].pieces()
+        _, _, b, valid = sim.plans[r]
+        exp = oracle.shard_pieces(w.numel, b, valid)
+        assert [(p[0], p[1], p[2], p[4]) for p in pieces] == exp
+
+
+# --------------------------------------------------------------------------
+# one already-reduced flat gradient (the ZeRO-1 path), fp16 with loss scale 2^16
+
+
+@pytest.mark.parametrize("nd,psi", [(5, 300_001), (2, 64 * 8192 + 3), (1, 77_777)])
+def test_flat_prereduced_all_ranks(nd, psi):
+    w = recipes.zero1_7p5b()
+    w.tensors = [("flat", psi)]
+    master, p16 = master_of(w, psi)
+    sim = Sim(w.numel, nd, w.dtype, p16, master, "flat")
+    sim.p16_initial = p16.copy()
+    hp = hp_of(w.hp)
+    for step in range(1, 4):
+        sim.step(grads_for(w, step, psi, 1), 1.0 / w.loss_scale, w.max_norm, hp)
+        sim.compare()
+
+
+@pytest.mark.parametrize("nd", [2, 3, 8, 11])
+def test_reduce_fan_in(nd):
+    """Local reduce with the specialised (2, 8) and the generic (3, 11) fan-ins."""
+    w = recipes.reduce8()
+    psi = 40_000 * nd + 13
+    w.tensors = [("flat", psi)]
+    master, p16 = master_of(w, psi)
+    sim = Sim(w.numel, nd, w.dtype, p16, master, "reduce", ranks=[0, nd - 1])
+    sim.p16_initial = p16.copy()
+    for step in range(1, 3):
+        sim.step(grads_for(w, step, psi, nd), 1.0, w.max_norm, hp_of(w.hp))
+        sim.compare()
+
+
+# --------------------------------------------------------------------------
+# edge cases
+
+
+def test_ranks_without_elements_and_tiny_tensors():
+    # psi below N_d * 64: the last ranks own nothing; tensors of 0, 1 and 7 elements
+    numel = [0, 1, 7, 50, 0, 3]
+    w = recipes.ragged_mini(5)
+    psi = sum(numel)
+    master, p16 = master_of(w, psi)
+    sim = Sim(numel, 5, BF16, p16, None, "ragged", per_tensor_params=True)
+    sim.p16_initial = p16.copy()
+    assert [p[3] for p in sim.plans] == [61, 0, 0, 0, 0]
+    for step in range(1, 3):
+        sim.step(grads_for(w, step, psi, 1), 1.0, 1.0, hp_of(w.hp))
+        sim.compare()
+
+
+@pytest.mark.parametrize("pmis,gmis", [((1, 3, 5, 7), (0,)), ((2,), (1,)), ((3,), (3,)), ((1, 2), (2, 1))])
+def test_misaligned_tensors(pmis, gmis):
+    """Per-tensor parameters and gradients starting at odd element offsets: the
+    kernels peel heads or fall back to one element per lane, same results."""
+    numel = [5000, 1, 8193, 64, 12345, 3]
+    w = recipes.ragged_mini(3)
+    psi = sum(numel)
+    master, p16 = master_of(w, psi)
+    sim = Sim(numel, 3, F16, p16, master, "ragged", per_tensor_params=True, param_misalign=pmis,
+              grad_misalign=gmis)
+    sim.p16_initial = p16.copy()
+    for step in range(1, 3):
+        sim.step(grads_for(w, step, psi, 1), 1.0, 1.0, hp_of(w.hp))
+        sim.compare()
+
+
+def test_extreme_values_and_clipping_off():
+    """Gradients at the fp16 extremes (subnormals, 65504) and clipping disabled."""
+    psi, nd = 70_000, 2
+    w = recipes.tiny()
+    master, p16 = master_of(w, psi)
+    vals = np.array([6e-8, -6e-8, 1e-7, 65504.0, -65504.0, 0.0, -0.0, 1.0, 3e-5], np.float32)
+    g = np.resize(oracle.encode16(F16, vals), psi)
+    g2 = np.resize(oracle.encode16(F16, vals[::-1].copy()), psi)
+    sim = Sim([psi], nd, F16, p16, master, "reduce")
+    sim.p16_initial = p16.copy()
+    sim.step([g, g2], 1.0, 0.0, hp_of(w.hp))
+    sim.compare()
+    sim.step([g2, g], 1.0 / 65536, 1e30, hp_of(w.hp))
+    sim.compare()
+
+
+def test_step_order_is_enforced():
+    from zero_partitioned_mixed_reduce_amd import ZeroError
+    from zero_partitioned_mixed_reduce_amd._abi import ZERO_ESTATE, ZERO_EINVAL
+    psi = 4096
+    w = recipes.tiny()
+    _, p16 = master_of(w, psi)
+    from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
+    params = dev16(p16)
+    s = ZeroShard([psi], 1, 0, F16, params)
+    g = dev16(grads_for(w, 1, psi, 1)[0])
+    with pytest.raises(ZeroError) as e:
+        s.zero_adam_step(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    assert e.value.status == ZERO_ESTATE
+    with pytest.raises(ZeroError) as e:
+        s.zero_reduce_grads([], 1.0)          # no registered gradient
+    assert e.value.status == ZERO_EINVAL
+    s.zero_reduce_grads([g], 1.0)
+    with pytest.raises(ZeroError):
+        s.zero_grad_norm(0.0, 1.0)            # check_overflow first
+    s.zero_check_overflow(False)
+    s.zero_grad_norm(0.0, 1.0)
+    s.zero_adam_step(1e-3, 0.9, 0.999, 1e-8, 0.0, fuse_cast=False)
+    with pytest.raises(ZeroError):
+        s.zero_reduce_grads([g], 1.0)         # cast pending
+    s.zero_cast_params()
+    s.zero_cast_params()                      # already done: no-op
+    s.zero_reduce_grads([g], 1.0)
+    assert s.query()["t"] == 1
+
+
+def test_statistics_are_deterministic():
+    psi = 3_000_000
+    w = recipes.gpt2_shard()
+    _, p16 = master_of(w, psi)
+    from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
+    s = ZeroShard([psi], 1, 0, BF16, dev16(p16))
+    g = dev16(grads_for(w, 1, psi, 1)[0])
+    vals = set()
+    for _ in range(10):
+        s.zero_reduce_grads([g], 1.0)
+        vals.add(s.zero_local_stats()[1])
+    assert len(vals) == 1
+
+
+def test_device_generator_matches_host_generator():
+    n = 5_000_003
+    t = torch.empty(n, dtype=torch.int16, device="cuda")
+    synth.gpu_normal_16(t, F16, 77, 5, first=123, sigma=3.0, zero_seed=9, zero_mod=100)
+    assert (host16(t) == synth.normal_16(n, F16, 77, 5, 123, 3.0, 9, 100)).all()
+    f = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.gpu_normal_f32(f, 77, 6, first=5, sigma=0.02)
+    assert (f.cpu().numpy().view(np.uint32) == synth.normal_f32(n, 77, 6, 5, 0.02).view(np.uint32)).all()

@@ -1,0 +1,110 @@
+"""Host side of the C ABI, on the CPU: the library loads, exports every symbol
+the header declares, and its partition and layout agree with the oracle's."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import zero_partitioned_mixed_reduce_amd as zpm
+from zero_partitioned_mixed_reduce_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "zero_shard.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:zero_status_t|const char\*)\s+(zero_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_step_calls():
+    names = header_functions()
+    for required in ("zero_shard_init", "zero_reduce_grads", "zero_check_overflow", "zero_grad_norm",
+                     "zero_adam_step", "zero_cast_params"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _abi.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+        assert name in _abi._PROTOS or name == "zero_last_error"
+
+
+def test_binding_exposes_same_names():
+    for name in header_functions():
+        assert hasattr(zpm, name), name
+
+
+def desc_for(numel, nd, r, dtype=_abi.ZERO_F16, base=1 << 20, per_tensor=False, grads=False, align=0):
+    """Description with fake (never dereferenced) 256-byte aligned device addresses."""
+    d = _abi.zero_shard_desc_t()
+    d.dp_size, d.dp_rank, d.dtype, d.align = nd, r, dtype, align
+    arr = (ctypes.c_int64 * len(numel))(*numel)
+    d.num_tensors = len(numel)
+    d.numel = ctypes.cast(arr, _abi.c_i64p)
+    keep = [arr]
+    if per_tensor:
+        addrs, a = [], base
+        for n in numel:
+            addrs.append(a)
+            a += (2 * n + 255) // 256 * 256 + 256
+        p = (ctypes.c_void_p * len(numel))(*addrs)
+        keep.append(p)
+        d.param16 = ctypes.cast(p, ctypes.POINTER(ctypes.c_void_p))
+        if grads:
+            g = (ctypes.c_void_p * len(numel))(*[x + (1 << 40) for x in addrs])
+            keep.append(g)
+            d.grad16 = ctypes.cast(g, ctypes.POINTER(ctypes.c_void_p))
+    else:
+        d.flat_param16 = base
+        if grads:
+            d.flat_grad16 = base + (1 << 40)
+    d._keep = keep
+    return d
+
+
+CASES = [[1 << 20], [5], [0, 3], [1000, 0, 37, 1], [123457, 99, 640001], [64 * 64 * 3 + 1]]
+
+
+@pytest.mark.parametrize("numel", CASES)
+@pytest.mark.parametrize("nd", [1, 2, 3, 7, 8, 64])
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_plan_matches_oracle(numel, nd, per_tensor):
+    for r in range(nd):
+        info = zpm.zero_shard_plan(desc_for(numel, nd, r, per_tensor=per_tensor))
+        psi, S, b, valid = oracle.plan(numel, nd, r)
+        assert (info.psi, info.shard_elems, info.shard_begin, info.valid_elems) == (psi, S, b, valid)
+        assert info.state_elems >= max(valid, 64) and info.state_elems % 64 == 0
+        assert info.model_state_bytes == 4 * psi + 12 * info.state_elems
+
+
+def test_zero1_7p5b_state_matches_page_formula():
+    from oracle.memory import model_state_bytes
+    full = zpm.zero_shard_plan(desc_for([7_500_000_000], 64, 0))
+    assert abs(full.model_state_bytes - model_state_bytes(1, 7.5e9, 64)) <= 12 * 64
+    last = zpm.zero_shard_plan(desc_for([7_500_000_000], 64, 63))
+    assert last.valid_elems == 7_500_000_000 - 63 * last.shard_elems
+    # the last rank's shard is short by the padding; its state follows its valid length
+    assert last.state_elems == (last.valid_elems + 63) // 64 * 64
+
+
+def test_errors_are_reported():
+    d = desc_for([100], 4, 4)
+    with pytest.raises(zpm.ZeroError) as e:
+        zpm.zero_shard_plan(d)
+    assert e.value.status == _abi.ZERO_EINVAL and "dp_rank" in str(e.value)
+    d = desc_for([100], 2, 0, dtype=3)
+    with pytest.raises(zpm.ZeroError):
+        zpm.zero_shard_plan(d)
+    d = desc_for([100], 2, 0, align=12)
+    with pytest.raises(zpm.ZeroError):
+        zpm.zero_shard_plan(d)
+    d = desc_for([100, -1], 2, 0)
+    with pytest.raises(zpm.ZeroError):
+        zpm.zero_shard_plan(d)
+    # null handles are rejected, not dereferenced
+    assert _abi.lib().zero_cast_params(None, None) == _abi.ZERO_EINVAL
+    assert "null handle" in zpm.zero_last_error()

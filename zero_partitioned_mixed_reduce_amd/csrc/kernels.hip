@@ -1,0 +1,668 @@
+// gfx950 kernels of the partitioned mixed-precision optimizer step.
+//
+// Every kernel walks the shard's chunk table with a persistent grid (block b
+// takes chunks b, b + G, b + 2G, ...).  Inside a chunk a block peels at most 3
+// leading elements, streams the body as 4-element quads -- 8-byte loads and
+// stores of 16-bit data, 16-byte loads and stores of fp32 data, each wave
+// covering 256 consecutive elements per quad slot so every memory instruction
+// is fully coalesced -- with U quads per lane in flight, then finishes a tail
+// of at most 3 elements.  Chunks whose streams are not co-aligned fall back to
+// one element per lane.  Per-element arithmetic is plain fp32 (compiled with
+// -ffp-contract=off and the default correctly rounded division and square
+// root), identical in the vector and scalar paths.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zs_internal.h"
+
+namespace zs {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// 16-bit formats
+
+template <int DT>
+__device__ __forceinline__ float dec16(uint32_t h) {
+  if constexpr (DT == ZERO_BF16) {
+    return __uint_as_float(h << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t enc16(float x) {
+  if constexpr (DT == ZERO_BF16) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // quiet NaN
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;                   // round to nearest even
+  } else {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);      // v_cvt_f16_f32, RNE
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4 dec16x4(u32x2 r) {
+  f32x4 o;
+  o.x = dec16<DT>(r.x & 0xFFFFu);
+  o.y = dec16<DT>(r.x >> 16);
+  o.z = dec16<DT>(r.y & 0xFFFFu);
+  o.w = dec16<DT>(r.y >> 16);
+  return o;
+}
+
+template <int DT>
+__device__ __forceinline__ u32x2 enc16x4(f32x4 w) {
+  u32x2 r;
+  r.x = enc16<DT>(w.x) | (enc16<DT>(w.y) << 16);
+  r.y = enc16<DT>(w.z) | (enc16<DT>(w.w) << 16);
+  return r;
+}
+
+__device__ __forceinline__ u32x2 ld16x4(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st16x4_nt(uint16_t* p, u32x2 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ f32x4 ld32x4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld32x4_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ void st32x4_nt(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
+__device__ __forceinline__ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Leading elements before a 16-bit pointer reaches an 8-byte boundary (0..3).
+__device__ __forceinline__ int head16(const uint16_t* p) { return (int)(((8u - ((uintptr_t)p & 7u)) & 7u) >> 1); }
+
+// ---------------------------------------------------------------------------
+// chunk driver
+
+template <int U, class Op>
+__device__ __forceinline__ void run_chunk(Op& op, int64_t len, int head, bool vec_ok) {
+  const int64_t tid = threadIdx.x;
+  if (!vec_ok) {
+    for (int64_t j = tid; j < len; j += kBlock) op.elem(j);
+    return;
+  }
+  if (head > len) head = (int)len;
+  if (tid < head) op.elem(tid);
+  const int64_t nq = (len - head) >> 2;  // whole quads in the body
+  int64_t q = tid;
+  for (; q + (U - 1) * kBlock < nq; q += U * kBlock) op.template quads<U>(head + 4 * q, 4 * kBlock);
+  for (; q < nq; q += kBlock) op.template quads<1>(head + 4 * q, 0);
+  const int64_t t0 = head + 4 * nq;
+  if (tid < len - t0) op.elem(t0 + tid);
+}
+
+// ---------------------------------------------------------------------------
+// deterministic block reductions (fixed butterfly, fixed cross-wave order)
+
+__device__ __forceinline__ double block_sum(double x, double* lds) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) lds[wave] = x;
+  __syncthreads();
+  double r = lds[0];
+  for (int w = 1; w < kBlock / 64; ++w) r += lds[w];
+  return r;
+}
+
+// Called by every block of a statistics pass with its partial sum and flag.
+// The last block to finish combines all partials in block order and publishes
+// the local sum of squares and flag; it then re-arms the completion counter.
+__device__ void finish_stats(double acc, int flag, DevScalars* sc, StatsPart* parts) {
+  __shared__ double lds[kBlock / 64];
+  __shared__ int is_last;
+  const double bsum = block_sum(acc, lds);
+  const int bflag = __syncthreads_or(flag);
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(&parts[blockIdx.x].sumsq_bits, (uint64_t)__double_as_longlong(bsum), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&parts[blockIdx.x].flag, (uint32_t)bflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(&sc->counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (prev == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  double s = 0.0;
+  int f = 0;
+  for (uint32_t b = threadIdx.x; b < gridDim.x; b += kBlock) {
+    s += __longlong_as_double(
+        (long long)__hip_atomic_load(&parts[b].sumsq_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    f |= (int)__hip_atomic_load(&parts[b].flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const double total = block_sum(s, lds);
+  const int tflag = __syncthreads_or(f);
+  if (threadIdx.x == 0) {
+    sc->local_sumsq = total;
+    sc->local_flag = tflag;
+    __hip_atomic_store(&sc->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// statistics pass over an already-reduced 16-bit gradient
+
+template <int DT>
+struct Stats16Op {
+  const uint16_t* g;
+  float inv;
+  double acc;
+  int flag;
+  __device__ __forceinline__ void add(float u) {
+    flag |= !__builtin_isfinite(u);
+    const double d = (double)u;
+    acc += d * d;
+  }
+  __device__ __forceinline__ void elem(int64_t j) { add(dec16<DT>(g[j]) * inv); }
+  template <int U>
+  __device__ __forceinline__ void quads(int64_t j, int64_t stride) {
+    u32x2 r[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) r[k] = ld16x4(g + j + k * stride);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const f32x4 x = dec16x4<DT>(r[k]);
+      add(x.x * inv);
+      add(x.y * inv);
+      add(x.z * inv);
+      add(x.w * inv);
+    }
+  }
+};
+
+struct StatsArgs {
+  const Chunk* chunks;
+  int64_t n_chunks;
+  const uint16_t* flat_g;  // flat [psi] gradient, or null to use chunk.g16
+  float inv;
+  DevScalars* sc;
+  StatsPart* parts;
+};
+
+template <int DT>
+__global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
+  Stats16Op<DT> op{nullptr, a.inv, 0.0, 0};
+  for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
+    const Chunk ch = a.chunks[c];
+    op.g = a.flat_g ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
+    run_chunk<4>(op, ch.len, head16(op.g), true);
+  }
+  finish_stats(op.acc, op.flag, a.sc, a.parts);
+}
+
+// ---------------------------------------------------------------------------
+// local reduce of N rank buffers (rank order, fp32) + unscale + statistics
+
+struct ReduceArgs {
+  const Chunk* chunks;
+  int64_t n_chunks;
+  const uint16_t* ranks[kMaxRanks];
+  int32_t n_ranks;
+  float inv;
+  float* red;
+  DevScalars* sc;
+  StatsPart* parts;
+};
+
+template <int DT, int NR>
+struct ReduceOp {
+  const ReduceArgs* a;
+  int64_t flat_off;
+  float* red;
+  float inv;
+  int nr;
+  double acc;
+  int flag;
+  __device__ __forceinline__ int nranks() const { return NR > 0 ? NR : nr; }
+  __device__ __forceinline__ float add(float u) {
+    flag |= !__builtin_isfinite(u);
+    const double d = (double)u;
+    acc += d * d;
+    return u;
+  }
+  __device__ __forceinline__ void elem(int64_t j) {
+    float r = dec16<DT>(a->ranks[0][flat_off + j]);
+    for (int q = 1; q < nranks(); ++q) r = r + dec16<DT>(a->ranks[q][flat_off + j]);
+    red[j] = add(r * inv);
+  }
+  template <int U>
+  __device__ __forceinline__ void quads(int64_t j, int64_t stride) {
+    f32x4 s[U];
+    if constexpr (NR > 0) {
+      u32x2 raw[NR][U];
+#pragma unroll
+      for (int q = 0; q < NR; ++q)
+#pragma unroll
+        for (int k = 0; k < U; ++k) raw[q][k] = ld16x4(a->ranks[q] + flat_off + j + k * stride);
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        s[k] = dec16x4<DT>(raw[0][k]);
+#pragma unroll
+        for (int q = 1; q < NR; ++q) s[k] = s[k] + dec16x4<DT>(raw[q][k]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < U; ++k) s[k] = dec16x4<DT>(ld16x4(a->ranks[0] + flat_off + j + k * stride));
+      for (int q = 1; q < nr; ++q)
+#pragma unroll
+        for (int k = 0; k < U; ++k) s[k] = s[k] + dec16x4<DT>(ld16x4(a->ranks[q] + flat_off + j + k * stride));
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      f32x4 u;
+      u.x = add(s[k].x * inv);
+      u.y = add(s[k].y * inv);
+      u.z = add(s[k].z * inv);
+      u.w = add(s[k].w * inv);
+      st32x4_nt(red + j + k * stride, u);
+    }
+  }
+};
+
+template <int DT, int NR>
+__global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
+  ReduceOp<DT, NR> op{&a, 0, nullptr, a.inv, a.n_ranks, 0.0, 0};
+  for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
+    const Chunk ch = a.chunks[c];
+    op.flat_off = ch.flat_off;
+    op.red = a.red + ch.state_off;
+    const int head = head16(a.ranks[0] + ch.flat_off);
+    bool ok = aligned(op.red + head, 16);
+    for (int q = 0; q < a.n_ranks; ++q) ok = ok && aligned(a.ranks[q] + ch.flat_off + head, 8);
+    run_chunk<2>(op, ch.len, head, ok);
+  }
+  finish_stats(op.acc, op.flag, a.sc, a.parts);
+}
+
+// ---------------------------------------------------------------------------
+// Adam with bias correction, decoupled weight decay, clip; optional fused cast
+
+struct AdamScalars {
+  float inv, clip, b1, b2, omb1, omb2, bc1, bc2, lr, eps, wd;
+};
+
+__device__ __forceinline__ void adam_elem(float u, float& w, float& m, float& v, const AdamScalars& s) {
+  const float g = u * s.clip;
+  const float mi = s.b1 * m + s.omb1 * g;
+  const float vi = s.b2 * v + s.omb2 * (g * g);
+  const float mh = mi / s.bc1;
+  const float vh = vi / s.bc2;
+  const float den = __builtin_sqrtf(vh) + s.eps;
+  const float upd = mh / den;
+  w = w - s.lr * (upd + s.wd * w);
+  m = mi;
+  v = vi;
+}
+
+enum { kGradFlat16 = 0, kGradChunk16 = 1, kGradRed = 2 };
+
+template <int DT, int GS, bool CAST>
+struct AdamOp {
+  const uint16_t* g16;
+  const float* gred;
+  float* w;
+  float* m;
+  float* v;
+  uint16_t* p16;
+  AdamScalars s;
+  __device__ __forceinline__ float grad(int64_t j) const {
+    if constexpr (GS == kGradRed) return gred[j];
+    else return dec16<DT>(g16[j]) * s.inv;
+  }
+  __device__ __forceinline__ void elem(int64_t j) {
+    float wj = w[j], mj = m[j], vj = v[j];
+    adam_elem(grad(j), wj, mj, vj, s);
+    w[j] = wj;
+    m[j] = mj;
+    v[j] = vj;
+    if constexpr (CAST) p16[j] = (uint16_t)enc16<DT>(wj);
+  }
+  template <int U>
+  __device__ __forceinline__ void quads(int64_t j, int64_t stride) {
+    f32x4 G[U], W[U], M[U], V[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int64_t o = j + k * stride;
+      if constexpr (GS == kGradRed) {
+        G[k] = ld32x4_nt(gred + o);
+      } else {
+        G[k] = dec16x4<DT>(ld16x4(g16 + o)) * s.inv;
+      }
+      W[k] = ld32x4_nt(w + o);
+      M[k] = ld32x4_nt(m + o);
+      V[k] = ld32x4_nt(v + o);
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float we = W[k][e], me = M[k][e], ve = V[k][e];
+        adam_elem(G[k][e], we, me, ve, s);
+        W[k][e] = we;
+        M[k][e] = me;
+        V[k][e] = ve;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int64_t o = j + k * stride;
+      st32x4_nt(w + o, W[k]);
+      st32x4_nt(m + o, M[k]);
+      st32x4_nt(v + o, V[k]);
+      if constexpr (CAST) st16x4_nt(p16 + o, enc16x4<DT>(W[k]));
+    }
+  }
+};
+
+struct AdamArgs {
+  const Chunk* chunks;
+  int64_t n_chunks;
+  const uint16_t* flat_g;  // kGradFlat16 source
+  const float* red;        // kGradRed source
+  float* master;
+  float* m;
+  float* v;
+  DevScalars* sc;
+  int32_t slot;            // slot to read; the other one receives this step's counters
+  int32_t other_flag;
+  double other_sumsq;
+  float max_norm;
+  float inv;
+  float lr, beta1, beta2, eps, wd;
+};
+
+// Step scalars, computed identically by every block from the device scalar
+// block and the call's arguments.  Returns the skip decision.
+__device__ __forceinline__ int step_scalars(const AdamArgs& a, AdamScalars& s, Slot& next, double& norm) {
+  const DevScalars* sc = a.sc;
+  const int skip = (sc->local_flag | a.other_flag) != 0;
+  norm = sqrt(sc->local_sumsq + a.other_sumsq);
+  float clip = 1.0f;
+  if (a.max_norm > 0.0f) {
+    const double c = (double)a.max_norm / (norm + 1e-6);
+    if (c < 1.0) clip = (float)c;
+  }
+  const Slot cur = sc->slot[a.slot];
+  next = cur;
+  if (!skip) {
+    next.t = cur.t + 1;
+    next.p1 = cur.p1 * (double)a.beta1;
+    next.p2 = cur.p2 * (double)a.beta2;
+  }
+  s.inv = a.inv;
+  s.clip = clip;
+  s.b1 = a.beta1;
+  s.b2 = a.beta2;
+  s.omb1 = 1.0f - a.beta1;
+  s.omb2 = 1.0f - a.beta2;
+  s.bc1 = (float)(1.0 - next.p1);
+  s.bc2 = (float)(1.0 - next.p2);
+  s.lr = a.lr;
+  s.eps = a.eps;
+  s.wd = a.wd;
+  return skip;
+}
+
+template <int DT, int GS, bool CAST>
+__global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
+  AdamScalars s;
+  Slot next;
+  double norm;
+  const int skip = step_scalars(a, s, next, norm);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.sc->slot[a.slot ^ 1] = next;
+    a.sc->norm = norm;
+    a.sc->clip = s.clip;
+    a.sc->skipped = skip;
+    a.sc->report_t = next.t;
+  }
+  if (skip) return;
+  AdamOp<DT, GS, CAST> op{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s};
+  for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
+    const Chunk ch = a.chunks[c];
+    op.w = a.master + ch.state_off;
+    op.m = a.m + ch.state_off;
+    op.v = a.v + ch.state_off;
+    op.p16 = reinterpret_cast<uint16_t*>(ch.p16);
+    int head;
+    bool ok;
+    if constexpr (GS == kGradRed) {
+      op.gred = a.red + ch.state_off;
+      head = head16(op.p16);
+      ok = aligned(op.w + head, 16) && aligned(op.gred + head, 16);
+    } else {
+      op.g16 = GS == kGradFlat16 ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
+      head = head16(op.g16);
+      ok = aligned(op.w + head, 16) && aligned(op.g16 + head, 8);
+    }
+    if constexpr (CAST) ok = ok && aligned(op.p16 + head, 8);
+    ok = ok && aligned(op.m + head, 16) && aligned(op.v + head, 16);
+    run_chunk<2>(op, ch.len, head, ok);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// standalone write-back, init, export, fill
+
+template <int DT>
+struct CastOp {
+  const float* w;
+  uint16_t* p16;
+  __device__ __forceinline__ void elem(int64_t j) { p16[j] = (uint16_t)enc16<DT>(w[j]); }
+  template <int U>
+  __device__ __forceinline__ void quads(int64_t j, int64_t stride) {
+    f32x4 W[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) W[k] = ld32x4_nt(w + j + k * stride);
+#pragma unroll
+    for (int k = 0; k < U; ++k) st16x4_nt(p16 + j + k * stride, enc16x4<DT>(W[k]));
+  }
+};
+
+template <int DT>
+__global__ void __launch_bounds__(kBlock) cast_kernel(const Chunk* chunks, int64_t n_chunks, const float* master,
+                                                      const DevScalars* sc) {
+  if (sc->skipped) return;
+  CastOp<DT> op{nullptr, nullptr};
+  for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    const Chunk ch = chunks[c];
+    op.w = master + ch.state_off;
+    op.p16 = reinterpret_cast<uint16_t*>(ch.p16);
+    const int head = head16(op.p16);
+    run_chunk<4>(op, ch.len, head, aligned(op.w + head, 16));
+  }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kBlock) init_kernel(const Chunk* chunks, int64_t n_chunks, float* master,
+                                                      const float* master_init) {
+  for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    const Chunk ch = chunks[c];
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(ch.p16);
+    float* w = master + ch.state_off;
+    for (int64_t j = threadIdx.x; j < ch.len; j += kBlock)
+      w[j] = master_init ? master_init[ch.shard_off + j] : dec16<DT>(p[j]);
+  }
+}
+
+__global__ void __launch_bounds__(kBlock) export_kernel(const Chunk* chunks, int64_t n_chunks, const float* src,
+                                                        float* dst) {
+  for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    const Chunk ch = chunks[c];
+    for (int64_t j = threadIdx.x; j < ch.len; j += kBlock) dst[ch.shard_off + j] = src[ch.state_off + j];
+  }
+}
+
+__global__ void __launch_bounds__(kBlock) fill_zero_kernel(float* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < n; j += stride) p[j] = 0.0f;
+}
+
+__global__ void empty_stats_kernel(DevScalars* sc) {
+  sc->local_sumsq = 0.0;
+  sc->local_flag = 0;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (host)
+
+struct Launch {
+  hipStream_t stream;
+  unsigned grid;
+};
+
+static unsigned clamp_grid(int64_t n_chunks, int64_t cap) {
+  int64_t g = n_chunks < cap ? n_chunks : cap;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
+                          DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st) {
+  if (n_chunks == 0) {
+    hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc);
+    return hipGetLastError();
+  }
+  StatsArgs a{chunks, n_chunks, flat_g, inv, sc, parts};
+  const unsigned g = clamp_grid(n_chunks, grid_cap < kMaxStatsBlocks ? grid_cap : kMaxStatsBlocks);
+  if (dtype == ZERO_BF16)
+    hipLaunchKernelGGL(stats16_kernel<ZERO_BF16>, dim3(g), dim3(kBlock), 0, st, a);
+  else
+    hipLaunchKernelGGL(stats16_kernel<ZERO_F16>, dim3(g), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+static void launch_reduce_dt(const ReduceArgs& a, unsigned g, hipStream_t st) {
+  switch (a.n_ranks) {
+    case 2: hipLaunchKernelGGL((reduce_kernel<DT, 2>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((reduce_kernel<DT, 4>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((reduce_kernel<DT, 8>), dim3(g), dim3(kBlock), 0, st, a); break;
+    default: hipLaunchKernelGGL((reduce_kernel<DT, 0>), dim3(g), dim3(kBlock), 0, st, a); break;
+  }
+}
+
+hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
+                         int32_t n_ranks, float inv, float* red, DevScalars* sc, StatsPart* parts,
+                         int64_t grid_cap, hipStream_t st) {
+  if (n_chunks == 0) {
+    hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc);
+    return hipGetLastError();
+  }
+  ReduceArgs a;
+  a.chunks = chunks;
+  a.n_chunks = n_chunks;
+  for (int q = 0; q < kMaxRanks; ++q) a.ranks[q] = q < n_ranks ? static_cast<const uint16_t*>(ranks[q]) : nullptr;
+  a.n_ranks = n_ranks;
+  a.inv = inv;
+  a.red = red;
+  a.sc = sc;
+  a.parts = parts;
+  const unsigned g = clamp_grid(n_chunks, grid_cap < kMaxStatsBlocks ? grid_cap : kMaxStatsBlocks);
+  if (dtype == ZERO_BF16)
+    launch_reduce_dt<ZERO_BF16>(a, g, st);
+  else
+    launch_reduce_dt<ZERO_F16>(a, g, st);
+  return hipGetLastError();
+}
+
+template <int DT, int GS>
+static void launch_adam_gs(const AdamArgs& a, bool cast, unsigned g, hipStream_t st) {
+  if (cast)
+    hipLaunchKernelGGL((adam_kernel<DT, GS, true>), dim3(g), dim3(kBlock), 0, st, a);
+  else
+    hipLaunchKernelGGL((adam_kernel<DT, GS, false>), dim3(g), dim3(kBlock), 0, st, a);
+}
+
+template <int DT>
+static void launch_adam_dt(const AdamArgs& a, int gs, bool cast, unsigned g, hipStream_t st) {
+  if (gs == kGradFlat16) launch_adam_gs<DT, kGradFlat16>(a, cast, g, st);
+  else if (gs == kGradChunk16) launch_adam_gs<DT, kGradChunk16>(a, cast, g, st);
+  else launch_adam_gs<DT, kGradRed>(a, cast, g, st);
+}
+
+hipError_t launch_adam(int dtype, int grad_source, bool cast, const AdamArgs& a, int64_t grid_cap, hipStream_t st) {
+  const unsigned g = clamp_grid(a.n_chunks, grid_cap);
+  if (dtype == ZERO_BF16)
+    launch_adam_dt<ZERO_BF16>(a, grad_source, cast, g, st);
+  else
+    launch_adam_dt<ZERO_F16>(a, grad_source, cast, g, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* chunks, int64_t n_chunks,
+                            const uint16_t* flat_g, const float* red, float* master, float* m, float* v,
+                            DevScalars* sc, int32_t slot, int32_t other_flag, double other_sumsq, float max_norm,
+                            float inv, const zero_adam_hparams_t* hp, int64_t grid_cap, hipStream_t st) {
+  AdamArgs a;
+  a.chunks = chunks;
+  a.n_chunks = n_chunks;
+  a.flat_g = flat_g;
+  a.red = red;
+  a.master = master;
+  a.m = m;
+  a.v = v;
+  a.sc = sc;
+  a.slot = slot;
+  a.other_flag = other_flag;
+  a.other_sumsq = other_sumsq;
+  a.max_norm = max_norm;
+  a.inv = inv;
+  a.lr = hp->lr;
+  a.beta1 = hp->beta1;
+  a.beta2 = hp->beta2;
+  a.eps = hp->eps;
+  a.wd = hp->weight_decay;
+  return launch_adam(dtype, grad_source, cast, a, grid_cap, st);
+}
+
+hipError_t launch_cast(int dtype, const Chunk* chunks, int64_t n_chunks, const float* master,
+                       const DevScalars* sc, int64_t grid_cap, hipStream_t st) {
+  if (n_chunks == 0) return hipSuccess;
+  const unsigned g = clamp_grid(n_chunks, grid_cap);
+  if (dtype == ZERO_BF16)
+    hipLaunchKernelGGL(cast_kernel<ZERO_BF16>, dim3(g), dim3(kBlock), 0, st, chunks, n_chunks, master, sc);
+  else
+    hipLaunchKernelGGL(cast_kernel<ZERO_F16>, dim3(g), dim3(kBlock), 0, st, chunks, n_chunks, master, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_init(int dtype, const Chunk* chunks, int64_t n_chunks, float* master, float* m, float* v,
+                       int64_t state_elems, const float* master_init, int64_t grid_cap, hipStream_t st) {
+  const unsigned gz = clamp_grid((state_elems + kBlock - 1) / kBlock, 4096);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(gz), dim3(kBlock), 0, st, master, state_elems);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(gz), dim3(kBlock), 0, st, m, state_elems);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(gz), dim3(kBlock), 0, st, v, state_elems);
+  if (n_chunks > 0) {
+    const unsigned g = clamp_grid(n_chunks, grid_cap);
+    if (dtype == ZERO_BF16)
+      hipLaunchKernelGGL(init_kernel<ZERO_BF16>, dim3(g), dim3(kBlock), 0, st, chunks, n_chunks, master,
+                         master_init);
+    else
+      hipLaunchKernelGGL(init_kernel<ZERO_F16>, dim3(g), dim3(kBlock), 0, st, chunks, n_chunks, master,
+                         master_init);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const unsigned gz = clamp_grid((n + kBlock - 1) / kBlock, 4096);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(gz), dim3(kBlock), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_export(const Chunk* chunks, int64_t n_chunks, const float* src, float* dst, int64_t grid_cap,
+                         hipStream_t st) {
+  if (n_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(export_kernel, dim3(clamp_grid(n_chunks, grid_cap)), dim3(kBlock), 0, st, chunks, n_chunks,
+                     src, dst);
+  return hipGetLastError();
+}
+
+}  // namespace zs

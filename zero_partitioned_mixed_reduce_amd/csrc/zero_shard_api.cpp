@@ -1,0 +1,381 @@
+// C ABI of one data-parallel rank's partitioned mixed-precision optimizer step.
+// Host side: argument checks, the step-order state machine, the device scalar
+// block and kernel launches.  The arithmetic is in kernels.hip.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "zero_shard.h"
+#include "zs_internal.h"
+
+namespace zs {
+hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
+                          DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st);
+hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
+                         int32_t n_ranks, float inv, float* red, DevScalars* sc, StatsPart* parts,
+                         int64_t grid_cap, hipStream_t st);
+struct AdamArgs;
+hipError_t launch_cast(int dtype, const Chunk* chunks, int64_t n_chunks, const float* master,
+                       const DevScalars* sc, int64_t grid_cap, hipStream_t st);
+hipError_t launch_init(int dtype, const Chunk* chunks, int64_t n_chunks, float* master, float* m, float* v,
+                       int64_t state_elems, const float* master_init, int64_t grid_cap, hipStream_t st);
+hipError_t launch_export(const Chunk* chunks, int64_t n_chunks, const float* src, float* dst, int64_t grid_cap,
+                         hipStream_t st);
+hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* chunks, int64_t n_chunks,
+                            const uint16_t* flat_g, const float* red, float* master, float* m, float* v,
+                            DevScalars* sc, int32_t slot, int32_t other_flag, double other_sumsq, float max_norm,
+                            float inv, const zero_adam_hparams_t* hp, int64_t grid_cap, hipStream_t st);
+}  // namespace zs
+
+namespace {
+
+thread_local std::string g_err;
+
+zero_status_t fail(zero_status_t s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+zero_status_t hip_fail(const char* what, hipError_t e) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return ZERO_EHIP;
+}
+
+#define ZS_HIP(call)                              \
+  do {                                            \
+    hipError_t e_ = (call);                       \
+    if (e_ != hipSuccess) return hip_fail(#call, e_); \
+  } while (0)
+
+enum Phase { kReady, kReduced, kChecked, kNormed, kStepped };
+enum { kGradFlat16 = 0, kGradChunk16 = 1, kGradRed = 2 };
+
+}  // namespace
+
+struct zero_shard {
+  zero_shard_info_t info;
+  std::vector<zs::Piece> pieces;
+  int dtype;
+  int device;
+  bool has_registered_grads;
+  float *master, *m, *v, *red;
+  zs::DevScalars* sc;
+  zs::StatsPart* parts;
+  zs::Chunk* chunks;
+  int64_t n_chunks;
+  int64_t grid_stats, grid_main;
+  Phase phase;
+  bool cast_pending;
+  // current step
+  int grad_source;
+  const uint16_t* step_flat_g;
+  float inv;
+  int32_t other_flag;
+  double other_sumsq;
+  float max_norm;
+  int64_t adam_calls;  // parity selects the counter slot
+};
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  bool changed = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != dev) changed = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(prev);
+  }
+};
+
+int64_t blocks_per_cu() {
+  const char* e = getenv("ZERO_SHARD_BLOCKS_PER_CU");
+  if (e) {
+    long v = strtol(e, nullptr, 10);
+    if (v >= 1 && v <= 64) return v;
+  }
+  return 8;
+}
+
+zero_status_t sync_read_scalars(zero_shard* h, hipStream_t st, zs::DevScalars* out) {
+  ZS_HIP(hipStreamSynchronize(st));
+  ZS_HIP(hipMemcpy(out, h->sc, sizeof(zs::DevScalars), hipMemcpyDeviceToHost));
+  return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zero_last_error(void) { return g_err.c_str(); }
+
+zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* out) {
+  if (!out) return fail(ZERO_EINVAL, "null output");
+  zs::Plan p;
+  zero_status_t s = zs::build_plan(desc, &p, &g_err);
+  if (s != ZERO_OK) return s;
+  *out = p.info;
+  return ZERO_OK;
+}
+
+zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
+                              const float* master_init, void* stream, zero_shard_t* out) {
+  if (!bufs || !out) return fail(ZERO_EINVAL, "null buffers or output handle");
+  *out = nullptr;
+  zs::Plan p;
+  zero_status_t s = zs::build_plan(desc, &p, &g_err);
+  if (s != ZERO_OK) return s;
+  if (!bufs->master || !bufs->m || !bufs->v || !bufs->workspace)
+    return fail(ZERO_EINVAL, "master, m, v and workspace must be non-null");
+  auto mis16 = [](const void* q) { return ((uintptr_t)q & 15u) != 0; };
+  if (mis16(bufs->master) || mis16(bufs->m) || mis16(bufs->v) || (bufs->red && mis16(bufs->red)))
+    return fail(ZERO_EINVAL, "state buffers must be 16-byte aligned");
+  if (((uintptr_t)bufs->workspace & 255u) != 0) return fail(ZERO_EINVAL, "workspace must be 256-byte aligned");
+  if (bufs->state_capacity < p.info.state_elems)
+    return fail(ZERO_EINVAL, "state_capacity " + std::to_string(bufs->state_capacity) + " < state_elems " +
+                                 std::to_string(p.info.state_elems));
+  if (bufs->workspace_capacity < p.info.workspace_bytes)
+    return fail(ZERO_EINVAL, "workspace_capacity " + std::to_string(bufs->workspace_capacity) +
+                                 " < workspace_bytes " + std::to_string(p.info.workspace_bytes));
+  if (master_init && mis16(master_init)) return fail(ZERO_EINVAL, "master_init must be 16-byte aligned");
+
+  zero_shard* h = new (std::nothrow) zero_shard();
+  if (!h) return fail(ZERO_EINVAL, "out of host memory");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  int cus = 0;
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail("hipGetDevice/hipDeviceGetAttribute", e);
+  }
+  h->info = p.info;
+  h->pieces = std::move(p.pieces);
+  h->dtype = desc->dtype;
+  h->device = dev;
+  h->has_registered_grads = desc->grad16 || desc->flat_grad16;
+  h->master = bufs->master;
+  h->m = bufs->m;
+  h->v = bufs->v;
+  h->red = bufs->red;
+  char* ws = static_cast<char*>(bufs->workspace);
+  h->sc = reinterpret_cast<zs::DevScalars*>(ws);
+  h->parts = reinterpret_cast<zs::StatsPart*>(ws + zs::kPartsOff);
+  h->chunks = reinterpret_cast<zs::Chunk*>(ws + zs::kChunksOff);
+  h->n_chunks = (int64_t)p.chunks.size();
+  h->grid_main = (int64_t)cus * blocks_per_cu();
+  h->grid_stats = h->grid_main < zs::kMaxStatsBlocks ? h->grid_main : zs::kMaxStatsBlocks;
+  h->phase = kReady;
+  h->cast_pending = false;
+  h->adam_calls = 0;
+
+  zs::DevScalars init_sc;
+  memset(&init_sc, 0, sizeof(init_sc));
+  init_sc.slot[0] = zs::Slot{0, 1.0, 1.0};
+  init_sc.slot[1] = zs::Slot{0, 1.0, 1.0};
+  init_sc.clip = 1.0f;
+  zero_status_t rs = ZERO_OK;
+  do {
+    if ((e = hipMemcpyAsync(h->sc, &init_sc, sizeof(init_sc), hipMemcpyHostToDevice, st)) != hipSuccess) {
+      rs = hip_fail("hipMemcpyAsync(scalars)", e);
+      break;
+    }
+    if (!p.chunks.empty() &&
+        (e = hipMemcpyAsync(h->chunks, p.chunks.data(), p.chunks.size() * sizeof(zs::Chunk), hipMemcpyHostToDevice,
+                            st)) != hipSuccess) {
+      rs = hip_fail("hipMemcpyAsync(chunk table)", e);
+      break;
+    }
+    if ((e = zs::launch_init(h->dtype, h->chunks, h->n_chunks, h->master, h->m, h->v, h->info.state_elems,
+                             master_init, h->grid_main, st)) != hipSuccess) {
+      rs = hip_fail("init kernels", e);
+      break;
+    }
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) {
+      rs = hip_fail("hipStreamSynchronize(init)", e);
+      break;
+    }
+  } while (0);
+  if (rs != ZERO_OK) {
+    delete h;
+    return rs;
+  }
+  *out = h;
+  return ZERO_OK;
+}
+
+zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks, float inv_loss_scale,
+                                void* stream) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (h->phase == kStepped && h->cast_pending)
+    return fail(ZERO_ESTATE, "zero_cast_params of the previous step is pending");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceGuard dg(h->device);
+  hipError_t e;
+  if (n_ranks == 0) {
+    if (!h->has_registered_grads) return fail(ZERO_EINVAL, "n_ranks == 0 needs gradients registered at init");
+    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, nullptr, inv_loss_scale, h->sc, h->parts,
+                           h->grid_stats, st);
+    if (e != hipSuccess) return hip_fail("statistics kernel", e);
+    h->grad_source = kGradChunk16;
+    h->step_flat_g = nullptr;
+  } else if (n_ranks == 1) {
+    if (!rank_grads || !rank_grads[0]) return fail(ZERO_EINVAL, "rank_grads[0] is null");
+    const uint16_t* g = static_cast<const uint16_t*>(rank_grads[0]);
+    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, g, inv_loss_scale, h->sc, h->parts, h->grid_stats, st);
+    if (e != hipSuccess) return hip_fail("statistics kernel", e);
+    h->grad_source = kGradFlat16;
+    h->step_flat_g = g;
+  } else {
+    if (n_ranks > zs::kMaxRanks) return fail(ZERO_EINVAL, "n_ranks above 64");
+    if (!rank_grads) return fail(ZERO_EINVAL, "rank_grads is null");
+    for (int q = 0; q < n_ranks; ++q)
+      if (!rank_grads[q]) return fail(ZERO_EINVAL, "rank_grads[" + std::to_string(q) + "] is null");
+    if (!h->red) return fail(ZERO_EINVAL, "reducing N_d >= 2 buffers needs bufs.red");
+    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, inv_loss_scale, h->red, h->sc,
+                          h->parts, h->grid_stats, st);
+    if (e != hipSuccess) return hip_fail("reduce kernel", e);
+    h->grad_source = kGradRed;
+    h->step_flat_g = nullptr;
+  }
+  h->inv = inv_loss_scale;
+  h->other_flag = 0;
+  h->other_sumsq = 0.0;
+  h->max_norm = 0.0f;
+  h->phase = kReduced;
+  h->cast_pending = false;
+  return ZERO_OK;
+}
+
+zero_status_t zero_local_stats(zero_shard_t h, int32_t* found_inf, double* sumsq, void* stream) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (h->phase == kReady || h->phase == kStepped) return fail(ZERO_ESTATE, "no gradient intake in this step yet");
+  DeviceGuard dg(h->device);
+  zs::DevScalars sc;
+  zero_status_t s = sync_read_scalars(h, static_cast<hipStream_t>(stream), &sc);
+  if (s != ZERO_OK) return s;
+  if (found_inf) *found_inf = sc.local_flag;
+  if (sumsq) *sumsq = sc.local_sumsq;
+  return ZERO_OK;
+}
+
+zero_status_t zero_check_overflow(zero_shard_t h, int32_t other_ranks_found_inf, int32_t* host_found_inf,
+                                  void* stream) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (h->phase != kReduced && h->phase != kChecked)
+    return fail(ZERO_ESTATE, "zero_check_overflow must follow zero_reduce_grads");
+  h->other_flag = other_ranks_found_inf ? 1 : 0;
+  h->phase = kChecked;
+  if (host_found_inf) {
+    DeviceGuard dg(h->device);
+    zs::DevScalars sc;
+    zero_status_t s = sync_read_scalars(h, static_cast<hipStream_t>(stream), &sc);
+    if (s != ZERO_OK) return s;
+    *host_found_inf = (sc.local_flag | h->other_flag) ? 1 : 0;
+  }
+  return ZERO_OK;
+}
+
+zero_status_t zero_grad_norm(zero_shard_t h, double other_ranks_sumsq, float max_norm, double* host_norm,
+                             void* stream) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (h->phase != kChecked && h->phase != kNormed)
+    return fail(ZERO_ESTATE, "zero_grad_norm must follow zero_check_overflow");
+  h->other_sumsq = other_ranks_sumsq;
+  h->max_norm = max_norm;
+  h->phase = kNormed;
+  if (host_norm) {
+    DeviceGuard dg(h->device);
+    zs::DevScalars sc;
+    zero_status_t s = sync_read_scalars(h, static_cast<hipStream_t>(stream), &sc);
+    if (s != ZERO_OK) return s;
+    *host_norm = sqrt(sc.local_sumsq + other_ranks_sumsq);
+  }
+  return ZERO_OK;
+}
+
+zero_status_t zero_adam_step(zero_shard_t h, const zero_adam_hparams_t* hp, int32_t fuse_cast, void* stream) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (!hp) return fail(ZERO_EINVAL, "null hyperparameters");
+  if (h->phase != kNormed) return fail(ZERO_ESTATE, "zero_adam_step must follow zero_grad_norm");
+  DeviceGuard dg(h->device);
+  hipError_t e = zs::launch_adam_step(h->dtype, h->grad_source, fuse_cast != 0, h->chunks, h->n_chunks,
+                                      h->step_flat_g, h->red, h->master, h->m, h->v, h->sc,
+                                      (int32_t)(h->adam_calls & 1), h->other_flag, h->other_sumsq, h->max_norm,
+                                      h->inv, hp, h->grid_main, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("adam kernel", e);
+  h->adam_calls += 1;
+  h->phase = kStepped;
+  h->cast_pending = fuse_cast == 0;
+  return ZERO_OK;
+}
+
+zero_status_t zero_cast_params(zero_shard_t h, void* stream) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (h->phase != kStepped) return fail(ZERO_ESTATE, "zero_cast_params must follow zero_adam_step");
+  if (!h->cast_pending) return ZERO_OK;
+  DeviceGuard dg(h->device);
+  hipError_t e = zs::launch_cast(h->dtype, h->chunks, h->n_chunks, h->master, h->sc, h->grid_main,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("cast kernel", e);
+  h->cast_pending = false;
+  return ZERO_OK;
+}
+
+zero_status_t zero_shard_info(zero_shard_t h, zero_shard_info_t* out) {
+  if (!h || !out) return fail(ZERO_EINVAL, "null handle or output");
+  *out = h->info;
+  return ZERO_OK;
+}
+
+zero_status_t zero_shard_pieces(zero_shard_t h, int64_t* out, int64_t cap) {
+  if (!h || (!out && cap > 0)) return fail(ZERO_EINVAL, "null handle or output");
+  for (int64_t p = 0; p < cap && p < (int64_t)h->pieces.size(); ++p) {
+    const zs::Piece& pc = h->pieces[p];
+    out[5 * p + 0] = pc.tensor;
+    out[5 * p + 1] = pc.tensor_off;
+    out[5 * p + 2] = pc.shard_off;
+    out[5 * p + 3] = pc.state_off;
+    out[5 * p + 4] = pc.len;
+  }
+  return ZERO_OK;
+}
+
+zero_status_t zero_shard_query(zero_shard_t h, int64_t* t, int32_t* last_skipped, double* last_norm,
+                               float* last_clip, void* stream) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  DeviceGuard dg(h->device);
+  zs::DevScalars sc;
+  zero_status_t s = sync_read_scalars(h, static_cast<hipStream_t>(stream), &sc);
+  if (s != ZERO_OK) return s;
+  if (t) *t = sc.slot[h->adam_calls & 1].t;
+  if (last_skipped) *last_skipped = h->adam_calls ? sc.skipped : 0;
+  if (last_norm) *last_norm = sc.norm;
+  if (last_clip) *last_clip = sc.clip;
+  return ZERO_OK;
+}
+
+zero_status_t zero_export_state(zero_shard_t h, int32_t which, float* dst, void* stream) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  const float* src = which == 0 ? h->master : which == 1 ? h->m : which == 2 ? h->v : which == 3 ? h->red : nullptr;
+  if (!src) return fail(ZERO_EINVAL, "which must be 0 (master), 1 (m), 2 (v) or 3 (red, when allocated)");
+  if (!dst && h->info.valid_elems > 0) return fail(ZERO_EINVAL, "null destination");
+  DeviceGuard dg(h->device);
+  hipError_t e = zs::launch_export(h->chunks, h->n_chunks, src, dst, h->grid_main, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("export kernel", e);
+  return ZERO_OK;
+}
+
+zero_status_t zero_shard_destroy(zero_shard_t h) {
+  delete h;
+  return ZERO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal layout shared by the host plan and the gfx950 kernels.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "zero_shard.h"
+
+namespace zs {
+
+// Elements per work item.  A multiple of 8, so that every chunk after the
+// first of a tensor piece starts on a 16-byte boundary of the 16-bit data.
+constexpr int64_t kChunk = 8192;
+// Per-block partial slots of the statistics pass (grid cap of that kernel).
+constexpr int kMaxStatsBlocks = 4096;
+// Local-reduce fan-in limit (rank pointers travel as kernel arguments).
+constexpr int kMaxRanks = 64;
+constexpr int kBlock = 256;
+
+// One work item: a run of `len` consecutive shard elements inside one tensor.
+struct alignas(16) Chunk {
+  int64_t state_off;  // offset in master / m / v / red
+  int64_t flat_off;   // flat model index of the first element (rank buffers are flat)
+  int64_t shard_off;  // logical offset inside the shard
+  uint64_t p16;       // device address of the first 16-bit parameter
+  uint64_t g16;       // device address of the first registered gradient element, or 0
+  int32_t len;
+  int32_t tensor;
+};
+static_assert(sizeof(Chunk) == 48, "chunk layout");
+
+struct Slot {
+  int64_t t;      // applied steps
+  double p1, p2;  // beta1^t, beta2^t (fp64 running products)
+};
+
+// Device-resident scalars of the step (first 256 bytes of the workspace).
+struct alignas(256) DevScalars {
+  double local_sumsq;  // this rank's sum of u^2 (statistics pass)
+  int32_t local_flag;  // this rank's non-finite flag
+  uint32_t counter;    // blocks finished in the statistics pass (reset by the last one)
+  Slot slot[2];        // step counters; zero_adam_step reads one and writes the other
+  double norm;         // report of the last zero_adam_step
+  float clip;
+  int32_t skipped;
+  int64_t report_t;
+};
+static_assert(sizeof(DevScalars) == 256, "scalar block");
+
+struct StatsPart {
+  uint64_t sumsq_bits;  // fp64 partial of one block, as bits
+  uint32_t flag;
+  uint32_t pad;
+};
+
+constexpr int64_t kPartsOff = sizeof(DevScalars);
+constexpr int64_t kChunksOff = kPartsOff + kMaxStatsBlocks * (int64_t)sizeof(StatsPart);
+
+struct Piece {
+  int64_t tensor, tensor_off, shard_off, state_off, len;
+};
+
+struct Plan {
+  zero_shard_info_t info;
+  std::vector<Piece> pieces;
+  std::vector<Chunk> chunks;
+};
+
+// Validates the description and lays out pieces and chunks.  Returns
+// ZERO_OK or ZERO_EINVAL with *err set.
+zero_status_t build_plan(const zero_shard_desc_t* d, Plan* out, std::string* err);
+
+}  // namespace zs

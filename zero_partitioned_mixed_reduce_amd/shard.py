@@ -1,0 +1,118 @@
+"""Torch-side convenience around the C ABI: allocates the caller-owned device
+buffers with torch and passes torch's current HIP stream.  Every step of the
+path runs in libzero_shard.so; this module only marshals arguments."""
+import ctypes
+
+import torch
+
+from . import _abi as abi
+
+_TDT = {abi.ZERO_F16: torch.float16, abi.ZERO_BF16: torch.bfloat16}
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_desc(numel, dp_size, dp_rank, dtype, params, grads=None, align=0):
+    """params / grads: one flat tensor, or a list of per-tensor tensors (or None)."""
+    numel = [int(n) for n in numel]
+    keep = {}
+    d = abi.zero_shard_desc_t()
+    d.dp_size, d.dp_rank, d.dtype, d.align = dp_size, dp_rank, dtype, align
+    arr = (ctypes.c_int64 * len(numel))(*numel)
+    keep["numel"] = arr
+    d.num_tensors = len(numel)
+    d.numel = ctypes.cast(arr, abi.c_i64p)
+
+    def ptrs(ts):
+        a = (ctypes.c_void_p * len(ts))(*[t.data_ptr() if t is not None else None for t in ts])
+        return a
+
+    if isinstance(params, (list, tuple)):
+        keep["p"] = ptrs(params)
+        d.param16 = ctypes.cast(keep["p"], ctypes.POINTER(ctypes.c_void_p))
+    else:
+        d.flat_param16 = params.data_ptr()
+    if grads is not None:
+        if isinstance(grads, (list, tuple)):
+            keep["g"] = ptrs(grads)
+            d.grad16 = ctypes.cast(keep["g"], ctypes.POINTER(ctypes.c_void_p))
+        else:
+            d.flat_grad16 = grads.data_ptr()
+    d._keep = keep
+    return d
+
+
+class ZeroShard:
+    """One rank's shard: plan, caller-owned buffers (torch), handle."""
+
+    def __init__(self, numel, dp_size, dp_rank, dtype, params, grads=None, master_init=None, with_red=False,
+                 device="cuda"):
+        self.dtype = dtype
+        self.desc = make_desc(numel, dp_size, dp_rank, dtype, params, grads)
+        self._params, self._grads = params, grads
+        self.info = abi.zero_shard_plan(self.desc)
+        n = self.info.state_elems
+        self.master = torch.empty(n, dtype=torch.float32, device=device)
+        self.m = torch.empty(n, dtype=torch.float32, device=device)
+        self.v = torch.empty(n, dtype=torch.float32, device=device)
+        self.red = torch.empty(n, dtype=torch.float32, device=device) if with_red else None
+        self.workspace = torch.empty(self.info.workspace_bytes, dtype=torch.uint8, device=device)
+        b = abi.zero_shard_bufs_t()
+        b.master, b.m, b.v = self.master.data_ptr(), self.m.data_ptr(), self.v.data_ptr()
+        b.red = self.red.data_ptr() if self.red is not None else None
+        b.workspace = self.workspace.data_ptr()
+        b.state_capacity = n
+        b.workspace_capacity = self.info.workspace_bytes
+        self.bufs = b
+        mi = None
+        if master_init is not None:
+            assert master_init.dtype == torch.float32 and master_init.numel() == self.info.valid_elems
+            mi = master_init.data_ptr()
+        self.h = abi.zero_shard_init(self.desc, b, mi, _stream())
+
+    # step calls (same names as the C ABI)
+    def zero_reduce_grads(self, rank_grads, inv_loss_scale):
+        ptrs = [g.data_ptr() for g in rank_grads] if rank_grads else []
+        abi.zero_reduce_grads(self.h, ptrs, inv_loss_scale, _stream())
+
+    def zero_local_stats(self):
+        return abi.zero_local_stats(self.h, _stream())
+
+    def zero_check_overflow(self, other_ranks_found_inf=False, sync=False):
+        return abi.zero_check_overflow(self.h, other_ranks_found_inf, _stream(), sync)
+
+    def zero_grad_norm(self, other_ranks_sumsq=0.0, max_norm=1.0, sync=False):
+        return abi.zero_grad_norm(self.h, other_ranks_sumsq, max_norm, _stream(), sync)
+
+    def zero_adam_step(self, lr, beta1, beta2, eps, weight_decay, fuse_cast=True):
+        hp = abi.zero_adam_hparams_t(lr, beta1, beta2, eps, weight_decay)
+        abi.zero_adam_step(self.h, hp, fuse_cast, _stream())
+
+    def zero_cast_params(self):
+        abi.zero_cast_params(self.h, _stream())
+
+    def query(self):
+        return abi.zero_shard_query(self.h, _stream())
+
+    def pieces(self):
+        return abi.zero_shard_pieces(self.h, self.info.num_pieces)
+
+    def export(self, which):
+        """State buffer `which` ('master', 'm', 'v', 'red') in logical shard order (device fp32)."""
+        idx = {"master": 0, "m": 1, "v": 2, "red": 3}[which]
+        out = torch.empty(self.info.valid_elems, dtype=torch.float32, device=self.master.device)
+        abi.zero_export_state(self.h, idx, out.data_ptr() if out.numel() else None, _stream())
+        return out
+
+    def close(self):
+        if self.h:
+            abi.zero_shard_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
