@@ -1,0 +1,269 @@
+"""Benchmark: one data-parallel rank's partitioned optimizer step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic
+gradients: [local reduce of N_d rank buffers] + unscale + overflow flag +
+sum of squares (one pass), global norm and clip, Adam with bias correction
+and decoupled weight decay, and the fused 16-bit write-back.  All inputs are
+resident in HBM before the timed region; the timed region is exactly K steps
+bracketed by device synchronisation.
+
+Prints one JSON line.  `value` is shard parameters updated per second;
+`roofline` reports the dominant kernel (the Adam pass) against the HBM peak;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "shard params/s per optimizer step and achieved HBM GB/s (% of peak), 1 GPU"
+DTYPE_NAME = {1: "fp16", 2: "bf16"}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="full7p5b", choices=["tiny", "gpt2", "zero1_7p5b", "reduce8", "full7p5b"])
+    p.add_argument("--rank", type=int, default=None, help="data-parallel rank whose shard is stepped")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=1 << 26, help="elements of the oracle's timed sample")
+    p.add_argument("--cpu-steps", type=int, default=3)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run one 1 GiB device copy before the timed region (for counter scaling)")
+    return p.parse_args()
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "zs_internal.h"):
+        with open(os.path.join(ROOT, "zero_partitioned_mixed_reduce_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Workload:
+    """Device-resident inputs and the library handle for one rank."""
+
+    def __init__(self, w, rank):
+        import torch
+        import synth
+        from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
+
+        self.w, self.rank = w, rank
+        dt = w.dtype
+        psi = w.psi
+        starts = [0]
+        for n in w.numel:
+            starts.append(starts[-1] + n)
+        self.starts = starts
+        mstream = synth.stream_id(synth.MASTER)
+
+        def filled16(n, first, sigma, stream, zero=False):
+            t = torch.empty(n, dtype=torch.int16, device="cuda")
+            synth.gpu_normal_16(t, dt, w.seed, stream, first=first, sigma=sigma,
+                                zero_seed=w.seed if zero else 0, zero_mod=w.zero_mod if zero else 0)
+            return t
+
+        # 16-bit parameters: RNE16 of the master values, full model (the all-gather target)
+        if w.param_mode == "flat":
+            self.params = filled16(psi, 0, w.master_sigma, mstream)
+        else:
+            self.params = [filled16(n, starts[k], w.master_sigma, mstream) for k, n in enumerate(w.numel)]
+        # gradients
+        self.rank_grads, grads_reg = [], None
+        gstream = synth.stream_id(synth.GRAD, 0, 0)
+        if w.grad_mode == "reduce":
+            self.rank_grads = [filled16(psi, 0, w.grad_sigma, synth.stream_id(synth.GRAD, q, 0), zero=True)
+                               for q in range(w.nd)]
+        elif w.grad_mode == "flat":
+            grads_reg = filled16(psi, 0, w.grad_sigma, gstream)
+        else:
+            grads_reg = [filled16(n, starts[k], w.grad_sigma, gstream) for k, n in enumerate(w.numel)]
+        self.grads_reg = grads_reg
+        # fp32 master of this shard (logical order) -> library state
+        import zero_partitioned_mixed_reduce_amd as zpm
+        from zero_partitioned_mixed_reduce_amd import shard as shmod
+        info = zpm.zero_shard_plan(shmod.make_desc(w.numel, w.nd, rank, dt, self.params, grads_reg))
+        b, valid = info.shard_begin, info.valid_elems
+        mi = torch.empty(max(valid, 1), dtype=torch.float32, device="cuda")[:valid]
+        if valid:
+            synth.gpu_normal_f32(mi, w.seed, mstream, first=b, sigma=w.master_sigma)
+        self.shard = ZeroShard(w.numel, w.nd, rank, dt, self.params, grads=grads_reg,
+                               master_init=mi if w.master_given else None, with_red=(w.grad_mode == "reduce"))
+        del mi
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        self.info = self.shard.info
+        self.inv = 1.0 / w.loss_scale
+        # the other ranks' sum of squares: the expected value under the synthetic distribution
+        sig_u = w.grad_sigma * self.inv * (w.nd ** 0.5 if w.grad_mode == "reduce" else 1.0)
+        self.other_sumsq = float(psi - valid) * sig_u * sig_u
+
+    def step(self, ev=None):
+        s, w = self.shard, self.w
+        if ev:
+            ev[0].record()
+        s.zero_reduce_grads(self.rank_grads, self.inv)
+        if ev:
+            ev[1].record()
+        s.zero_check_overflow(False)
+        s.zero_grad_norm(self.other_sumsq, w.max_norm)
+        s.zero_adam_step(w.hp["lr"], w.hp["beta1"], w.hp["beta2"], w.hp["eps"], w.hp["weight_decay"],
+                         fuse_cast=True)
+        if ev:
+            ev[2].record()
+
+
+def bytes_per_param(w):
+    """Dependency-minimal HBM bytes per shard parameter for the whole step, and for the Adam pass."""
+    if w.grad_mode == "reduce":
+        step = 2 * w.nd + 4 + 4 + 26        # read N_d x 16-bit, write fp32 u; Adam reads u
+        adam = 4 + 12 + 12 + 2
+    else:
+        step = 2 + 2 + 12 + 12 + 2          # statistics pass re-reads the 16-bit gradient
+        adam = 2 + 12 + 12 + 2
+    return step, adam
+
+
+def cpu_baseline(w, sample, steps):
+    """The oracle, single-threaded, on the first `sample` elements of the workload's
+    gradient and state (pre-reduced or N_d-way reduce, as configured)."""
+    import numpy as np
+
+    import oracle
+    import synth
+    n = sample
+    gs = []
+    if w.grad_mode == "reduce":
+        for q in range(w.nd):
+            gs.append(synth.normal_16(n, w.dtype, w.seed, synth.stream_id(synth.GRAD, q, 0), 0, w.grad_sigma,
+                                      w.seed, w.zero_mod))
+    else:
+        gs.append(synth.normal_16(n, w.dtype, w.seed, synth.stream_id(synth.GRAD, 0, 0), 0, w.grad_sigma))
+    st = oracle.RankState(w.dtype, synth.normal_16(n, w.dtype, w.seed, synth.stream_id(synth.MASTER), 0,
+                                                   w.master_sigma),
+                          synth.normal_f32(n, w.seed, synth.stream_id(synth.MASTER), 0, w.master_sigma))
+    hp = oracle.HParams(w.hp["lr"], w.hp["beta1"], w.hp["beta2"], w.hp["eps"], w.hp["weight_decay"])
+    inv = 1.0 / w.loss_scale
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        u, flag, ss = oracle.grad_stats(w.dtype, gs, inv)
+        clip, _ = oracle.clip_coef(ss, w.max_norm)
+        oracle.adam(flag, u, clip, hp, st.counters, st.w, st.m, st.v)
+        if not flag:
+            oracle.cast(w.dtype, st.w, st.p16)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(st.w).all()
+    return n * steps / dt, dt
+
+
+def traffic_from_profiles(cfg, adam_launch_bytes):
+    """HBM bytes per Adam launch from committed rocprofv3 counter summaries, when they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"adam_{cfg}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": f"this build runs one data-parallel rank on one GPU; --gpus {a.gpus} "
+                                   "is not supported (the path has no collectives: see the design notes "
+                                   "for how it shards)"}), flush=True)
+        sys.exit(2)
+    import torch
+    from synth import recipes
+
+    w = recipes.ALL[a.config]()
+    rank = a.rank if a.rank is not None else w.ranks[0]
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    wl = Workload(w, rank)
+    setup_s = time.perf_counter() - t_setup
+    valid = wl.info.valid_elems
+    step_b, adam_b = bytes_per_param(w)
+
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(7)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(a.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    q = wl.shard.query()
+    assert not q["skipped"] and q["t"] == a.warmup, q
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(a.steps):
+        wl.step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q = wl.shard.query()
+    assert not q["skipped"] and q["t"] == a.warmup + a.steps, q
+
+    ms_step = wall * 1e3 / a.steps
+    stats_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / a.steps
+    adam_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps
+    adam_bytes = adam_b * valid
+    achieved = adam_bytes / (adam_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(a.config, adam_bytes)
+    out = {
+        "metric": METRIC,
+        "value": valid / (ms_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "psi": w.psi, "dp_size": w.nd, "dp_rank": rank, "shard_params": valid,
+                   "param_grad_dtype": DTYPE_NAME[w.dtype], "grad_source": w.grad_mode,
+                   "tensors": len(w.numel), "loss_scale": w.loss_scale, "max_norm": w.max_norm,
+                   "adam": w.hp},
+        "hbm_gbps_step": step_b * valid / (ms_step * 1e-3) / 1e9,
+        "hbm_frac_step": step_b * valid / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "bytes_per_param_step": step_b,
+        "breakdown_ms": {"intake_stats": stats_ms, "norm_adam_cast": adam_ms},
+        "roofline": {"kernel": "adam_kernel (Adam + fused 16-bit write-back)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": adam_bytes, "bytes_per_param": adam_b,
+                     "avg_launch_ms": adam_ms},
+        "setup_s": setup_s,
+    }
+    if not a.no_cpu_baseline:
+        n = min(a.cpu_sample, valid)
+        rate, secs = cpu_baseline(w, n, a.cpu_steps)
+        out["cpu_baseline"] = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {n} elements of the shard's workload, {a.cpu_steps} steps "
+                                         f"(statistics, clip, Adam, cast), {secs:.1f} s single-threaded"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,6 +15,28 @@
 
 #include "zs_internal.h"
 
+// Tuning knobs (measured on MI355X; see the design notes):
+//   ZS_ADAM_U   quads per lane in flight in the Adam pass
+//   ZS_STATS_U  quads per lane in flight in the statistics pass
+//   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
+//   ZS_NT_LOAD  non-temporal loads of the fp32 state (read once per step)
+//   ZS_NT_STORE non-temporal stores of the fp32 state and 16-bit parameters
+#ifndef ZS_ADAM_U
+#define ZS_ADAM_U 2
+#endif
+#ifndef ZS_STATS_U
+#define ZS_STATS_U 4
+#endif
+#ifndef ZS_REDUCE_U
+#define ZS_REDUCE_U 2
+#endif
+#ifndef ZS_NT_LOAD
+#define ZS_NT_LOAD 1
+#endif
+#ifndef ZS_NT_STORE
+#define ZS_NT_STORE 1
+#endif
+
 namespace zs {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -63,14 +85,26 @@ __device__ __forceinline__ u32x2 enc16x4(f32x4 w) {
 
 __device__ __forceinline__ u32x2 ld16x4(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void st16x4_nt(uint16_t* p, u32x2 v) {
+#if ZS_NT_STORE
   __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+#else
+  *reinterpret_cast<u32x2*>(p) = v;
+#endif
 }
 __device__ __forceinline__ f32x4 ld32x4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 ld32x4_nt(const float* p) {
+#if ZS_NT_LOAD
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+#else
+  return *reinterpret_cast<const f32x4*>(p);
+#endif
 }
 __device__ __forceinline__ void st32x4_nt(float* p, f32x4 v) {
+#if ZS_NT_STORE
   __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+#else
+  *reinterpret_cast<f32x4*>(p) = v;
+#endif
 }
 
 __device__ __forceinline__ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -191,7 +225,7 @@ __global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
   for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
     const Chunk ch = a.chunks[c];
     op.g = a.flat_g ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
-    run_chunk<4>(op, ch.len, head16(op.g), true);
+    run_chunk<ZS_STATS_U>(op, ch.len, head16(op.g), true);
   }
   finish_stats(op.acc, op.flag, a.sc, a.parts);
 }
@@ -275,7 +309,7 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
     const int head = head16(a.ranks[0] + ch.flat_off);
     bool ok = aligned(op.red + head, 16);
     for (int q = 0; q < a.n_ranks; ++q) ok = ok && aligned(a.ranks[q] + ch.flat_off + head, 8);
-    run_chunk<2>(op, ch.len, head, ok);
+    run_chunk<ZS_REDUCE_U>(op, ch.len, head, ok);
   }
   finish_stats(op.acc, op.flag, a.sc, a.parts);
 }
@@ -443,7 +477,7 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
     }
     if constexpr (CAST) ok = ok && aligned(op.p16 + head, 8);
     ok = ok && aligned(op.m + head, 16) && aligned(op.v + head, 16);
-    run_chunk<2>(op, ch.len, head, ok);
+    run_chunk<ZS_ADAM_U>(op, ch.len, head, ok);
   }
 }
 

@@ -11,7 +11,10 @@ namespace zs {
 
 // Elements per work item.  A multiple of 8, so that every chunk after the
 // first of a tensor piece starts on a 16-byte boundary of the 16-bit data.
-constexpr int64_t kChunk = 8192;
+#ifndef ZS_CHUNK
+#define ZS_CHUNK 8192
+#endif
+constexpr int64_t kChunk = ZS_CHUNK;
 // Per-block partial slots of the statistics pass (grid cap of that kernel).
 constexpr int kMaxStatsBlocks = 4096;
 // Local-reduce fan-in limit (rank pointers travel as kernel arguments).
