@@ -31,6 +31,7 @@ def host():
         L.zs_gather_16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                    ctypes.c_uint64, ctypes.c_uint64, ctypes.c_double, ctypes.c_uint64,
                                    ctypes.c_uint32]
+        L.zs_set_threads.argtypes = [ctypes.c_int]
         L.zs_gather_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
                                     ctypes.c_uint64, ctypes.c_double]
         _host = L
@@ -52,6 +53,11 @@ def gpu():
         L.zs_gpu_fill_16.restype = ctypes.c_int
         _gpu = L
     return _gpu
+
+
+def set_host_threads(n: int) -> None:
+    """OpenMP threads per host fill call (0 = default); global for the process."""
+    host().zs_set_threads(n)
 
 
 def stream_id(array: int, rank: int = 0, step: int = 0) -> int:

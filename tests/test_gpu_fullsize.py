@@ -1,0 +1,160 @@
+"""Full-size parity: the large workloads in the benchmark's own launch
+configuration, checked against the oracle on sampled elements.
+
+The oracle computes this rank's sum of squares over the whole shard (host
+threads over fixed chunks, partials added in chunk order), the clip
+coefficient and bias corrections, then every sampled element one by one:
+shard ends, both sides of every tensor-piece and chunk boundary, and random
+positions.  Two applied steps with the benchmark's gradient.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import recipes
+from tests.gpu_harness import assert_16_close, assert_f32_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu(need_gpu):
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def host_grad(w, q, idx_or_range):
+    """16-bit gradient of rank buffer q (or the reduced buffer) at flat indices."""
+    stream = synth.stream_id(synth.GRAD, q, 0)
+    zs, zm = (w.seed, w.zero_mod) if w.grad_mode == "reduce" else (0, 0)
+    if isinstance(idx_or_range, tuple):
+        lo, n = idx_or_range
+        return synth.normal_16(n, w.dtype, w.seed, stream, lo, w.grad_sigma, zs, zm)
+    return synth.gather_16(idx_or_range, w.dtype, w.seed, stream, w.grad_sigma, zs, zm)
+
+
+def oracle_local_sumsq(w, b, valid, inv):
+    nsrc = w.nd if w.grad_mode == "reduce" else 1
+    step = 1 << 24
+    blocks = [(lo, min(step, valid - lo)) for lo in range(0, valid, step)]
+
+    def part(blk):
+        lo, n = blk
+        srcs = [host_grad(w, q, (b + lo, n)) for q in range(nsrc)]
+        _, flag, ss = oracle.grad_stats(w.dtype, srcs, inv)
+        return flag, ss
+
+    synth.set_host_threads(1)          # the pool below already uses every core
+    try:
+        with ThreadPoolExecutor(16) as ex:
+            parts = list(ex.map(part, blocks))
+    finally:
+        synth.set_host_threads(0)
+    total = 0.0
+    for _, ss in parts:
+        total = total + ss
+    return any(f for f, _ in parts), total
+
+
+def sample_positions(info, pieces, rng):
+    valid = info.valid_elems
+    S = []
+    S.append(np.arange(min(4096, valid)))
+    S.append(np.arange(max(0, valid - 4096), valid))
+    for (_, _, soff, _, ln) in pieces:
+        for edge in (soff, soff + ln):
+            S.append(np.arange(max(0, edge - 64), min(valid, edge + 64)))
+    # chunk boundaries (multiples of 4096 from a piece start, shifted by < 8 for alignment): 4000 of them
+    starts = np.array([p[2] for p in pieces], np.int64)
+    lens = np.array([p[4] for p in pieces], np.int64)
+    k = rng.integers(0, len(pieces), size=4000)
+    e = starts[k] + (rng.integers(0, 1 << 40, size=4000) % np.maximum(lens[k] // 4096, 1)) * 4096
+    S.append((e[:, None] + np.arange(-8, 8)[None, :]).ravel().clip(0, valid - 1))
+    S.append(rng.integers(0, valid, size=200_000))
+    return np.unique(np.concatenate(S).astype(np.int64))
+
+
+def state_index(pieces, pos):
+    soffs = np.array([p[2] for p in pieces], np.int64)
+    stoffs = np.array([p[3] for p in pieces], np.int64)
+    k = np.searchsorted(soffs, pos, side="right") - 1
+    return stoffs[k] + (pos - soffs[k])
+
+
+def gpu_params_at(wl, flat_idx):
+    if not isinstance(wl.params, list):
+        t = torch.from_numpy(flat_idx).cuda()
+        return wl.params[t].cpu().numpy().view(np.uint16)
+    starts = np.array(wl.starts[:-1], np.int64)
+    k = np.searchsorted(starts, flat_idx, side="right") - 1
+    out = np.empty(flat_idx.size, np.uint16)
+    for kk in np.unique(k):
+        sel = np.flatnonzero(k == kk)
+        off = torch.from_numpy(flat_idx[sel] - starts[kk]).cuda()
+        out[sel] = wl.params[kk][off].cpu().numpy().view(np.uint16)
+    return out
+
+
+@pytest.mark.parametrize("cfg,rank", [("zero1_7p5b", 63), ("gpt2", 7), ("reduce8", 7), ("full7p5b", 0)])
+def test_full_size_sampled(cfg, rank):
+    import bench
+    w = recipes.ALL[cfg]()
+    print(f"\n[fullsize] {cfg} rank {rank}: setting up", flush=True)
+    wl = bench.Workload(w, rank)
+    info = wl.info
+    b, valid = info.shard_begin, info.valid_elems
+    pieces = wl.shard.pieces()
+    for _ in range(2):
+        wl.step()
+    torch.cuda.synchronize()
+    q = wl.shard.query()
+    assert q["t"] == 2 and not q["skipped"]
+
+    print(f"[fullsize] {cfg}: oracle sum of squares over {valid} elements", flush=True)
+    flag, local = oracle_local_sumsq(w, b, valid, wl.inv)
+    assert not flag
+    clip, norm = oracle.clip_coef(local + wl.other_sumsq, w.max_norm)
+    assert q["clip"] == clip, (q, clip)
+    assert abs(q["norm"] - norm) <= 1e-9 * norm       # the device's fp64 sum agrees to ~1e-12
+
+    rng = np.random.default_rng(2024)
+    pos = sample_positions(info, pieces, rng)
+    flat = b + pos
+    nsrc = w.nd if w.grad_mode == "reduce" else 1
+    u, _, _ = oracle.grad_stats(w.dtype, [host_grad(w, qq, flat) for qq in range(nsrc)], wl.inv)
+    mstream = synth.stream_id(synth.MASTER)
+    if w.master_given:
+        wv = synth.gather_f32(flat, w.seed, mstream, w.master_sigma)
+    else:
+        wv = oracle.decode16(w.dtype, synth.gather_16(flat, w.dtype, w.seed, mstream, w.master_sigma))
+    mv = np.zeros_like(wv)
+    vv = np.zeros_like(wv)
+    hp = oracle.HParams(w.hp["lr"], w.hp["beta1"], w.hp["beta2"], w.hp["eps"], w.hp["weight_decay"])
+    ctr = oracle.Counters.fresh()
+    for _ in range(2):
+        bc1, bc2 = oracle.next_scalars(hp, ctr)
+        oracle.adam_elems(u, clip, hp, bc1, bc2, wv, mv, vv)
+        ctr.t += 1
+        ctr.p1 *= float(np.float32(hp.beta1))
+        ctr.p2 *= float(np.float32(hp.beta2))
+    p16 = oracle.encode16(w.dtype, wv)
+
+    sidx = torch.from_numpy(state_index(pieces, pos)).cuda()
+    s = wl.shard
+    assert_f32_close(s.master[sidx].cpu().numpy(), wv, f"{cfg} master")
+    assert_f32_close(s.m[sidx].cpu().numpy(), mv, f"{cfg} m")
+    assert_f32_close(s.v[sidx].cpu().numpy(), vv, f"{cfg} v")
+    assert_16_close(gpu_params_at(wl, flat), p16, f"{cfg} p16")
+    # parameters outside this rank's shard are untouched: check around both shard edges
+    outside = np.concatenate([np.arange(max(0, b - 2048), b), np.arange(b + valid, min(w.psi, b + valid + 2048))])
+    if outside.size:
+        exp = synth.gather_16(outside, w.dtype, w.seed, mstream, w.master_sigma)
+        assert (gpu_params_at(wl, outside) == exp).all()
+    print(f"[fullsize] {cfg}: {pos.size} sampled elements match", flush=True)
+    wl.shard.close()
+    del wl

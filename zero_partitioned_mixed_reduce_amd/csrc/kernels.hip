@@ -21,6 +21,9 @@
 //   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
 //   ZS_NT_LOAD  non-temporal loads of the fp32 state (read once per step)
 //   ZS_NT_STORE non-temporal stores of the fp32 state and 16-bit parameters
+//   ZS_ADAM_REVERSE  the Adam pass walks the chunks last to first, so that its
+//               re-read of the gradient starts with what the statistics pass
+//               read most recently (still in the last-level cache)
 #ifndef ZS_ADAM_U
 #define ZS_ADAM_U 2
 #endif
@@ -29,6 +32,9 @@
 #endif
 #ifndef ZS_REDUCE_U
 #define ZS_REDUCE_U 2
+#endif
+#ifndef ZS_ADAM_REVERSE
+#define ZS_ADAM_REVERSE 0
 #endif
 #ifndef ZS_NT_LOAD
 #define ZS_NT_LOAD 1
@@ -115,7 +121,11 @@ __device__ __forceinline__ int head16(const uint16_t* p) { return (int)(((8u - (
 // ---------------------------------------------------------------------------
 // chunk driver
 
-template <int U, class Op>
+// A chunk of `len` elements: `head` leading elements one per lane, then groups of
+// V consecutive elements per lane (U groups in flight, each wave covering 64*V
+// consecutive elements per group slot), then a tail of fewer than V elements.
+// When the streams are not co-aligned (vec_ok false) every element goes one per lane.
+template <int U, int V, class Op>
 __device__ __forceinline__ void run_chunk(Op& op, int64_t len, int head, bool vec_ok) {
   const int64_t tid = threadIdx.x;
   if (!vec_ok) {
@@ -124,11 +134,11 @@ __device__ __forceinline__ void run_chunk(Op& op, int64_t len, int head, bool ve
   }
   if (head > len) head = (int)len;
   if (tid < head) op.elem(tid);
-  const int64_t nq = (len - head) >> 2;  // whole quads in the body
+  const int64_t ng = (len - head) / V;  // whole groups in the body
   int64_t q = tid;
-  for (; q + (U - 1) * kBlock < nq; q += U * kBlock) op.template quads<U>(head + 4 * q, 4 * kBlock);
-  for (; q < nq; q += kBlock) op.template quads<1>(head + 4 * q, 0);
-  const int64_t t0 = head + 4 * nq;
+  for (; q + (U - 1) * kBlock < ng; q += U * kBlock) op.template groups<U>(head + V * q, V * kBlock);
+  for (; q < ng; q += kBlock) op.template groups<1>(head + V * q, 0);
+  const int64_t t0 = head + V * ng;
   if (tid < len - t0) op.elem(t0 + tid);
 }
 
@@ -146,35 +156,30 @@ __device__ __forceinline__ double block_sum(double x, double* lds) {
   return r;
 }
 
-// Called by every block of a statistics pass with its partial sum and flag.
-// The last block to finish combines all partials in block order and publishes
-// the local sum of squares and flag; it then re-arms the completion counter.
-__device__ void finish_stats(double acc, int flag, DevScalars* sc, StatsPart* parts) {
+// Called by every block of a statistics pass with its partial sum of squares.
+// The last block to finish adds all partials in block order, publishes the
+// local sum and the local non-finite flag (the sum is non-finite exactly when
+// some u is, see SumSq), and re-arms the completion counter.
+__device__ void finish_stats(double acc, DevScalars* sc, StatsPart* parts) {
   __shared__ double lds[kBlock / 64];
   __shared__ int is_last;
   const double bsum = block_sum(acc, lds);
-  const int bflag = __syncthreads_or(flag);
   if (threadIdx.x == 0) {
     __hip_atomic_store(&parts[blockIdx.x].sumsq_bits, (uint64_t)__double_as_longlong(bsum), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&parts[blockIdx.x].flag, (uint32_t)bflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t prev = __hip_atomic_fetch_add(&sc->counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (prev == gridDim.x - 1);
   }
   __syncthreads();
   if (!is_last) return;
   double s = 0.0;
-  int f = 0;
-  for (uint32_t b = threadIdx.x; b < gridDim.x; b += kBlock) {
+  for (uint32_t b = threadIdx.x; b < gridDim.x; b += kBlock)
     s += __longlong_as_double(
         (long long)__hip_atomic_load(&parts[b].sumsq_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    f |= (int)__hip_atomic_load(&parts[b].flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
   const double total = block_sum(s, lds);
-  const int tflag = __syncthreads_or(f);
   if (threadIdx.x == 0) {
     sc->local_sumsq = total;
-    sc->local_flag = tflag;
+    sc->local_flag = !__builtin_isfinite(total);
     __hip_atomic_store(&sc->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -182,30 +187,38 @@ __device__ void finish_stats(double acc, int flag, DevScalars* sc, StatsPart* pa
 // ---------------------------------------------------------------------------
 // statistics pass over an already-reduced 16-bit gradient
 
+// Sum of squares in fp64.  The square of a float is exact in fp64 (at most 48
+// significant bits), so fma(d, d, acc) rounds exactly like acc + d * d.  One
+// accumulator per group slot keeps the dependency chains short; they are added
+// in a fixed order at the end.  No separate non-finite test is needed: a finite
+// float squared is at most 1.2e77, so a sum of fewer than 2^63 of them stays
+// finite, and the sum is non-finite exactly when some u is (squares are >= 0,
+// so no inf - inf can occur).
+struct SumSq {
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  __device__ __forceinline__ void add(int k, float u) {
+    const double d = (double)u;
+    acc[k & 3] = __builtin_fma(d, d, acc[k & 3]);
+  }
+  __device__ __forceinline__ double total() const { return ((acc[0] + acc[1]) + acc[2]) + acc[3]; }
+};
+
 template <int DT>
 struct Stats16Op {
   const uint16_t* g;
   float inv;
-  double acc;
-  int flag;
-  __device__ __forceinline__ void add(float u) {
-    flag |= !__builtin_isfinite(u);
-    const double d = (double)u;
-    acc += d * d;
-  }
-  __device__ __forceinline__ void elem(int64_t j) { add(dec16<DT>(g[j]) * inv); }
+  SumSq ss;
+  __device__ __forceinline__ void elem(int64_t j) { ss.add(0, dec16<DT>(g[j]) * inv); }
   template <int U>
-  __device__ __forceinline__ void quads(int64_t j, int64_t stride) {
+  __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
     u32x2 r[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) r[k] = ld16x4(g + j + k * stride);
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const f32x4 x = dec16x4<DT>(r[k]);
-      add(x.x * inv);
-      add(x.y * inv);
-      add(x.z * inv);
-      add(x.w * inv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss.add(k, x[e] * inv);
     }
   }
 };
@@ -221,13 +234,13 @@ struct StatsArgs {
 
 template <int DT>
 __global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
-  Stats16Op<DT> op{nullptr, a.inv, 0.0, 0};
+  Stats16Op<DT> op{nullptr, a.inv, SumSq{}};
   for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
     const Chunk ch = a.chunks[c];
     op.g = a.flat_g ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
-    run_chunk<ZS_STATS_U>(op, ch.len, head16(op.g), true);
+    run_chunk<ZS_STATS_U, 4>(op, ch.len, head16(op.g), true);
   }
-  finish_stats(op.acc, op.flag, a.sc, a.parts);
+  finish_stats(op.ss.total(), a.sc, a.parts);
 }
 
 // ---------------------------------------------------------------------------
@@ -251,22 +264,17 @@ struct ReduceOp {
   float* red;
   float inv;
   int nr;
-  double acc;
-  int flag;
+  SumSq ss;
   __device__ __forceinline__ int nranks() const { return NR > 0 ? NR : nr; }
-  __device__ __forceinline__ float add(float u) {
-    flag |= !__builtin_isfinite(u);
-    const double d = (double)u;
-    acc += d * d;
-    return u;
-  }
   __device__ __forceinline__ void elem(int64_t j) {
     float r = dec16<DT>(a->ranks[0][flat_off + j]);
     for (int q = 1; q < nranks(); ++q) r = r + dec16<DT>(a->ranks[q][flat_off + j]);
-    red[j] = add(r * inv);
+    const float u = r * inv;
+    ss.add(0, u);
+    red[j] = u;
   }
   template <int U>
-  __device__ __forceinline__ void quads(int64_t j, int64_t stride) {
+  __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
     f32x4 s[U];
     if constexpr (NR > 0) {
       u32x2 raw[NR][U];
@@ -289,11 +297,9 @@ struct ReduceOp {
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      f32x4 u;
-      u.x = add(s[k].x * inv);
-      u.y = add(s[k].y * inv);
-      u.z = add(s[k].z * inv);
-      u.w = add(s[k].w * inv);
+      const f32x4 u = s[k] * inv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss.add(k, u[e]);
       st32x4_nt(red + j + k * stride, u);
     }
   }
@@ -301,7 +307,7 @@ struct ReduceOp {
 
 template <int DT, int NR>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
-  ReduceOp<DT, NR> op{&a, 0, nullptr, a.inv, a.n_ranks, 0.0, 0};
+  ReduceOp<DT, NR> op{&a, 0, nullptr, a.inv, a.n_ranks, SumSq{}};
   for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
     const Chunk ch = a.chunks[c];
     op.flat_off = ch.flat_off;
@@ -309,9 +315,9 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
     const int head = head16(a.ranks[0] + ch.flat_off);
     bool ok = aligned(op.red + head, 16);
     for (int q = 0; q < a.n_ranks; ++q) ok = ok && aligned(a.ranks[q] + ch.flat_off + head, 8);
-    run_chunk<ZS_REDUCE_U>(op, ch.len, head, ok);
+    run_chunk<ZS_REDUCE_U, 4>(op, ch.len, head, ok);
   }
-  finish_stats(op.acc, op.flag, a.sc, a.parts);
+  finish_stats(op.ss.total(), a.sc, a.parts);
 }
 
 // ---------------------------------------------------------------------------
@@ -358,7 +364,7 @@ struct AdamOp {
     if constexpr (CAST) p16[j] = (uint16_t)enc16<DT>(wj);
   }
   template <int U>
-  __device__ __forceinline__ void quads(int64_t j, int64_t stride) {
+  __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
     f32x4 G[U], W[U], M[U], V[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
@@ -458,7 +464,8 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
   }
   if (skip) return;
   AdamOp<DT, GS, CAST> op{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s};
-  for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
+  for (int64_t i = blockIdx.x; i < a.n_chunks; i += gridDim.x) {
+    const int64_t c = ZS_ADAM_REVERSE ? a.n_chunks - 1 - i : i;
     const Chunk ch = a.chunks[c];
     op.w = a.master + ch.state_off;
     op.m = a.m + ch.state_off;
@@ -477,7 +484,7 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
     }
     if constexpr (CAST) ok = ok && aligned(op.p16 + head, 8);
     ok = ok && aligned(op.m + head, 16) && aligned(op.v + head, 16);
-    run_chunk<ZS_ADAM_U>(op, ch.len, head, ok);
+    run_chunk<ZS_ADAM_U, 4>(op, ch.len, head, ok);
   }
 }
 
@@ -490,7 +497,7 @@ struct CastOp {
   uint16_t* p16;
   __device__ __forceinline__ void elem(int64_t j) { p16[j] = (uint16_t)enc16<DT>(w[j]); }
   template <int U>
-  __device__ __forceinline__ void quads(int64_t j, int64_t stride) {
+  __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
     f32x4 W[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) W[k] = ld32x4_nt(w + j + k * stride);
@@ -509,7 +516,7 @@ __global__ void __launch_bounds__(kBlock) cast_kernel(const Chunk* chunks, int64
     op.w = master + ch.state_off;
     op.p16 = reinterpret_cast<uint16_t*>(ch.p16);
     const int head = head16(op.p16);
-    run_chunk<4>(op, ch.len, head, aligned(op.w + head, 16));
+    run_chunk<4, 4>(op, ch.len, head, aligned(op.w + head, 16));
   }
 }
 

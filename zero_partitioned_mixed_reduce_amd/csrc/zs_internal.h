@@ -52,9 +52,8 @@ struct alignas(256) DevScalars {
 static_assert(sizeof(DevScalars) == 256, "scalar block");
 
 struct StatsPart {
-  uint64_t sumsq_bits;  // fp64 partial of one block, as bits
-  uint32_t flag;
-  uint32_t pad;
+  uint64_t sumsq_bits;  // fp64 partial sum of squares of one block, as bits
+  uint64_t pad;
 };
 
 constexpr int64_t kPartsOff = sizeof(DevScalars);

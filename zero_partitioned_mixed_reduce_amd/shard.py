@@ -54,10 +54,7 @@ class ZeroShard:
         self._params, self._grads = params, grads
         self.info = abi.zero_shard_plan(self.desc)
         n = self.info.state_elems
-        self.master = torch.empty(n, dtype=torch.float32, device=device)
-        self.m = torch.empty(n, dtype=torch.float32, device=device)
-        self.v = torch.empty(n, dtype=torch.float32, device=device)
-        self.red = torch.empty(n, dtype=torch.float32, device=device) if with_red else None
+        self.master, self.m, self.v, self.red = self._alloc_state(n, with_red, device)
         self.workspace = torch.empty(self.info.workspace_bytes, dtype=torch.uint8, device=device)
         b = abi.zero_shard_bufs_t()
         b.master, b.m, b.v = self.master.data_ptr(), self.m.data_ptr(), self.v.data_ptr()
@@ -71,6 +68,20 @@ class ZeroShard:
             assert master_init.dtype == torch.float32 and master_init.numel() == self.info.valid_elems
             mi = master_init.data_ptr()
         self.h = abi.zero_shard_init(self.desc, b, mi, _stream())
+
+    # Offset, in floats, between consecutive state arrays carved from one allocation.
+    # None: one allocation per array.
+    state_stagger = None
+
+    def _alloc_state(self, n, with_red, device):
+        k = 4 if with_red else 3
+        if self.state_stagger is None:
+            arrs = [torch.empty(n, dtype=torch.float32, device=device) for _ in range(k)]
+        else:
+            pitch = n + self.state_stagger
+            self._state_store = torch.empty(k * pitch, dtype=torch.float32, device=device)
+            arrs = [self._state_store[i * pitch:i * pitch + n] for i in range(k)]
+        return arrs[0], arrs[1], arrs[2], (arrs[3] if with_red else None)
 
     # step calls (same names as the C ABI)
     def zero_reduce_grads(self, rank_grads, inv_loss_scale):
