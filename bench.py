@@ -36,9 +36,9 @@ def parse():
     p.add_argument("--rank", type=int, default=None, help="data-parallel rank whose shard is stepped")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1 << 26, help="elements of the oracle's timed sample")
-    p.add_argument("--cpu-steps", type=int, default=3)
+    p.add_argument("--cpu-steps", type=int, default=7)
     p.add_argument("--copy-calibration", action="store_true",
-                   help="run one 1 GiB device copy before the timed region (for counter scaling)")
+                   help="run one 1 GiB read + 1 GiB write elementwise kernel first (scales the traffic counters)")
     return p.parse_args()
 
 
@@ -166,17 +166,25 @@ def cpu_baseline(w, sample, steps):
     return n * steps / dt, dt
 
 
-def traffic_from_profiles(cfg, adam_launch_bytes):
-    """HBM bytes per Adam launch from committed rocprofv3 counter summaries, when they
-    were taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"adam_{cfg}_traffic.json")
+def traffic_from_profiles(cfg, rank, adam_launch_bytes):
+    """HBM bytes per Adam launch from the committed rocprofv3 counter summary
+    (profiles/adam_<config>_traffic.txt), when it was taken on the current kernel
+    source and the same shard size; else None."""
+    path = os.path.join(ROOT, "profiles", f"adam_{cfg}_traffic.txt")
     if not os.path.exists(path):
         return None
+    kv = {}
     with open(path) as f:
-        t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_sha():
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
         return None
-    return t.get("traffic_bytes_per_launch")
+    if int(kv.get("algorithmic_bytes_per_launch", -1)) != adam_launch_bytes:
+        return None
+    return int(kv["traffic_bytes_per_launch"])
 
 
 def main():
@@ -199,10 +207,11 @@ def main():
     step_b, adam_b = bytes_per_param(w)
 
     if a.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # a plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB), used to scale
+        # the FETCH_SIZE / WRITE_SIZE counters of the same run
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        src.fill_(7)
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -227,7 +236,7 @@ def main():
     adam_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps
     adam_bytes = adam_b * valid
     achieved = adam_bytes / (adam_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(a.config, adam_bytes)
+    traffic = traffic_from_profiles(a.config, rank, adam_bytes)
     out = {
         "metric": METRIC,
         "value": valid / (ms_step * 1e-3),
