@@ -18,6 +18,7 @@
 // Tuning knobs (measured on MI355X; see the design notes):
 //   ZS_ADAM_U   quads per lane in flight in the Adam pass
 //   ZS_STATS_U  quads per lane in flight in the statistics pass
+//   ZS_STATS_MIN_CHUNKS  minimum chunks per block of a statistics pass
 //   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
 //   ZS_NT_LOAD  non-temporal loads of the fp32 state (read once per step)
 //   ZS_NT_STORE non-temporal stores of the fp32 state and 16-bit parameters
@@ -28,7 +29,10 @@
 #define ZS_ADAM_U 2
 #endif
 #ifndef ZS_STATS_U
-#define ZS_STATS_U 4
+#define ZS_STATS_U 8
+#endif
+#ifndef ZS_STATS_MIN_CHUNKS
+#define ZS_STATS_MIN_CHUNKS 32
 #endif
 #ifndef ZS_REDUCE_U
 #define ZS_REDUCE_U 2
@@ -172,10 +176,20 @@ __device__ void finish_stats(double acc, DevScalars* sc, StatsPart* parts) {
   }
   __syncthreads();
   if (!is_last) return;
+  // every load of this thread is issued before any is consumed (one memory round trip,
+  // not one per partial); the partials are then added in block order
+  constexpr int kPer = kMaxStatsBlocks / kBlock;
+  double v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const uint32_t b = threadIdx.x + i * kBlock;
+    v[i] = b < gridDim.x ? __longlong_as_double((long long)__hip_atomic_load(
+                               &parts[b].sumsq_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                         : 0.0;
+  }
   double s = 0.0;
-  for (uint32_t b = threadIdx.x; b < gridDim.x; b += kBlock)
-    s += __longlong_as_double(
-        (long long)__hip_atomic_load(&parts[b].sumsq_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) s += v[i];
   const double total = block_sum(s, lds);
   if (threadIdx.x == 0) {
     sc->local_sumsq = total;
@@ -563,6 +577,15 @@ static unsigned clamp_grid(int64_t n_chunks, int64_t cap) {
   return (unsigned)(g < 1 ? 1 : g);
 }
 
+// Grid of a statistics pass: each block finishes with a device-scope atomic on
+// one counter (plus its release and acquire), so a block should carry at least
+// ZS_STATS_MIN_CHUNKS chunks; capped by the partial-sum slots and the device.
+static unsigned stats_grid(int64_t n_chunks, int64_t grid_cap) {
+  int64_t cap = grid_cap < kMaxStatsBlocks ? grid_cap : kMaxStatsBlocks;
+  int64_t want = (n_chunks + ZS_STATS_MIN_CHUNKS - 1) / ZS_STATS_MIN_CHUNKS;
+  return clamp_grid(want, cap);
+}
+
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
                           DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st) {
   if (n_chunks == 0) {
@@ -570,7 +593,7 @@ hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, cons
     return hipGetLastError();
   }
   StatsArgs a{chunks, n_chunks, flat_g, inv, sc, parts};
-  const unsigned g = clamp_grid(n_chunks, grid_cap < kMaxStatsBlocks ? grid_cap : kMaxStatsBlocks);
+  const unsigned g = stats_grid(n_chunks, grid_cap);
   if (dtype == ZERO_BF16)
     hipLaunchKernelGGL(stats16_kernel<ZERO_BF16>, dim3(g), dim3(kBlock), 0, st, a);
   else
@@ -604,7 +627,7 @@ hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const
   a.red = red;
   a.sc = sc;
   a.parts = parts;
-  const unsigned g = clamp_grid(n_chunks, grid_cap < kMaxStatsBlocks ? grid_cap : kMaxStatsBlocks);
+  const unsigned g = stats_grid(n_chunks, grid_cap);
   if (dtype == ZERO_BF16)
     launch_reduce_dt<ZERO_BF16>(a, g, st);
   else

@@ -20,6 +20,7 @@ constexpr int kMaxStatsBlocks = 4096;
 // Local-reduce fan-in limit (rank pointers travel as kernel arguments).
 constexpr int kMaxRanks = 64;
 constexpr int kBlock = 256;
+static_assert(kMaxStatsBlocks % kBlock == 0, "partials are read kMaxStatsBlocks / kBlock per thread");
 
 // One work item: a run of `len` consecutive shard elements inside one tensor.
 struct alignas(16) Chunk {
