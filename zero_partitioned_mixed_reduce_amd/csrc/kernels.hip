@@ -579,10 +579,14 @@ static unsigned clamp_grid(int64_t n_chunks, int64_t cap) {
 
 // Grid of a statistics pass: each block finishes with a device-scope atomic on
 // one counter (plus its release and acquire), so a block should carry at least
-// ZS_STATS_MIN_CHUNKS chunks; capped by the partial-sum slots and the device.
+// ZS_STATS_MIN_CHUNKS chunks -- but small shards still get up to 256 blocks (one
+// block per CU) so that no block walks a long serial run of chunks.  Capped by
+// the partial-sum slots and the device.
 static unsigned stats_grid(int64_t n_chunks, int64_t grid_cap) {
-  int64_t cap = grid_cap < kMaxStatsBlocks ? grid_cap : kMaxStatsBlocks;
+  const int64_t cap = grid_cap < kMaxStatsBlocks ? grid_cap : kMaxStatsBlocks;
   int64_t want = (n_chunks + ZS_STATS_MIN_CHUNKS - 1) / ZS_STATS_MIN_CHUNKS;
+  const int64_t floor_blocks = n_chunks < 256 ? n_chunks : 256;
+  if (want < floor_blocks) want = floor_blocks;
   return clamp_grid(want, cap);
 }
 
