@@ -22,9 +22,7 @@
 //   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
 //   ZS_NT_LOAD  non-temporal loads of the fp32 state (read once per step)
 //   ZS_NT_STORE non-temporal stores of the fp32 state and 16-bit parameters
-//   ZS_ADAM_REVERSE  the Adam pass walks the chunks last to first, so that its
-//               re-read of the gradient starts with what the statistics pass
-//               read most recently (still in the last-level cache)
+//   ZS_ADAM_SPLIT    parts per chunk in the Adam pass (one block per part)
 #ifndef ZS_ADAM_U
 #define ZS_ADAM_U 2
 #endif
@@ -37,8 +35,8 @@
 #ifndef ZS_REDUCE_U
 #define ZS_REDUCE_U 2
 #endif
-#ifndef ZS_ADAM_REVERSE
-#define ZS_ADAM_REVERSE 0
+#ifndef ZS_ADAM_SPLIT
+#define ZS_ADAM_SPLIT 4
 #endif
 #ifndef ZS_NT_LOAD
 #define ZS_NT_LOAD 1
@@ -478,27 +476,34 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
   }
   if (skip) return;
   AdamOp<DT, GS, CAST> op{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s};
-  for (int64_t i = blockIdx.x; i < a.n_chunks; i += gridDim.x) {
-    const int64_t c = ZS_ADAM_REVERSE ? a.n_chunks - 1 - i : i;
-    const Chunk ch = a.chunks[c];
-    op.w = a.master + ch.state_off;
-    op.m = a.m + ch.state_off;
-    op.v = a.v + ch.state_off;
-    op.p16 = reinterpret_cast<uint16_t*>(ch.p16);
+  // Work item i is part i % ZS_ADAM_SPLIT of chunk i / ZS_ADAM_SPLIT: one short-lived block per
+  // part, scheduled by the hardware dispatcher (measured faster than a persistent grid here).
+  const int64_t n_items = a.n_chunks * ZS_ADAM_SPLIT;
+  for (int64_t i = blockIdx.x; i < n_items; i += gridDim.x) {
+    const Chunk ch = a.chunks[i / ZS_ADAM_SPLIT];
+    const int64_t part = i % ZS_ADAM_SPLIT;
+    const int64_t sub = ((ch.len + ZS_ADAM_SPLIT - 1) / ZS_ADAM_SPLIT + 7) & ~(int64_t)7;
+    const int64_t lo = part * sub;
+    if (lo >= ch.len) continue;
+    const int64_t len = (lo + sub < ch.len ? lo + sub : ch.len) - lo;
+    op.w = a.master + ch.state_off + lo;
+    op.m = a.m + ch.state_off + lo;
+    op.v = a.v + ch.state_off + lo;
+    op.p16 = reinterpret_cast<uint16_t*>(ch.p16) + lo;
     int head;
     bool ok;
     if constexpr (GS == kGradRed) {
-      op.gred = a.red + ch.state_off;
+      op.gred = a.red + ch.state_off + lo;
       head = head16(op.p16);
       ok = aligned(op.w + head, 16) && aligned(op.gred + head, 16);
     } else {
-      op.g16 = GS == kGradFlat16 ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
+      op.g16 = (GS == kGradFlat16 ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16)) + lo;
       head = head16(op.g16);
       ok = aligned(op.w + head, 16) && aligned(op.g16 + head, 8);
     }
     if constexpr (CAST) ok = ok && aligned(op.p16 + head, 8);
     ok = ok && aligned(op.m + head, 16) && aligned(op.v + head, 16);
-    run_chunk<ZS_ADAM_U, 4>(op, ch.len, head, ok);
+    run_chunk<ZS_ADAM_U, 4>(op, len, head, ok);
   }
 }
 
@@ -655,7 +660,7 @@ static void launch_adam_dt(const AdamArgs& a, int gs, bool cast, unsigned g, hip
 }
 
 hipError_t launch_adam(int dtype, int grad_source, bool cast, const AdamArgs& a, int64_t grid_cap, hipStream_t st) {
-  const unsigned g = clamp_grid(a.n_chunks, grid_cap);
+  const unsigned g = clamp_grid(a.n_chunks * ZS_ADAM_SPLIT, grid_cap);
   if (dtype == ZERO_BF16)
     launch_adam_dt<ZERO_BF16>(a, grad_source, cast, g, st);
   else

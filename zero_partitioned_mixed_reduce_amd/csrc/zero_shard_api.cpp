@@ -94,13 +94,16 @@ struct DeviceGuard {
   }
 };
 
+// Grid cap of the streaming kernels, in blocks per CU.  The default leaves the
+// grid at one block per work item (the hardware dispatcher balances the load);
+// ZERO_SHARD_BLOCKS_PER_CU caps it to make the kernels persistent instead.
 int64_t blocks_per_cu() {
   const char* e = getenv("ZERO_SHARD_BLOCKS_PER_CU");
   if (e) {
     long v = strtol(e, nullptr, 10);
-    if (v >= 1 && v <= 64) return v;
+    if (v >= 1 && v <= 65536) return v;
   }
-  return 8;
+  return 65536;
 }
 
 zero_status_t sync_read_scalars(zero_shard* h, hipStream_t st, zs::DevScalars* out) {
@@ -171,7 +174,8 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
   h->chunks = reinterpret_cast<zs::Chunk*>(ws + zs::kChunksOff);
   h->n_chunks = (int64_t)p.chunks.size();
   h->grid_main = (int64_t)cus * blocks_per_cu();
-  h->grid_stats = h->grid_main < zs::kMaxStatsBlocks ? h->grid_main : zs::kMaxStatsBlocks;
+  // statistics passes stay persistent: at most 8 resident blocks per CU (and the partial slots)
+  h->grid_stats = (int64_t)cus * 8 < zs::kMaxStatsBlocks ? (int64_t)cus * 8 : zs::kMaxStatsBlocks;
   h->phase = kReady;
   h->cast_pending = false;
   h->adam_calls = 0;
