@@ -18,22 +18,34 @@
 // Tuning knobs (measured on MI355X; see the design notes):
 //   ZS_ADAM_U   quads per lane in flight in the Adam pass
 //   ZS_STATS_U  quads per lane in flight in the statistics pass
+//   ZS_STATS_V  elements per lane per group in the statistics pass (4: 8-byte loads, 8: 16-byte)
+//   ZS_STATS_NT non-temporal gradient loads in the statistics pass
 //   ZS_STATS_MIN_CHUNKS  minimum chunks per block of a statistics pass
 //   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
 //   ZS_NT_LOAD  non-temporal loads of the fp32 state (read once per step)
 //   ZS_NT_STORE non-temporal stores of the fp32 state and 16-bit parameters
 //   ZS_ADAM_SPLIT    parts per chunk in the Adam pass (one block per part)
+//   ZS_ADAM_BLOCK    threads per block of the Adam pass
 #ifndef ZS_ADAM_U
 #define ZS_ADAM_U 2
 #endif
 #ifndef ZS_STATS_U
 #define ZS_STATS_U 8
 #endif
+#ifndef ZS_STATS_V
+#define ZS_STATS_V 4
+#endif
+#ifndef ZS_STATS_NT
+#define ZS_STATS_NT 0
+#endif
 #ifndef ZS_STATS_MIN_CHUNKS
 #define ZS_STATS_MIN_CHUNKS 32
 #endif
 #ifndef ZS_REDUCE_U
 #define ZS_REDUCE_U 2
+#endif
+#ifndef ZS_ADAM_BLOCK
+#define ZS_ADAM_BLOCK 256
 #endif
 #ifndef ZS_ADAM_SPLIT
 #define ZS_ADAM_SPLIT 4
@@ -49,6 +61,7 @@ namespace zs {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // 16-bit formats
@@ -92,6 +105,20 @@ __device__ __forceinline__ u32x2 enc16x4(f32x4 w) {
 }
 
 __device__ __forceinline__ u32x2 ld16x4(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ u32x2 ld16x4_stats(const uint16_t* p) {
+#if ZS_STATS_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+#else
+  return *reinterpret_cast<const u32x2*>(p);
+#endif
+}
+__device__ __forceinline__ u32x4 ld16x8(const uint16_t* p) {
+#if ZS_STATS_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
 __device__ __forceinline__ void st16x4_nt(uint16_t* p, u32x2 v) {
 #if ZS_NT_STORE
   __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
@@ -119,6 +146,10 @@ __device__ __forceinline__ bool aligned(const void* p, uintptr_t a) { return ((u
 
 // Leading elements before a 16-bit pointer reaches an 8-byte boundary (0..3).
 __device__ __forceinline__ int head16(const uint16_t* p) { return (int)(((8u - ((uintptr_t)p & 7u)) & 7u) >> 1); }
+// Leading elements before a 16-bit pointer reaches a 16-byte boundary (0..7).
+__device__ __forceinline__ int head16x8(const uint16_t* p) {
+  return (int)(((16u - ((uintptr_t)p & 15u)) & 15u) >> 1);
+}
 
 // ---------------------------------------------------------------------------
 // chunk driver
@@ -127,19 +158,19 @@ __device__ __forceinline__ int head16(const uint16_t* p) { return (int)(((8u - (
 // V consecutive elements per lane (U groups in flight, each wave covering 64*V
 // consecutive elements per group slot), then a tail of fewer than V elements.
 // When the streams are not co-aligned (vec_ok false) every element goes one per lane.
-template <int U, int V, class Op>
+template <int U, int V, class Op, int BS = kBlock>
 __device__ __forceinline__ void run_chunk(Op& op, int64_t len, int head, bool vec_ok) {
   const int64_t tid = threadIdx.x;
   if (!vec_ok) {
-    for (int64_t j = tid; j < len; j += kBlock) op.elem(j);
+    for (int64_t j = tid; j < len; j += BS) op.elem(j);
     return;
   }
   if (head > len) head = (int)len;
   if (tid < head) op.elem(tid);
   const int64_t ng = (len - head) / V;  // whole groups in the body
   int64_t q = tid;
-  for (; q + (U - 1) * kBlock < ng; q += U * kBlock) op.template groups<U>(head + V * q, V * kBlock);
-  for (; q < ng; q += kBlock) op.template groups<1>(head + V * q, 0);
+  for (; q + (U - 1) * BS < ng; q += U * BS) op.template groups<U>(head + V * q, V * BS);
+  for (; q < ng; q += BS) op.template groups<1>(head + V * q, 0);
   const int64_t t0 = head + V * ng;
   if (tid < len - t0) op.elem(t0 + tid);
 }
@@ -223,15 +254,30 @@ struct Stats16Op {
   __device__ __forceinline__ void elem(int64_t j) { ss.add(0, dec16<DT>(g[j]) * inv); }
   template <int U>
   __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
-    u32x2 r[U];
+#if ZS_STATS_V == 8
+    u32x4 r[U];  // 8 elements per group: 16-byte loads
 #pragma unroll
-    for (int k = 0; k < U; ++k) r[k] = ld16x4(g + j + k * stride);
+    for (int k = 0; k < U; ++k) r[k] = ld16x8(g + j + k * stride);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const f32x4 lo = dec16x4<DT>(u32x2{r[k].x, r[k].y});
+      const f32x4 hi = dec16x4<DT>(u32x2{r[k].z, r[k].w});
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss.add(k, lo[e] * inv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss.add(k, hi[e] * inv);
+    }
+#else
+    u32x2 r[U];  // 4 elements per group: 8-byte loads
+#pragma unroll
+    for (int k = 0; k < U; ++k) r[k] = ld16x4_stats(g + j + k * stride);
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const f32x4 x = dec16x4<DT>(r[k]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) ss.add(k, x[e] * inv);
     }
+#endif
   }
 };
 
@@ -250,7 +296,11 @@ __global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
   for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
     const Chunk ch = a.chunks[c];
     op.g = a.flat_g ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
+#if ZS_STATS_V == 8
+    run_chunk<ZS_STATS_U, 8>(op, ch.len, head16x8(op.g), true);
+#else
     run_chunk<ZS_STATS_U, 4>(op, ch.len, head16(op.g), true);
+#endif
   }
   finish_stats(op.ss.total(), a.sc, a.parts);
 }
@@ -462,7 +512,7 @@ __device__ __forceinline__ int step_scalars(const AdamArgs& a, AdamScalars& s, S
 }
 
 template <int DT, int GS, bool CAST>
-__global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
+__global__ void __launch_bounds__(ZS_ADAM_BLOCK) adam_kernel(AdamArgs a) {
   AdamScalars s;
   Slot next;
   double norm;
@@ -503,7 +553,7 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(AdamArgs a) {
     }
     if constexpr (CAST) ok = ok && aligned(op.p16 + head, 8);
     ok = ok && aligned(op.m + head, 16) && aligned(op.v + head, 16);
-    run_chunk<ZS_ADAM_U, 4>(op, len, head, ok);
+    run_chunk<ZS_ADAM_U, 4, AdamOp<DT, GS, CAST>, ZS_ADAM_BLOCK>(op, len, head, ok);
   }
 }
 
@@ -647,9 +697,9 @@ hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const
 template <int DT, int GS>
 static void launch_adam_gs(const AdamArgs& a, bool cast, unsigned g, hipStream_t st) {
   if (cast)
-    hipLaunchKernelGGL((adam_kernel<DT, GS, true>), dim3(g), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((adam_kernel<DT, GS, true>), dim3(g), dim3(ZS_ADAM_BLOCK), 0, st, a);
   else
-    hipLaunchKernelGGL((adam_kernel<DT, GS, false>), dim3(g), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((adam_kernel<DT, GS, false>), dim3(g), dim3(ZS_ADAM_BLOCK), 0, st, a);
 }
 
 template <int DT>
