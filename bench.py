@@ -43,10 +43,15 @@ def parse():
 
 
 def kernel_source_sha():
+    """Hash of the device code's source (kernels.hip and zs_internal.h) with // comments and
+    blank lines removed: counter summaries stay valid across comment-only edits."""
     h = hashlib.sha256()
     for f in ("kernels.hip", "zs_internal.h"):
-        with open(os.path.join(ROOT, "zero_partitioned_mixed_reduce_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "zero_partitioned_mixed_reduce_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

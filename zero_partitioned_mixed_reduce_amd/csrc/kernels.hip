@@ -1,15 +1,19 @@
 // gfx950 kernels of the partitioned mixed-precision optimizer step.
 //
-// Every kernel walks the shard's chunk table with a persistent grid (block b
-// takes chunks b, b + G, b + 2G, ...).  Inside a chunk a block peels at most 3
-// leading elements, streams the body as 4-element quads -- 8-byte loads and
-// stores of 16-bit data, 16-byte loads and stores of fp32 data, each wave
-// covering 256 consecutive elements per quad slot so every memory instruction
-// is fully coalesced -- with U quads per lane in flight, then finishes a tail
-// of at most 3 elements.  Chunks whose streams are not co-aligned fall back to
-// one element per lane.  Per-element arithmetic is plain fp32 (compiled with
-// -ffp-contract=off and the default correctly rounded division and square
-// root), identical in the vector and scalar paths.
+// The kernels walk the shard's chunk table (chunks of at most kChunk elements
+// inside one tensor piece).  The statistics passes use a persistent grid sized
+// by work (block b takes chunks b, b + G, ...; each block ends with one
+// completion atomic, so blocks are few); the Adam pass launches one short-lived
+// block per part of a chunk and lets the hardware dispatcher balance the load.
+// Inside a run of elements a block peels at most 3 leading elements, streams
+// the body as 4-element quads -- 8-byte loads and stores of 16-bit data,
+// 16-byte loads and stores of fp32 data, each wave covering 256 consecutive
+// elements per quad slot so every memory instruction is fully coalesced --
+// with U quads per lane in flight, then finishes a tail of at most 3 elements.
+// Runs whose streams are not co-aligned fall back to one element per lane.
+// Per-element arithmetic is plain fp32 (compiled with -ffp-contract=off and
+// the default correctly rounded division and square root), identical in the
+// vector and scalar paths.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
