@@ -1,0 +1,30 @@
+"""bench.py on the CPU: byte accounting and the one-GPU contract."""
+import json
+import subprocess
+import sys
+import os
+
+import bench
+from synth import recipes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bytes_per_param():
+    assert bench.bytes_per_param(recipes.full7p5b()) == (30, 28)
+    assert bench.bytes_per_param(recipes.zero1_7p5b()) == (30, 28)
+    assert bench.bytes_per_param(recipes.reduce8()) == (50, 30)       # 2*8 + 4 + 4 + 26
+    assert bench.bytes_per_param(recipes.tiny()) == (42, 30)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "8"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_traffic_summary_is_tied_to_the_kernel_source():
+    # a committed summary is only used for the shard size it was taken on
+    assert bench.traffic_from_profiles("full7p5b", 0, 1) is None
+    assert bench.traffic_from_profiles("no_such_config", 0, 1) is None

@@ -100,7 +100,8 @@ def gpu_params_at(wl, flat_idx):
     return out
 
 
-@pytest.mark.parametrize("cfg,rank", [("zero1_7p5b", 63), ("gpt2", 7), ("reduce8", 7), ("full7p5b", 0)])
+@pytest.mark.parametrize("cfg,rank", [("zero1_7p5b", 0), ("zero1_7p5b", 63), ("gpt2", 7), ("gpt2", 3), ("reduce8", 7),
+                                      ("reduce8", 0), ("full7p5b", 0)])
 def test_full_size_sampled(cfg, rank):
     import bench
     w = recipes.ALL[cfg]()
