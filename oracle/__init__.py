@@ -57,6 +57,11 @@ def lib():
         L.orc_grad_stats.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
                                      ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
         L.orc_grad_stats.restype = ctypes.c_int
+        L.orc_accumulate.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_int]
+        L.orc_stats_f32.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                                    ctypes.POINTER(ctypes.c_double)]
+        L.orc_stats_f32.restype = ctypes.c_int
         L.orc_clip_coef.argtypes = [ctypes.c_double, ctypes.c_float, ctypes.POINTER(ctypes.c_double)]
         L.orc_clip_coef.restype = ctypes.c_float
         L.orc_next_scalars.argtypes = [ctypes.POINTER(HParams), ctypes.POINTER(Counters),
@@ -144,6 +149,24 @@ def grad_stats(dtype, srcs, inv_loss_scale, sumsq_acc=0.0):
     return u, bool(flag), acc.value
 
 
+def accumulate(dtype, srcs, acc, first):
+    """acc (float32, in place) = s or acc + s, with s the rank-order fp32 sum of srcs."""
+    srcs = [_u16(np.ascontiguousarray(x)) for x in srcs]
+    acc = _f32(acc)
+    assert all(x.size == acc.size for x in srcs)
+    arr = (ctypes.c_void_p * len(srcs))(*[x.ctypes.data for x in srcs])
+    lib().orc_accumulate(dtype, arr, len(srcs), acc.size, _ptr(acc), int(bool(first)))
+
+
+def stats_f32(acc, inv_loss_scale, sumsq_acc=0.0):
+    """(u, flag, sumsq) of an accumulated fp32 gradient."""
+    acc = _f32(np.ascontiguousarray(acc, dtype=np.float32))
+    u = np.empty(acc.size, np.float32)
+    ss = ctypes.c_double(sumsq_acc)
+    flag = lib().orc_stats_f32(_ptr(acc), acc.size, ctypes.c_float(inv_loss_scale), _ptr(u), ctypes.byref(ss))
+    return u, bool(flag), ss.value
+
+
 def clip_coef(global_sumsq, max_norm):
     norm = ctypes.c_double()
     c = lib().orc_clip_coef(global_sumsq, ctypes.c_float(max_norm), ctypes.byref(norm))
@@ -196,6 +219,22 @@ class RankState:
         self.counters = Counters.fresh()
 
 
+def step_ranks_accumulated(states, micro_grads, begins, inv_loss_scale, max_norm, hp, extra_found_inf=False):
+    """One optimizer step over K micro-steps: micro_grads[k] is the list of flat
+    uint16 buffers of micro-step k (one already-reduced buffer, or one per rank).
+    Each rank accumulates its slice over the micro-steps in fp32, then the step
+    proceeds as in step_ranks on the accumulated gradient."""
+    nd = len(states)
+    locs = []
+    for r, st in enumerate(states):
+        n, b = st.w.size, begins[r]
+        acc = np.zeros(n, np.float32)
+        for k, grads in enumerate(micro_grads):
+            accumulate(st.dtype, [g[b:b + n] for g in grads], acc, first=(k == 0))
+        locs.append(stats_f32(acc, inv_loss_scale))
+    return _finish_step(states, locs, nd, max_norm, hp, extra_found_inf)
+
+
 def step_ranks(states, rank_grads, begins, inv_loss_scale, max_norm, hp, extra_found_inf=False):
     """One optimizer step of every simulated rank.
 
@@ -212,6 +251,11 @@ def step_ranks(states, rank_grads, begins, inv_loss_scale, max_norm, hp, extra_f
         b = begins[r]
         u, flag, ss = grad_stats(st.dtype, [g[b:b + n] for g in rank_grads], inv_loss_scale)
         locs.append((u, flag, ss))
+    return _finish_step(states, locs, nd, max_norm, hp, extra_found_inf)
+
+
+def _finish_step(states, locs, nd, max_norm, hp, extra_found_inf):
+    """Exchange of flags and sums between the ranks, then each rank's update and cast."""
     out = []
     for r, st in enumerate(states):
         u, flag, ss = locs[r]

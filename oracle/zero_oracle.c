@@ -151,6 +151,34 @@ int orc_grad_stats(int dtype, const uint16_t* const* src, int n_src, int64_t n, 
   return flag;
 }
 
+/* Gradient accumulation over micro-steps ("DeepSpeed ZeRO", ZeRO Stage 2: with
+ * gradient accumulation every backward reduce-scatters and the rank adds its
+ * 1/N_d slice to what it has accumulated).  s = g_0 + g_1 + ... in fp32 rank
+ * order (one source = already reduced); acc = s on the first micro-step, else
+ * acc = acc + s. */
+void orc_accumulate(int dtype, const uint16_t* const* src, int n_src, int64_t n, float* acc, int first) {
+  for (int64_t i = 0; i < n; ++i) {
+    float s = dec16(dtype, src[0][i]);
+    for (int q = 1; q < n_src; ++q) s = s + dec16(dtype, src[q][i]);
+    acc[i] = first ? s : acc[i] + s;
+  }
+}
+
+/* Intake of an accumulated fp32 gradient: u = acc * inv_loss_scale, flag = any u
+ * not finite, *sumsq_acc += u^2 in fp64 in index order.  Returns the flag. */
+int orc_stats_f32(const float* acc, int64_t n, float inv_loss_scale, float* u, double* sumsq_acc) {
+  int flag = 0;
+  double a = *sumsq_acc;
+  for (int64_t i = 0; i < n; ++i) {
+    float ui = acc[i] * inv_loss_scale;
+    if (!isfinite(ui)) flag = 1;
+    a = a + (double)ui * (double)ui;
+    u[i] = ui;
+  }
+  *sumsq_acc = a;
+  return flag;
+}
+
 /* Global-norm clipping coefficient.  norm = sqrt(global sum of squares);
  * coefficient = max_norm / (norm + 1e-6) when that is below 1, else 1; a
  * non-positive max_norm disables clipping. */

@@ -592,3 +592,69 @@ def test_c_oracle_equals_numpy_oracle_tiny_config():
         assert (states[r].m.view(np.uint32) == np_m[r].view(np.uint32)).all()
         assert (states[r].v.view(np.uint32) == np_v[r].view(np.uint32)).all()
         assert (states[r].p16 == onp.enc(dtype, np_w[r])).all()
+
+
+# --------------------------------------------------------------------------
+# gradient accumulation over micro-steps ("DeepSpeed ZeRO", ZeRO Stage 2, 梯度累积)
+
+
+def test_accumulation_exact_on_integer_grid():
+    nd, n, K = 8, 3000, 4
+    ks = rng.integers(-256, 257, size=(K, nd, n))
+    acc = np.zeros(n, np.float32)
+    for k in range(K):
+        bufs = [oracle.encode16(F16, (ks[k, q] * 2.0 ** -8).astype(np.float32)) for q in range(nd)]
+        oracle.accumulate(F16, bufs, acc, first=(k == 0))
+    assert (acc.astype(np.float64) == ks.sum(axis=(0, 1)) * 2.0 ** -8).all()
+    u, flag, ss = oracle.stats_f32(acc, 0.25)
+    assert not flag and (u.astype(np.float64) == ks.sum(axis=(0, 1)) * 2.0 ** -10).all()
+
+
+def test_accumulation_adds_the_reduced_micro_step():
+    # the micro-step's reduce-scatter result s = g_0 + g_1 is formed first, then added:
+    # acc = 1, s = 2^-24 + 2^-24 = 2^-23 gives 1 + 2^-23; adding g_0 then g_1 to acc would give 1
+    one = oracle.encode16(BF16, np.array([1.0], np.float32))
+    tiny = oracle.encode16(BF16, np.array([2.0 ** -24], np.float32))
+    acc = np.zeros(1, np.float32)
+    oracle.accumulate(BF16, [one], acc, first=True)
+    oracle.accumulate(BF16, [tiny, tiny], acc, first=False)
+    assert acc[0] == np.float32(1.0 + 2.0 ** -23)
+
+
+def test_single_micro_step_equals_plain_intake():
+    bufs = [rand16(F16, 5000, 300.0, 40 + q) for q in range(3)]
+    acc = np.full(5000, 7.0, np.float32)          # overwritten by the first micro-step
+    oracle.accumulate(F16, bufs, acc, first=True)
+    u1, f1, s1 = oracle.stats_f32(acc, 1 / 1024)
+    u2, f2, s2 = oracle.grad_stats(F16, bufs, 1 / 1024)
+    assert (u1.view(np.uint32) == u2.view(np.uint32)).all() and f1 == f2 and s1 == s2
+
+
+def test_overflow_in_any_micro_step_skips():
+    states, begins, _, _ = make_states(F16, 2, [4000], 8)
+    before = snapshot(states)
+    micro = [[rand16(F16, 4000, 100.0, 60 + k)] for k in range(3)]
+    micro[1][0] = micro[1][0].copy()
+    micro[1][0][123] = 0x7C00
+    res = oracle.step_ranks_accumulated(states, micro, begins, 1 / 1024, 1.0, hp_of())
+    assert [r["flag"] for r in res] == [True, False] and all(r["skipped"] for r in res)
+    assert all((a[0].view(np.uint32) == b[0].view(np.uint32)).all() for a, b in zip(before, snapshot(states)))
+
+
+@pytest.mark.parametrize("nd", [2, 5])
+def test_partition_invariance_with_accumulation(nd):
+    dtype, psi, K = F16, 6001, 3
+    hp = hp_of()
+    states, begins, p16_full, master = make_states(dtype, nd, [psi], 13)
+    whole = oracle.RankState(dtype, p16_full, master)
+    micro = [[rand16(dtype, psi, 100.0, 500 + 10 * k + q) for q in range(nd)] for k in range(K)]
+    res = oracle.step_ranks_accumulated(states, micro, begins, 1 / 1024, 1.0, hp)
+    acc = np.zeros(psi, np.float32)
+    for k in range(K):
+        oracle.accumulate(dtype, micro[k], acc, first=(k == 0))
+    u, flag, _ = oracle.stats_f32(acc, 1 / 1024)
+    oracle.adam(flag, u, res[0]["clip"], hp, whole.counters, whole.w, whole.m, whole.v)
+    oracle.cast(dtype, whole.w, whole.p16)
+    for name in ("w", "m", "v", "p16"):
+        cat = np.concatenate([getattr(st, name) for st in states])
+        assert (cat.view(np.uint8) == getattr(whole, name).view(np.uint8)).all(), name
