@@ -34,6 +34,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", default="full7p5b", choices=["tiny", "gpt2", "zero1_7p5b", "reduce8", "full7p5b"])
     p.add_argument("--rank", type=int, default=None, help="data-parallel rank whose shard is stepped")
+    p.add_argument("--micro-steps", type=int, default=1,
+                   help="gradient-accumulation micro-steps per optimizer step (K - 1 accumulations, then the "
+                        "step's own intake)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1 << 26, help="elements of the oracle's timed sample")
     p.add_argument("--cpu-steps", type=int, default=7)
@@ -58,12 +61,12 @@ def kernel_source_sha():
 class Workload:
     """Device-resident inputs and the library handle for one rank."""
 
-    def __init__(self, w, rank):
+    def __init__(self, w, rank, micro_steps=1):
         import torch
         import synth
         from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
 
-        self.w, self.rank = w, rank
+        self.w, self.rank, self.micro_steps = w, rank, micro_steps
         dt = w.dtype
         psi = w.psi
         starts = [0]
@@ -103,7 +106,8 @@ class Workload:
         if valid:
             synth.gpu_normal_f32(mi, w.seed, mstream, first=b, sigma=w.master_sigma)
         self.shard = ZeroShard(w.numel, w.nd, rank, dt, self.params, grads=grads_reg,
-                               master_init=mi if w.master_given else None, with_red=(w.grad_mode == "reduce"))
+                               master_init=mi if w.master_given else None,
+                               with_red=(w.grad_mode == "reduce" or micro_steps > 1))
         del mi
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -115,6 +119,8 @@ class Workload:
 
     def step(self, ev=None):
         s, w = self.shard, self.w
+        for _ in range(self.micro_steps - 1):
+            s.zero_accumulate_grads(self.rank_grads)      # the same gradient buffers every micro-step
         if ev:
             ev[0].record()
         s.zero_reduce_grads(self.rank_grads, self.inv)
@@ -128,15 +134,20 @@ class Workload:
             ev[2].record()
 
 
-def bytes_per_param(w):
-    """Dependency-minimal HBM bytes per shard parameter for the whole step, and for the Adam pass."""
-    if w.grad_mode == "reduce":
-        step = 2 * w.nd + 4 + 4 + 26        # read N_d x 16-bit, write fp32 u; Adam reads u
-        adam = 4 + 12 + 12 + 2
-    else:
-        step = 2 + 2 + 12 + 12 + 2          # statistics pass re-reads the 16-bit gradient
-        adam = 2 + 12 + 12 + 2
-    return step, adam
+def bytes_per_param(w, micro_steps=1):
+    """Dependency-minimal HBM bytes per shard parameter for the whole step, and for the Adam pass.
+
+    One micro-step reads its sources (2 B per rank buffer, or 2 B of already-reduced
+    gradient); the first accumulation writes the fp32 accumulator (4 B), later ones
+    read and write it (8 B); the step's intake on top of an accumulation reads it and
+    writes u (8 B); the Adam pass then reads u (4 B) instead of the 16-bit gradient."""
+    src = 2 * w.nd if w.grad_mode == "reduce" else 2
+    if micro_steps <= 1:
+        if w.grad_mode == "reduce":
+            return src + 4 + 4 + 26, 4 + 12 + 12 + 2      # write fp32 u; Adam reads u
+        return src + 2 + 12 + 12 + 2, 2 + 12 + 12 + 2    # statistics pass, then Adam re-reads the gradient
+    step = (src + 4) + (micro_steps - 2) * (src + 8) + (src + 8) + (4 + 12 + 12 + 2)
+    return step, 4 + 12 + 12 + 2
 
 
 def cpu_baseline(w, sample, steps):
@@ -206,10 +217,10 @@ def main():
     rank = a.rank if a.rank is not None else w.ranks[0]
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
-    wl = Workload(w, rank)
+    wl = Workload(w, rank, a.micro_steps)
     setup_s = time.perf_counter() - t_setup
     valid = wl.info.valid_elems
-    step_b, adam_b = bytes_per_param(w)
+    step_b, adam_b = bytes_per_param(w, a.micro_steps)
 
     if a.copy_calibration:
         # a plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB), used to scale
@@ -258,11 +269,13 @@ def main():
         "config": {"workload": w.name, "psi": w.psi, "dp_size": w.nd, "dp_rank": rank, "shard_params": valid,
                    "param_grad_dtype": DTYPE_NAME[w.dtype], "grad_source": w.grad_mode,
                    "tensors": len(w.numel), "loss_scale": w.loss_scale, "max_norm": w.max_norm,
+                   "micro_steps": a.micro_steps,
                    "adam": w.hp},
         "hbm_gbps_step": step_b * valid / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": step_b * valid / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "bytes_per_param_step": step_b,
-        "breakdown_ms": {"intake_stats": stats_ms, "norm_adam_cast": adam_ms},
+        "breakdown_ms": {"accumulate": ms_step - stats_ms - adam_ms if a.micro_steps > 1 else 0.0,
+                         "intake_stats": stats_ms, "norm_adam_cast": adam_ms},
         "roofline": {"kernel": "adam_kernel (Adam + fused 16-bit write-back)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,

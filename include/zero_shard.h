@@ -124,6 +124,22 @@ zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* 
 zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
                               const float* master_init, void* stream, zero_shard_t* out);
 
+/* Gradient accumulation ("DeepSpeed ZeRO", ZeRO Stage 2 under gradient
+ * accumulation: every micro-step's backward is reduce-scattered and the rank
+ * adds its 1/N_d slice to what it has accumulated).  Sources as in
+ * zero_reduce_grads (0: the registered gradient, 1: a flat already-reduced
+ * gradient, N_d: the ranks' buffers); s = their rank-order fp32 sum on this
+ * shard; the first micro-step of a step sets acc = s, later ones acc = acc + s,
+ * with acc in bufs.red (required).  No statistics.  The step then calls
+ * zero_reduce_grads, which adds its own sources (the last micro-step) to acc,
+ * or, with n_ranks = ZERO_ACCUMULATED, uses acc as it is, before unscaling.
+ * ESTATE after the step's zero_reduce_grads or with a cast pending; EINVAL on
+ * bad sources or without bufs.red. */
+zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks, void* stream);
+
+/* n_ranks value for zero_reduce_grads: no new gradient, use the accumulated one. */
+#define ZERO_ACCUMULATED (-1)
+
 /* Gradient intake of one step: the local reduce, the unscale, and this rank's
  * overflow flag and sum of squares, in one pass over the gradient.
  *   n_ranks == 0: use the already-reduced gradient registered at init
@@ -136,10 +152,14 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
  *                 g_0 + g_1 + ... + g_{N_d-1} (the local half of the
  *                 reduce-scatter, "DeepSpeed ZeRO" ZeRO Stage 2) and the
  *                 unscaled sum is kept in bufs.red.  N_d <= 64.
+ *   after zero_accumulate_grads: the sources above (or none, n_ranks =
+ *                 ZERO_ACCUMULATED) are added to the accumulated gradient in
+ *                 bufs.red first: acc + s.
  * u = gradient * inv_loss_scale (fp32); flag = any u not finite; sum of
  * squares = sum of u*u in fp64.  rank_grads is a host array of device
  * pointers.  EINVAL on bad n_ranks or null pointers; ESTATE if the previous
- * step's cast is still pending. */
+ * step's cast is still pending, or for ZERO_ACCUMULATED with nothing
+ * accumulated. */
 zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks,
                                 float inv_loss_scale, void* stream);
 

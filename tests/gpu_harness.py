@@ -104,7 +104,7 @@ class Sim:
     """N_d ranks of the HIP path plus the oracle, stepped together."""
 
     def __init__(self, numel, nd, dtype, p16_full, master_full, grad_mode, per_tensor_params=False,
-                 param_misalign=(0,), grad_misalign=(0,), ranks=None):
+                 param_misalign=(0,), grad_misalign=(0,), ranks=None, with_red=None):
         self.numel, self.nd, self.dtype, self.grad_mode = list(numel), nd, dtype, grad_mode
         self.psi = sum(numel)
         self.ranks = list(range(nd)) if ranks is None else ranks
@@ -135,8 +135,50 @@ class Sim:
                 grads = self.gviews
             elif grad_mode == "registered_flat":
                 grads = self.gstore
+            red = (grad_mode == "reduce") if with_red is None else with_red
             self.shards[r] = ZeroShard(numel, nd, r, dtype, views if views is not None else store, grads=grads,
-                                       master_init=mi, with_red=(grad_mode == "reduce"))
+                                       master_init=mi, with_red=red)
+
+    def _device_grads(self, grads):
+        """Sources for one intake call: the N_d rank buffers, the flat buffer, or
+        (ragged / registered) a copy into the registered storage and []."""
+        if self.grad_mode == "reduce":
+            return [dev16(g) for g in grads]
+        if self.grad_mode == "flat":
+            return [dev16(grads[0])]
+        src = dev16(grads[0])
+        if self.gviews is not None:
+            start = 0
+            for v, n in zip(self.gviews, self.numel):
+                v.copy_(src[start:start + n])
+                start += n
+        else:
+            self.gstore.copy_(src)
+        return []
+
+    def step_accumulated(self, micro, inv, max_norm, hp, fuse=True, last_fused=True):
+        """One step over the micro-steps in `micro` (each a list of flat uint16 arrays).
+        last_fused: the last micro-step goes through zero_reduce_grads itself; otherwise
+        every micro-step is accumulated and the intake uses ZERO_ACCUMULATED."""
+        from zero_partitioned_mixed_reduce_amd._abi import ZERO_ACCUMULATED
+        res = oracle.step_ranks_accumulated(self.ostates, micro, self.begins, inv, max_norm, hp)
+        loc = {}
+        for k, grads in enumerate(micro):
+            last = k == len(micro) - 1
+            for r in self.ranks:
+                dg = self._device_grads(grads)   # registered storage is rewritten per micro-step
+                s = self.shards[r]
+                if last and last_fused:
+                    s.zero_reduce_grads(dg, inv)
+                else:
+                    s.zero_accumulate_grads(dg)
+                    if last:
+                        s.zero_reduce_grads(ZERO_ACCUMULATED, inv)
+                torch.cuda.synchronize()
+        for r in self.ranks:
+            loc[r] = self.shards[r].zero_local_stats()
+        self._finish(res, loc, inv, max_norm, hp, fuse, False)
+        return res
 
     def step(self, grads, inv, max_norm, hp, fuse=True, extra_found_inf=False):
         """grads: list of flat uint16 arrays (N_d for 'reduce', else one)."""
@@ -160,6 +202,10 @@ class Sim:
         for r in self.ranks:
             self.shards[r].zero_reduce_grads(dg, inv)
             loc[r] = self.shards[r].zero_local_stats()
+        self._finish(res, loc, inv, max_norm, hp, fuse, extra_found_inf)
+        return res
+
+    def _finish(self, res, loc, inv, max_norm, hp, fuse, extra_found_inf):
         for r in self.ranks:
             flag_others = any((loc[q][0] if q in loc else res[q]["flag"]) for q in range(self.nd) if q != r)
             flag_others = flag_others or extra_found_inf
@@ -184,7 +230,6 @@ class Sim:
                 if not q["skipped"]:
                     assert q["clip"] == res[r]["clip"], (r, q, res[r])
             assert q["t"] == self.ostates[r].counters.t
-        return res
 
     def compare(self):
         """Every simulated rank's master, m, v and 16-bit slice against the oracle;

@@ -38,7 +38,18 @@ def host_grad(w, q, idx_or_range):
     return synth.gather_16(idx_or_range, w.dtype, w.seed, stream, w.grad_sigma, zs, zm)
 
 
-def oracle_local_sumsq(w, b, valid, inv):
+def oracle_u(w, srcs, inv, micro_steps):
+    """The oracle's unscaled gradient for one run of elements: the benchmark feeds the
+    same sources to every micro-step."""
+    if micro_steps <= 1:
+        return oracle.grad_stats(w.dtype, srcs, inv)
+    acc = np.zeros(srcs[0].size, np.float32)
+    for k in range(micro_steps):
+        oracle.accumulate(w.dtype, srcs, acc, first=(k == 0))
+    return oracle.stats_f32(acc, inv)
+
+
+def oracle_local_sumsq(w, b, valid, inv, micro_steps=1):
     nsrc = w.nd if w.grad_mode == "reduce" else 1
     step = 1 << 24
     blocks = [(lo, min(step, valid - lo)) for lo in range(0, valid, step)]
@@ -46,7 +57,7 @@ def oracle_local_sumsq(w, b, valid, inv):
     def part(blk):
         lo, n = blk
         srcs = [host_grad(w, q, (b + lo, n)) for q in range(nsrc)]
-        _, flag, ss = oracle.grad_stats(w.dtype, srcs, inv)
+        _, flag, ss = oracle_u(w, srcs, inv, micro_steps)
         return flag, ss
 
     synth.set_host_threads(1)          # the pool below already uses every core
@@ -100,13 +111,14 @@ def gpu_params_at(wl, flat_idx):
     return out
 
 
-@pytest.mark.parametrize("cfg,rank", [("zero1_7p5b", 0), ("zero1_7p5b", 63), ("gpt2", 7), ("gpt2", 3), ("reduce8", 7),
-                                      ("reduce8", 0), ("full7p5b", 0)])
-def test_full_size_sampled(cfg, rank):
+@pytest.mark.parametrize("cfg,rank,micro", [("zero1_7p5b", 0, 1), ("zero1_7p5b", 63, 1), ("gpt2", 7, 1), ("gpt2", 3, 1),
+                                            ("reduce8", 7, 1), ("reduce8", 0, 1), ("full7p5b", 0, 1),
+                                            ("reduce8", 7, 3), ("zero1_7p5b", 0, 2)])
+def test_full_size_sampled(cfg, rank, micro):
     import bench
     w = recipes.ALL[cfg]()
-    print(f"\n[fullsize] {cfg} rank {rank}: setting up", flush=True)
-    wl = bench.Workload(w, rank)
+    print(f"\n[fullsize] {cfg} rank {rank} micro-steps {micro}: setting up", flush=True)
+    wl = bench.Workload(w, rank, micro)
     info = wl.info
     b, valid = info.shard_begin, info.valid_elems
     pieces = wl.shard.pieces()
@@ -117,7 +129,7 @@ def test_full_size_sampled(cfg, rank):
     assert q["t"] == 2 and not q["skipped"]
 
     print(f"[fullsize] {cfg}: oracle sum of squares over {valid} elements", flush=True)
-    flag, local = oracle_local_sumsq(w, b, valid, wl.inv)
+    flag, local = oracle_local_sumsq(w, b, valid, wl.inv, micro)
     assert not flag
     clip, norm = oracle.clip_coef(local + wl.other_sumsq, w.max_norm)
     assert q["clip"] == clip, (q, clip)
@@ -127,7 +139,7 @@ def test_full_size_sampled(cfg, rank):
     pos = sample_positions(info, pieces, rng)
     flat = b + pos
     nsrc = w.nd if w.grad_mode == "reduce" else 1
-    u, _, _ = oracle.grad_stats(w.dtype, [host_grad(w, qq, flat) for qq in range(nsrc)], wl.inv)
+    u, _, _ = oracle_u(w, [host_grad(w, qq, flat) for qq in range(nsrc)], wl.inv, micro)
     mstream = synth.stream_id(synth.MASTER)
     if w.master_given:
         wv = synth.gather_f32(flat, w.seed, mstream, w.master_sigma)

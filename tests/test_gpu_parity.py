@@ -231,3 +231,80 @@ def test_device_generator_matches_host_generator():
     f = torch.empty(n, dtype=torch.float32, device="cuda")
     synth.gpu_normal_f32(f, 77, 6, first=5, sigma=0.02)
     assert (f.cpu().numpy().view(np.uint32) == synth.normal_f32(n, 77, 6, 5, 0.02).view(np.uint32)).all()
+
+
+# --------------------------------------------------------------------------
+# gradient accumulation over micro-steps
+
+
+def micro_grads(w, step, psi, nranks, K):
+    return [[synth.normal_16(psi, w.dtype, w.seed, synth.stream_id(synth.GRAD, q, 100 * step + k), 0, w.grad_sigma)
+             for q in range(nranks)] for k in range(K)]
+
+
+@pytest.mark.parametrize("last_fused", [True, False])
+def test_accumulation_tiny_all_ranks(last_fused):
+    w = recipes.tiny()
+    psi = w.psi
+    master, p16 = master_of(w, psi)
+    sim = Sim(w.numel, w.nd, w.dtype, p16, master, "reduce")
+    sim.p16_initial = p16.copy()
+    hp = hp_of(w.hp)
+    S = sim.plans[0][1]
+    for step in range(1, 4):
+        micro = micro_grads(w, step, psi, w.nd, 3)
+        if step == 2:
+            micro[1][2][1 * S + 5] = 0x7C00           # inf in rank 1's slice, micro-step 2 of step 2
+        res = sim.step_accumulated(micro, 1.0 / w.loss_scale, w.max_norm, hp, last_fused=last_fused)
+        assert all(x["skipped"] == (step == 2) for x in res)
+        sim.compare()
+
+
+@pytest.mark.parametrize("mode,nd,K", [("flat", 5, 4), ("ragged", 3, 2), ("reduce", 3, 2), ("reduce", 8, 2)])
+def test_accumulation_modes(mode, nd, K):
+    w = recipes.ragged_mini(nd) if mode == "ragged" else recipes.tiny()
+    psi = w.psi if mode == "ragged" else 200_003
+    numel = w.numel if mode == "ragged" else [psi]
+    master, p16 = master_of(w, psi)
+    sim = Sim(numel, nd, w.dtype, p16, None if mode == "ragged" else master, mode,
+              per_tensor_params=(mode == "ragged"), ranks=None if nd <= 5 else [0, nd - 1], with_red=True)
+    sim.p16_initial = p16.copy()
+    for step in range(1, 3):
+        micro = micro_grads(w, step, psi, nd if mode == "reduce" else 1, K)
+        sim.step_accumulated(micro, 1.0 / w.loss_scale, w.max_norm, hp_of(w.hp), last_fused=(step == 1))
+        sim.compare()
+
+
+def test_accumulation_misaligned_tensors():
+    numel = [5000, 1, 8193, 64, 12345, 3]
+    w = recipes.ragged_mini(3)
+    psi = sum(numel)
+    master, p16 = master_of(w, psi)
+    sim = Sim(numel, 3, F16, p16, master, "ragged", per_tensor_params=True, param_misalign=(1, 3),
+              grad_misalign=(2,), with_red=True)
+    sim.p16_initial = p16.copy()
+    sim.step_accumulated(micro_grads(w, 1, psi, 1, 3), 1.0, 1.0, hp_of(w.hp), last_fused=False)
+    sim.compare()
+
+
+def test_accumulation_step_order():
+    from zero_partitioned_mixed_reduce_amd import ZeroError, ZERO_ACCUMULATED
+    from zero_partitioned_mixed_reduce_amd._abi import ZERO_ESTATE, ZERO_EINVAL
+    from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
+    psi = 4096
+    w = recipes.tiny()
+    _, p16 = master_of(w, psi)
+    g = dev16(grads_for(w, 1, psi, 1)[0])
+    s = ZeroShard([psi], 1, 0, F16, dev16(p16), with_red=True)
+    with pytest.raises(ZeroError) as e:
+        s.zero_reduce_grads(ZERO_ACCUMULATED, 1.0)           # nothing accumulated
+    assert e.value.status == ZERO_ESTATE
+    s.zero_accumulate_grads([g])
+    s.zero_reduce_grads([g], 1.0)
+    with pytest.raises(ZeroError) as e:
+        s.zero_accumulate_grads([g])                         # after the step's intake
+    assert e.value.status == ZERO_ESTATE
+    s2 = ZeroShard([psi], 1, 0, F16, dev16(p16))             # no bufs.red
+    with pytest.raises(ZeroError) as e:
+        s2.zero_accumulate_grads([g])
+    assert e.value.status == ZERO_EINVAL

@@ -8,6 +8,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libzero_shard.so")
 
 ZERO_OK, ZERO_EINVAL, ZERO_EHIP, ZERO_ESTATE = 0, -1, -3, -4
 ZERO_F16, ZERO_BF16 = 1, 2
+ZERO_ACCUMULATED = -1
 
 c_i64p = ctypes.POINTER(ctypes.c_int64)
 
@@ -45,6 +46,7 @@ _PROTOS = {
                         ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)],
     "zero_reduce_grads": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_float,
                           ctypes.c_void_p],
+    "zero_accumulate_grads": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_void_p],
     "zero_local_stats": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
                          ctypes.c_void_p],
     "zero_check_overflow": [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p],
@@ -110,9 +112,19 @@ def zero_shard_init(desc, bufs, master_init_ptr, stream):
 
 
 def zero_reduce_grads(h, rank_grad_ptrs, inv_loss_scale, stream):
+    """rank_grad_ptrs: list of device pointers, or ZERO_ACCUMULATED."""
+    if rank_grad_ptrs is ZERO_ACCUMULATED or rank_grad_ptrs == ZERO_ACCUMULATED:
+        _call("zero_reduce_grads", h, None, ZERO_ACCUMULATED, inv_loss_scale, stream)
+        return
     n = len(rank_grad_ptrs)
     arr = (ctypes.c_void_p * max(n, 1))(*rank_grad_ptrs)
     _call("zero_reduce_grads", h, arr if n else None, n, inv_loss_scale, stream)
+
+
+def zero_accumulate_grads(h, rank_grad_ptrs, stream):
+    n = len(rank_grad_ptrs)
+    arr = (ctypes.c_void_p * max(n, 1))(*rank_grad_ptrs)
+    _call("zero_accumulate_grads", h, arr if n else None, n, stream)
 
 
 def zero_local_stats(h, stream):

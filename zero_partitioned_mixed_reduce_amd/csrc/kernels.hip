@@ -323,31 +323,36 @@ struct ReduceArgs {
   StatsPart* parts;
 };
 
+// Gradient sources of the intake passes.  NR > 0: that many rank buffers
+// (specialised fan-in); kSrcRanksN: a runtime number of rank buffers (>= 1);
+// kSrcChunk: the gradient registered at init (one already-reduced source per
+// chunk); kSrcNone: no new gradient (the accumulated one alone).
+enum { kSrcRanksN = 0, kSrcChunk = -1, kSrcNone = -2 };
+
+// s = the rank-order fp32 sum of this element's sources (g_0 + g_1 + ...).
 template <int DT, int NR>
-struct ReduceOp {
+struct GradSum {
   const ReduceArgs* a;
-  int64_t flat_off;
-  float* red;
-  float inv;
-  int nr;
-  SumSq ss;
-  __device__ __forceinline__ int nranks() const { return NR > 0 ? NR : nr; }
-  __device__ __forceinline__ void elem(int64_t j) {
-    float r = dec16<DT>(a->ranks[0][flat_off + j]);
-    for (int q = 1; q < nranks(); ++q) r = r + dec16<DT>(a->ranks[q][flat_off + j]);
-    const float u = r * inv;
-    ss.add(0, u);
-    red[j] = u;
+  const uint16_t* src0;  // registered chunk source (kSrcChunk)
+  int64_t flat_off;      // rank buffers are flat
+  __device__ __forceinline__ int nranks() const { return NR > 0 ? NR : a->n_ranks; }
+  __device__ __forceinline__ const uint16_t* src(int q) const {
+    return NR == kSrcChunk ? src0 : a->ranks[q] + flat_off;
+  }
+  __device__ __forceinline__ float one(int64_t j) const {
+    float r = dec16<DT>(src(0)[j]);
+    if constexpr (NR != kSrcChunk)
+      for (int q = 1; q < nranks(); ++q) r = r + dec16<DT>(src(q)[j]);
+    return r;
   }
   template <int U>
-  __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
-    f32x4 s[U];
+  __device__ __forceinline__ void quads(int64_t j, int64_t stride, f32x4 (&s)[U]) const {
     if constexpr (NR > 0) {
       u32x2 raw[NR][U];
 #pragma unroll
       for (int q = 0; q < NR; ++q)
 #pragma unroll
-        for (int k = 0; k < U; ++k) raw[q][k] = ld16x4(a->ranks[q] + flat_off + j + k * stride);
+        for (int k = 0; k < U; ++k) raw[q][k] = ld16x4(src(q) + j + k * stride);
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         s[k] = dec16x4<DT>(raw[0][k]);
@@ -356,10 +361,56 @@ struct ReduceOp {
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < U; ++k) s[k] = dec16x4<DT>(ld16x4(a->ranks[0] + flat_off + j + k * stride));
-      for (int q = 1; q < nr; ++q)
+      for (int k = 0; k < U; ++k) s[k] = dec16x4<DT>(ld16x4(src(0) + j + k * stride));
+      if constexpr (NR != kSrcChunk)
+        for (int q = 1; q < nranks(); ++q)
 #pragma unroll
-        for (int k = 0; k < U; ++k) s[k] = s[k] + dec16x4<DT>(ld16x4(a->ranks[q] + flat_off + j + k * stride));
+          for (int k = 0; k < U; ++k) s[k] = s[k] + dec16x4<DT>(ld16x4(src(q) + j + k * stride));
+    }
+  }
+  // leading elements to peel, and co-alignment of every source with the fp32 buffer after them
+  __device__ __forceinline__ int head(const float* red) const {
+    if constexpr (NR == kSrcNone) return (int)(((16u - ((uintptr_t)red & 15u)) & 15u) >> 2);
+    else return head16(src(0));
+  }
+  __device__ __forceinline__ bool aligned_at(int h, const float* red) const {
+    bool ok = aligned(red + h, 16);
+    if constexpr (NR != kSrcNone)
+      for (int q = 0; q < (NR == kSrcChunk ? 1 : nranks()); ++q) ok = ok && aligned(src(q) + h, 8);
+    return ok;
+  }
+};
+
+// Intake with statistics: u = (ACC ? red + s : s) * inv stored in red, plus the
+// fp64 sum of squares.  With kSrcNone, u = red * inv.
+template <int DT, int NR, bool ACC>
+struct ReduceOp {
+  GradSum<DT, NR> gs;
+  float* red;
+  float inv;
+  SumSq ss;
+  __device__ __forceinline__ void elem(int64_t j) {
+    float r;
+    if constexpr (NR == kSrcNone) r = red[j];
+    else if constexpr (ACC) r = red[j] + gs.one(j);
+    else r = gs.one(j);
+    const float u = r * inv;
+    ss.add(0, u);
+    red[j] = u;
+  }
+  template <int U>
+  __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
+    f32x4 s[U];
+    if constexpr (NR != kSrcNone) gs.template quads<U>(j, stride, s);
+    if constexpr (ACC || NR == kSrcNone) {
+      f32x4 acc[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) acc[k] = ld32x4_nt(red + j + k * stride);
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        if constexpr (NR == kSrcNone) s[k] = acc[k];
+        else s[k] = acc[k] + s[k];
+      }
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
@@ -371,19 +422,63 @@ struct ReduceOp {
   }
 };
 
-template <int DT, int NR>
+template <int DT, int NR, bool ACC>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
-  ReduceOp<DT, NR> op{&a, 0, nullptr, a.inv, a.n_ranks, SumSq{}};
+  ReduceOp<DT, NR, ACC> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, a.inv, SumSq{}};
   for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
     const Chunk ch = a.chunks[c];
-    op.flat_off = ch.flat_off;
+    op.gs.flat_off = ch.flat_off;
+    op.gs.src0 = reinterpret_cast<const uint16_t*>(ch.g16);
     op.red = a.red + ch.state_off;
-    const int head = head16(a.ranks[0] + ch.flat_off);
-    bool ok = aligned(op.red + head, 16);
-    for (int q = 0; q < a.n_ranks; ++q) ok = ok && aligned(a.ranks[q] + ch.flat_off + head, 8);
-    run_chunk<ZS_REDUCE_U, 4>(op, ch.len, head, ok);
+    const int head = op.gs.head(op.red);
+    run_chunk<ZS_REDUCE_U, 4>(op, ch.len, head, op.gs.aligned_at(head, op.red));
   }
   finish_stats(op.ss.total(), a.sc, a.parts);
+}
+
+// One micro-step into the accumulator, no statistics: red = FIRST ? s : red + s.
+template <int DT, int NR, bool FIRST>
+struct AccumOp {
+  GradSum<DT, NR> gs;
+  float* red;
+  __device__ __forceinline__ void elem(int64_t j) {
+    const float s = gs.one(j);
+    red[j] = FIRST ? s : red[j] + s;
+  }
+  template <int U>
+  __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
+    f32x4 s[U];
+    gs.template quads<U>(j, stride, s);
+    if constexpr (!FIRST) {
+      f32x4 acc[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) acc[k] = ld32x4_nt(red + j + k * stride);
+#pragma unroll
+      for (int k = 0; k < U; ++k) s[k] = acc[k] + s[k];
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) st32x4_nt(red + j + k * stride, s[k]);
+  }
+};
+
+// One short-lived block per part of a chunk, as in the Adam pass.
+template <int DT, int NR, bool FIRST>
+__global__ void __launch_bounds__(kBlock) accum_kernel(ReduceArgs a) {
+  AccumOp<DT, NR, FIRST> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr};
+  const int64_t n_items = a.n_chunks * ZS_ADAM_SPLIT;
+  for (int64_t i = blockIdx.x; i < n_items; i += gridDim.x) {
+    const Chunk ch = a.chunks[i / ZS_ADAM_SPLIT];
+    const int64_t part = i % ZS_ADAM_SPLIT;
+    const int64_t sub = ((ch.len + ZS_ADAM_SPLIT - 1) / ZS_ADAM_SPLIT + 7) & ~(int64_t)7;
+    const int64_t lo = part * sub;
+    if (lo >= ch.len) continue;
+    const int64_t len = (lo + sub < ch.len ? lo + sub : ch.len) - lo;
+    op.gs.flat_off = ch.flat_off + lo;
+    op.gs.src0 = reinterpret_cast<const uint16_t*>(ch.g16) + lo;
+    op.red = a.red + ch.state_off + lo;
+    const int head = op.gs.head(op.red);
+    run_chunk<ZS_REDUCE_U, 4>(op, len, head, op.gs.aligned_at(head, op.red));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -664,37 +759,91 @@ hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, cons
   return hipGetLastError();
 }
 
-template <int DT>
-static void launch_reduce_dt(const ReduceArgs& a, unsigned g, hipStream_t st) {
-  switch (a.n_ranks) {
-    case 2: hipLaunchKernelGGL((reduce_kernel<DT, 2>), dim3(g), dim3(kBlock), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((reduce_kernel<DT, 4>), dim3(g), dim3(kBlock), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((reduce_kernel<DT, 8>), dim3(g), dim3(kBlock), 0, st, a); break;
-    default: hipLaunchKernelGGL((reduce_kernel<DT, 0>), dim3(g), dim3(kBlock), 0, st, a); break;
+template <int DT, bool ACC>
+static void launch_reduce_acc(const ReduceArgs& a, int src, unsigned g, hipStream_t st) {
+  switch (src) {
+    case 1: hipLaunchKernelGGL((reduce_kernel<DT, 1, ACC>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((reduce_kernel<DT, 2, ACC>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((reduce_kernel<DT, 4, ACC>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((reduce_kernel<DT, 8, ACC>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case kSrcChunk: hipLaunchKernelGGL((reduce_kernel<DT, kSrcChunk, ACC>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case kSrcNone: hipLaunchKernelGGL((reduce_kernel<DT, kSrcNone, true>), dim3(g), dim3(kBlock), 0, st, a); break;
+    default: hipLaunchKernelGGL((reduce_kernel<DT, kSrcRanksN, ACC>), dim3(g), dim3(kBlock), 0, st, a); break;
   }
 }
 
+template <int DT, bool FIRST>
+static void launch_accum_first(const ReduceArgs& a, int src, unsigned g, hipStream_t st) {
+  switch (src) {
+    case 1: hipLaunchKernelGGL((accum_kernel<DT, 1, FIRST>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((accum_kernel<DT, 2, FIRST>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((accum_kernel<DT, 4, FIRST>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((accum_kernel<DT, 8, FIRST>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case kSrcChunk: hipLaunchKernelGGL((accum_kernel<DT, kSrcChunk, FIRST>), dim3(g), dim3(kBlock), 0, st, a); break;
+    default: hipLaunchKernelGGL((accum_kernel<DT, kSrcRanksN, FIRST>), dim3(g), dim3(kBlock), 0, st, a); break;
+  }
+}
+
+static ReduceArgs make_reduce_args(const Chunk* chunks, int64_t n_chunks, const void* const* ranks, int32_t n_ranks,
+                                   float inv, float* red, DevScalars* sc, StatsPart* parts) {
+  ReduceArgs a;
+  a.chunks = chunks;
+  a.n_chunks = n_chunks;
+  for (int q = 0; q < kMaxRanks; ++q)
+    a.ranks[q] = (ranks && q < n_ranks) ? static_cast<const uint16_t*>(ranks[q]) : nullptr;
+  a.n_ranks = n_ranks > 0 ? n_ranks : 1;
+  a.inv = inv;
+  a.red = red;
+  a.sc = sc;
+  a.parts = parts;
+  return a;
+}
+
+// Source code of the template switch: n_ranks >= 1 rank buffers (1, 2, 4, 8 are
+// specialised), 0 -> the registered gradient, -1 -> none (the accumulated one alone).
+static int src_code(int32_t n_ranks) {
+  if (n_ranks == 0) return kSrcChunk;
+  if (n_ranks < 0) return kSrcNone;
+  if (n_ranks == 1 || n_ranks == 2 || n_ranks == 4 || n_ranks == 8) return n_ranks;
+  return kSrcRanksN;
+}
+
+// Intake with statistics into red: u = (accumulate ? red + s : s) * inv, or red * inv
+// when n_ranks < 0; the local flag and sum of squares go to the scalar block.
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                         int32_t n_ranks, float inv, float* red, DevScalars* sc, StatsPart* parts,
+                         int32_t n_ranks, bool accumulate, float inv, float* red, DevScalars* sc, StatsPart* parts,
                          int64_t grid_cap, hipStream_t st) {
   if (n_chunks == 0) {
     hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc);
     return hipGetLastError();
   }
-  ReduceArgs a;
-  a.chunks = chunks;
-  a.n_chunks = n_chunks;
-  for (int q = 0; q < kMaxRanks; ++q) a.ranks[q] = q < n_ranks ? static_cast<const uint16_t*>(ranks[q]) : nullptr;
-  a.n_ranks = n_ranks;
-  a.inv = inv;
-  a.red = red;
-  a.sc = sc;
-  a.parts = parts;
+  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, inv, red, sc, parts);
   const unsigned g = stats_grid(n_chunks, grid_cap);
-  if (dtype == ZERO_BF16)
-    launch_reduce_dt<ZERO_BF16>(a, g, st);
-  else
-    launch_reduce_dt<ZERO_F16>(a, g, st);
+  const int src = src_code(n_ranks);
+  if (dtype == ZERO_BF16) {
+    if (accumulate) launch_reduce_acc<ZERO_BF16, true>(a, src, g, st);
+    else launch_reduce_acc<ZERO_BF16, false>(a, src, g, st);
+  } else {
+    if (accumulate) launch_reduce_acc<ZERO_F16, true>(a, src, g, st);
+    else launch_reduce_acc<ZERO_F16, false>(a, src, g, st);
+  }
+  return hipGetLastError();
+}
+
+// One micro-step into the accumulator: red = first ? s : red + s.
+hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
+                             int32_t n_ranks, bool first, float* red, int64_t grid_cap, hipStream_t st) {
+  if (n_chunks == 0) return hipSuccess;
+  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, 1.0f, red, nullptr, nullptr);
+  const unsigned g = clamp_grid(n_chunks * ZS_ADAM_SPLIT, grid_cap);
+  const int src = src_code(n_ranks);
+  if (dtype == ZERO_BF16) {
+    if (first) launch_accum_first<ZERO_BF16, true>(a, src, g, st);
+    else launch_accum_first<ZERO_BF16, false>(a, src, g, st);
+  } else {
+    if (first) launch_accum_first<ZERO_F16, true>(a, src, g, st);
+    else launch_accum_first<ZERO_F16, false>(a, src, g, st);
+  }
   return hipGetLastError();
 }
 

@@ -17,8 +17,10 @@ namespace zs {
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
                           DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st);
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                         int32_t n_ranks, float inv, float* red, DevScalars* sc, StatsPart* parts,
+                         int32_t n_ranks, bool accumulate, float inv, float* red, DevScalars* sc, StatsPart* parts,
                          int64_t grid_cap, hipStream_t st);
+hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
+                             int32_t n_ranks, bool first, float* red, int64_t grid_cap, hipStream_t st);
 struct AdamArgs;
 hipError_t launch_cast(int dtype, const Chunk* chunks, int64_t n_chunks, const float* master,
                        const DevScalars* sc, int64_t grid_cap, hipStream_t st);
@@ -71,6 +73,8 @@ struct zero_shard {
   int64_t grid_stats, grid_main;
   Phase phase;
   bool cast_pending;
+  bool accumulating;   // micro-steps summed into red since the last intake
+  int64_t dp_size;
   // current step
   int grad_source;
   const uint16_t* step_flat_g;
@@ -178,6 +182,8 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
   h->grid_stats = (int64_t)cus * 8 < zs::kMaxStatsBlocks ? (int64_t)cus * 8 : zs::kMaxStatsBlocks;
   h->phase = kReady;
   h->cast_pending = false;
+  h->accumulating = false;
+  h->dp_size = desc->dp_size;
   h->adam_calls = 0;
 
   zs::DevScalars init_sc;
@@ -215,6 +221,40 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
   return ZERO_OK;
 }
 
+namespace {
+// Checks a gradient source list: 0 (registered), 1 (flat, already reduced) or 2..64 rank buffers.
+zero_status_t check_sources(zero_shard* h, const void* const* rank_grads, int32_t n_ranks) {
+  if (n_ranks == 0) {
+    if (!h->has_registered_grads) return fail(ZERO_EINVAL, "n_ranks == 0 needs gradients registered at init");
+    return ZERO_OK;
+  }
+  if (n_ranks < 0 || n_ranks > zs::kMaxRanks) return fail(ZERO_EINVAL, "n_ranks must be 0..64");
+  if (!rank_grads) return fail(ZERO_EINVAL, "rank_grads is null");
+  for (int q = 0; q < n_ranks; ++q)
+    if (!rank_grads[q]) return fail(ZERO_EINVAL, "rank_grads[" + std::to_string(q) + "] is null");
+  return ZERO_OK;
+}
+}  // namespace
+
+zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks, void* stream) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (h->phase == kReduced || h->phase == kChecked || h->phase == kNormed)
+    return fail(ZERO_ESTATE, "micro-steps are accumulated before the step's zero_reduce_grads");
+  if (h->phase == kStepped && h->cast_pending)
+    return fail(ZERO_ESTATE, "zero_cast_params of the previous step is pending");
+  if (!h->red) return fail(ZERO_EINVAL, "accumulation needs bufs.red");
+  zero_status_t s = check_sources(h, rank_grads, n_ranks);
+  if (s != ZERO_OK) return s;
+  DeviceGuard dg(h->device);
+  hipError_t e = zs::launch_accumulate(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, !h->accumulating,
+                                       h->red, h->grid_main, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("accumulate kernel", e);
+  h->accumulating = true;
+  h->phase = kReady;
+  h->cast_pending = false;
+  return ZERO_OK;
+}
+
 zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks, float inv_loss_scale,
                                 void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
@@ -223,7 +263,21 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
   hipStream_t st = static_cast<hipStream_t>(stream);
   DeviceGuard dg(h->device);
   hipError_t e;
-  if (n_ranks == 0) {
+  if (h->accumulating) {
+    // last micro-step (or none: ZERO_ACCUMULATED) on top of the accumulated gradient
+    if (n_ranks != ZERO_ACCUMULATED) {
+      zero_status_t s = check_sources(h, rank_grads, n_ranks);
+      if (s != ZERO_OK) return s;
+    }
+    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, true, inv_loss_scale, h->red,
+                          h->sc, h->parts, h->grid_stats, st);
+    if (e != hipSuccess) return hip_fail("reduce kernel", e);
+    h->grad_source = kGradRed;
+    h->step_flat_g = nullptr;
+    h->accumulating = false;
+  } else if (n_ranks == ZERO_ACCUMULATED) {
+    return fail(ZERO_ESTATE, "ZERO_ACCUMULATED without zero_accumulate_grads in this step");
+  } else if (n_ranks == 0) {
     if (!h->has_registered_grads) return fail(ZERO_EINVAL, "n_ranks == 0 needs gradients registered at init");
     e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, nullptr, inv_loss_scale, h->sc, h->parts,
                            h->grid_stats, st);
@@ -243,8 +297,8 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     for (int q = 0; q < n_ranks; ++q)
       if (!rank_grads[q]) return fail(ZERO_EINVAL, "rank_grads[" + std::to_string(q) + "] is null");
     if (!h->red) return fail(ZERO_EINVAL, "reducing N_d >= 2 buffers needs bufs.red");
-    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, inv_loss_scale, h->red, h->sc,
-                          h->parts, h->grid_stats, st);
+    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, false, inv_loss_scale, h->red,
+                          h->sc, h->parts, h->grid_stats, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
     h->grad_source = kGradRed;
     h->step_flat_g = nullptr;

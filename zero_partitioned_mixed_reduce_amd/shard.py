@@ -85,8 +85,17 @@ class ZeroShard:
 
     # step calls (same names as the C ABI)
     def zero_reduce_grads(self, rank_grads, inv_loss_scale):
+        """rank_grads: list of 16-bit tensors ([] for the registered gradient) or
+        abi.ZERO_ACCUMULATED."""
+        if isinstance(rank_grads, int):
+            abi.zero_reduce_grads(self.h, rank_grads, inv_loss_scale, _stream())
+            return
         ptrs = [g.data_ptr() for g in rank_grads] if rank_grads else []
         abi.zero_reduce_grads(self.h, ptrs, inv_loss_scale, _stream())
+
+    def zero_accumulate_grads(self, rank_grads):
+        ptrs = [g.data_ptr() for g in rank_grads] if rank_grads else []
+        abi.zero_accumulate_grads(self.h, ptrs, _stream())
 
     def zero_local_stats(self):
         return abi.zero_local_stats(self.h, _stream())
