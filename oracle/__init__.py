@@ -62,6 +62,10 @@ def lib():
         L.orc_stats_f32.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
                                     ctypes.POINTER(ctypes.c_double)]
         L.orc_stats_f32.restype = ctypes.c_int
+        L.orc_loss_scale_update.argtypes = [ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_float,
+                                            ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]
+        L.orc_inv_scale.argtypes = [ctypes.c_float]
+        L.orc_inv_scale.restype = ctypes.c_float
         L.orc_clip_coef.argtypes = [ctypes.c_double, ctypes.c_float, ctypes.POINTER(ctypes.c_double)]
         L.orc_clip_coef.restype = ctypes.c_float
         L.orc_next_scalars.argtypes = [ctypes.POINTER(HParams), ctypes.POINTER(Counters),
@@ -205,6 +209,24 @@ def upcast(dtype, p16):
     w = np.empty(p16.size, np.float32)
     lib().orc_upcast(dtype, _ptr(p16), p16.size, _ptr(w))
     return w
+
+
+class LossScaler:
+    """Dynamic loss scale state of the oracle (see orc_loss_scale_update)."""
+
+    def __init__(self, init_scale=65536.0, growth=2.0, backoff=0.5, interval=1000, min_scale=1.0):
+        self.scale = ctypes.c_float(init_scale)
+        self.good = ctypes.c_int(0)
+        self.growth, self.backoff, self.interval, self.min_scale = growth, backoff, interval, min_scale
+
+    @property
+    def inv(self):
+        return float(lib().orc_inv_scale(self.scale))
+
+    def update(self, skipped):
+        lib().orc_loss_scale_update(int(bool(skipped)), ctypes.c_float(self.growth), ctypes.c_float(self.backoff),
+                                    int(self.interval), ctypes.c_float(self.min_scale), ctypes.byref(self.scale),
+                                    ctypes.byref(self.good))
 
 
 class RankState:

@@ -262,6 +262,29 @@ void orc_adam_elems(const float* u, int64_t n, float clip, const orc_hparams* hp
   }
 }
 
+/* Dynamic loss scale ("DeepSpeed ZeRO" 配置说明: fp16.loss_scale = 0 selects dynamic
+ * scaling, starting at 2^initial_scale_power).  The pages give no update rule; the
+ * rule taken is the standard one: after a step with an overflow the scale is
+ * multiplied by `backoff` (not below min_scale) and the count of good steps is
+ * reset; after `interval` consecutive good steps it is multiplied by `growth`
+ * and the count is reset.  The intake then unscales by inv = 1 / scale (fp32). */
+void orc_loss_scale_update(int skipped, float growth, float backoff, int interval, float min_scale, float* scale,
+                           int* good) {
+  if (skipped) {
+    float s = *scale * backoff;
+    *scale = s < min_scale ? min_scale : s;
+    *good = 0;
+  } else {
+    *good += 1;
+    if (*good == interval) {
+      *scale = *scale * growth;
+      *good = 0;
+    }
+  }
+}
+
+float orc_inv_scale(float scale) { return 1.0f / scale; }
+
 /* In-place 16-bit write-back of the updated fp32 slice: p16[i] = RNE(w[i]). */
 void orc_cast(int dtype, const float* w, int64_t n, uint16_t* p16) {
   for (int64_t i = 0; i < n; ++i) p16[i] = enc16(dtype, w[i]);

@@ -658,3 +658,36 @@ def test_partition_invariance_with_accumulation(nd):
     for name in ("w", "m", "v", "p16"):
         cat = np.concatenate([getattr(st, name) for st in states])
         assert (cat.view(np.uint8) == getattr(whole, name).view(np.uint8)).all(), name
+
+
+# --------------------------------------------------------------------------
+# dynamic loss scale ("DeepSpeed ZeRO" 配置说明: loss_scale 0, initial_scale_power 16)
+
+
+def test_loss_scale_against_torch_amp_update():
+    """Library routine: torch's _amp_update_scale_ (the GradScaler state machine) on the CPU."""
+    r = np.random.default_rng(99)
+    for interval in (1, 3, 7):
+        ls = oracle.LossScaler(init_scale=2.0 ** 16, growth=2.0, backoff=0.5, interval=interval, min_scale=2.0 ** -40)
+        scale = torch.full((1,), 2.0 ** 16, dtype=torch.float32)
+        tracker = torch.zeros(1, dtype=torch.int32)
+        for _ in range(200):
+            found = bool(r.random() < 0.3)
+            ls.update(found)
+            torch._amp_update_scale_(scale, tracker, torch.full((1,), float(found)), 2.0, 0.5, interval)
+            assert ls.scale.value == scale.item() and ls.good.value == tracker.item()
+
+
+def test_loss_scale_closed_forms():
+    ls = oracle.LossScaler()                       # 2^initial_scale_power with initial_scale_power = 16
+    assert ls.scale.value == 65536.0 and ls.inv == 2.0 ** -16
+    for k in range(1, 20):
+        ls.update(True)
+        assert ls.scale.value == max(2.0 ** (16 - k), 1.0)    # halves down to min_scale and stays
+    ls = oracle.LossScaler(init_scale=8.0, interval=4)
+    for k in range(1, 13):
+        ls.update(False)
+        assert ls.scale.value == 8.0 * 2 ** (k // 4) and ls.good.value == k % 4
+    ls.update(True)
+    assert ls.scale.value == 32.0 and ls.good.value == 0
+    assert oracle.LossScaler(init_scale=1000.0).inv == np.float32(1) / np.float32(1000)
