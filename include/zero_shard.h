@@ -124,6 +124,35 @@ zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* 
 zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
                               const float* master_init, void* stream, zero_shard_t* out);
 
+/* Dynamic loss scale kept on the device ("DeepSpeed ZeRO" 配置说明: fp16.loss_scale
+ * = 0 selects dynamic scaling, starting at 2^initial_scale_power).  The pages give
+ * no update rule; the one applied, by zero_adam_step on the device, is: after a
+ * skipped (overflow) step scale = max(scale * backoff_factor, min_scale) and the
+ * good-step count restarts; after growth_interval consecutive good steps scale =
+ * scale * growth_factor and the count restarts. */
+typedef struct {
+  float init_scale;       /* e.g. 65536 = 2^16                      */
+  float growth_factor;    /* >= 1, e.g. 2                           */
+  float backoff_factor;   /* in (0, 1], e.g. 0.5                    */
+  int32_t growth_interval;/* good steps before growing, >= 1        */
+  float min_scale;        /* floor of the scale, > 0, e.g. 1        */
+} zero_loss_scaler_t;
+
+/* Value of inv_loss_scale for zero_reduce_grads: unscale by 1 / the
+ * device-resident dynamic scale (fp32), as zero_adam_step last left it. */
+#define ZERO_DEVICE_LOSS_SCALE 0.0f
+
+/* Switches this handle to the device-resident dynamic loss scale, starting at
+ * cfg->init_scale.  Between steps only (ESTATE otherwise).  Afterwards every
+ * zero_reduce_grads must pass ZERO_DEVICE_LOSS_SCALE.  Synchronises the
+ * stream.  EINVAL on an invalid configuration. */
+zero_status_t zero_enable_dynamic_loss_scale(zero_shard_t h, const zero_loss_scaler_t* cfg, void* stream);
+
+/* The current dynamic loss scale (what the next step's backward should scale
+ * the loss by) and the count of good steps since it last changed.  Synchronises
+ * the stream.  ESTATE if dynamic scaling is not enabled. */
+zero_status_t zero_loss_scale(zero_shard_t h, float* host_scale, int32_t* host_good, void* stream);
+
 /* Gradient accumulation ("DeepSpeed ZeRO", ZeRO Stage 2 under gradient
  * accumulation: every micro-step's backward is reduce-scattered and the rank
  * adds its 1/N_d slice to what it has accumulated).  Sources as in
@@ -155,9 +184,11 @@ zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grad
  *   after zero_accumulate_grads: the sources above (or none, n_ranks =
  *                 ZERO_ACCUMULATED) are added to the accumulated gradient in
  *                 bufs.red first: acc + s.
- * u = gradient * inv_loss_scale (fp32); flag = any u not finite; sum of
- * squares = sum of u*u in fp64.  rank_grads is a host array of device
- * pointers.  EINVAL on bad n_ranks or null pointers; ESTATE if the previous
+ * u = gradient * inv_loss_scale (fp32), or gradient * (1 / device scale) with
+ * ZERO_DEVICE_LOSS_SCALE; flag = any u not finite; sum of squares = sum of u*u
+ * in fp64.  rank_grads is a host array of device pointers.  EINVAL on bad
+ * n_ranks, null pointers or an inv_loss_scale that is not finite and positive
+ * (or, with dynamic scaling, not ZERO_DEVICE_LOSS_SCALE); ESTATE if the previous
  * step's cast is still pending, or for ZERO_ACCUMULATED with nothing
  * accumulated. */
 zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks,

@@ -139,6 +139,33 @@ class Sim:
             self.shards[r] = ZeroShard(numel, nd, r, dtype, views if views is not None else store, grads=grads,
                                        master_init=mi, with_red=red)
 
+    def enable_dynamic(self, init_scale, growth, backoff, interval, min_scale):
+        """Device-resident dynamic loss scale on every simulated rank, mirrored by
+        an oracle LossScaler; each step then unscales by the current scale."""
+        self.scaler = oracle.LossScaler(init_scale, growth, backoff, interval, min_scale)
+        for s in self.shards.values():
+            s.zero_enable_dynamic_loss_scale(init_scale, growth, backoff, interval, min_scale)
+        self.check_scale()
+
+    def _intake_inv(self, inv):
+        """(oracle's inverse scale, the value passed to zero_reduce_grads)."""
+        if getattr(self, "scaler", None) is None:
+            return inv, inv
+        from zero_partitioned_mixed_reduce_amd._abi import ZERO_DEVICE_LOSS_SCALE
+        return self.scaler.inv, ZERO_DEVICE_LOSS_SCALE
+
+    def _after_step(self, res):
+        if getattr(self, "scaler", None) is None:
+            return
+        self.scaler.update(res[0]["skipped"])
+        self.check_scale()
+
+    def check_scale(self):
+        exp = (self.scaler.scale.value, self.scaler.good.value)
+        for r in self.ranks:
+            got = self.shards[r].zero_loss_scale()
+            assert got == exp, (r, got, exp)
+
     def _device_grads(self, grads):
         """Sources for one intake call: the N_d rank buffers, the flat buffer, or
         (ragged / registered) a copy into the registered storage and []."""
@@ -161,6 +188,7 @@ class Sim:
         last_fused: the last micro-step goes through zero_reduce_grads itself; otherwise
         every micro-step is accumulated and the intake uses ZERO_ACCUMULATED."""
         from zero_partitioned_mixed_reduce_amd._abi import ZERO_ACCUMULATED
+        inv, dev_inv = self._intake_inv(inv)
         res = oracle.step_ranks_accumulated(self.ostates, micro, self.begins, inv, max_norm, hp)
         loc = {}
         for k, grads in enumerate(micro):
@@ -169,40 +197,30 @@ class Sim:
                 dg = self._device_grads(grads)   # registered storage is rewritten per micro-step
                 s = self.shards[r]
                 if last and last_fused:
-                    s.zero_reduce_grads(dg, inv)
+                    s.zero_reduce_grads(dg, dev_inv)
                 else:
                     s.zero_accumulate_grads(dg)
                     if last:
-                        s.zero_reduce_grads(ZERO_ACCUMULATED, inv)
+                        s.zero_reduce_grads(ZERO_ACCUMULATED, dev_inv)
                 torch.cuda.synchronize()
         for r in self.ranks:
             loc[r] = self.shards[r].zero_local_stats()
         self._finish(res, loc, inv, max_norm, hp, fuse, False)
+        self._after_step(res)
         return res
 
     def step(self, grads, inv, max_norm, hp, fuse=True, extra_found_inf=False):
         """grads: list of flat uint16 arrays (N_d for 'reduce', else one)."""
+        inv, dev_inv = self._intake_inv(inv)
         res = oracle.step_ranks(self.ostates, grads, self.begins, inv, max_norm, hp, extra_found_inf)
-        if self.grad_mode == "reduce":
-            dg = [dev16(g) for g in grads]
-        elif self.grad_mode == "flat":
-            dg = [dev16(grads[0])]
-        else:
-            src = dev16(grads[0])
-            if self.gviews is not None:
-                start = 0
-                for v, n in zip(self.gviews, self.numel):
-                    v.copy_(src[start:start + n])
-                    start += n
-            else:
-                self.gstore.copy_(src)
-            dg = []
+        dg = self._device_grads(grads)
         # every simulated rank's own flag and sum (others from the oracle when not simulated on the GPU)
         loc = {}
         for r in self.ranks:
-            self.shards[r].zero_reduce_grads(dg, inv)
+            self.shards[r].zero_reduce_grads(dg, dev_inv)
             loc[r] = self.shards[r].zero_local_stats()
         self._finish(res, loc, inv, max_norm, hp, fuse, extra_found_inf)
+        self._after_step(res)
         return res
 
     def _finish(self, res, loc, inv, max_norm, hp, fuse, extra_found_inf):

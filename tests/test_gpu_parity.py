@@ -308,3 +308,116 @@ def test_accumulation_step_order():
     with pytest.raises(ZeroError) as e:
         s2.zero_accumulate_grads([g])
     assert e.value.status == ZERO_EINVAL
+
+
+# --------------------------------------------------------------------------
+# dynamic loss scale kept on the device
+
+
+def _poison(g, idx, dtype):
+    g[idx] = oracle.encode16(dtype, np.array([np.inf], np.float32))[0]
+
+
+def test_dynamic_loss_scale_tiny_all_ranks():
+    """Backoff to the floor, growth after `interval` good steps, overflow in another
+    rank's slice; the scale sequence is also checked against the rule by hand."""
+    w = recipes.tiny()
+    psi = w.psi
+    master, p16 = master_of(w, psi)
+    sim = Sim(w.numel, w.nd, w.dtype, p16, master, "reduce")
+    sim.p16_initial = p16.copy()
+    sim.enable_dynamic(init_scale=8.0, growth=2.0, backoff=0.5, interval=3, min_scale=2.0)
+    hp = hp_of(w.hp)
+    S = sim.plans[0][1]
+    bad = {2: 0, 3: 3, 4: 1, 9: 2}                  # step -> rank slice holding an inf
+    expect = {1: 8, 2: 4, 3: 2, 4: 2, 5: 2, 6: 2, 7: 4, 8: 4, 9: 2, 10: 2, 11: 2, 12: 4}
+    for step in range(1, 13):
+        g = grads_for(w, step, psi, w.nd)
+        if step in bad:
+            _poison(g[step % w.nd], bad[step] * S + 11 * step, w.dtype)
+        res = sim.step(g, None, w.max_norm, hp)
+        assert all(x["skipped"] == (step in bad) for x in res)
+        assert sim.scaler.scale.value == expect[step], step
+        sim.compare()
+    assert all(st.counters.t == 12 - len(bad) for st in sim.ostates)
+
+
+@pytest.mark.parametrize("mode,nd,fuse", [("flat", 3, True), ("ragged", 3, False), ("registered_flat", 2, True)])
+def test_dynamic_loss_scale_modes(mode, nd, fuse):
+    w = recipes.ragged_mini(nd) if mode == "ragged" else recipes.tiny()
+    psi = w.psi if mode == "ragged" else 150_001
+    numel = w.numel if mode == "ragged" else [psi]
+    master, p16 = master_of(w, psi)
+    sim = Sim(numel, nd, w.dtype, p16, None if mode == "ragged" else master, mode,
+              per_tensor_params=(mode == "ragged"))
+    sim.p16_initial = p16.copy()
+    sim.enable_dynamic(init_scale=2.0 ** 12, growth=2.0, backoff=0.25, interval=2, min_scale=1.0)
+    for step in range(1, 7):
+        g = grads_for(w, step, psi, 1)
+        if step in (3, 4):
+            _poison(g[0], psi - 1 - 5 * step, w.dtype)
+        res = sim.step(g, None, w.max_norm, hp_of(w.hp), fuse=fuse)
+        assert all(x["skipped"] == (step in (3, 4)) for x in res)
+        sim.compare()
+
+
+@pytest.mark.parametrize("last_fused", [True, False])
+def test_dynamic_loss_scale_with_accumulation(last_fused):
+    w = recipes.tiny()
+    psi = 120_007
+    master, p16 = master_of(w, psi)
+    sim = Sim([psi], 3, F16, p16, master, "reduce")
+    sim.p16_initial = p16.copy()
+    sim.enable_dynamic(init_scale=1024.0, growth=2.0, backoff=0.5, interval=1, min_scale=1.0)
+    S = sim.plans[0][1]
+    for step in range(1, 5):
+        micro = micro_grads(w, step, psi, 3, 2)
+        if step == 2:
+            _poison(micro[0][1], 2 * S + 3, F16)    # first micro-step: only the accumulation sees it
+        res = sim.step_accumulated(micro, None, w.max_norm, hp_of(w.hp), last_fused=last_fused)
+        assert all(x["skipped"] == (step == 2) for x in res)
+        sim.compare()
+
+
+def test_dynamic_loss_scale_errors():
+    from zero_partitioned_mixed_reduce_amd import ZeroError, ZERO_DEVICE_LOSS_SCALE
+    from zero_partitioned_mixed_reduce_amd._abi import ZERO_ESTATE, ZERO_EINVAL
+    from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
+    psi = 4096
+    w = recipes.tiny()
+    _, p16 = master_of(w, psi)
+    g = dev16(grads_for(w, 1, psi, 1)[0])
+    s = ZeroShard([psi], 1, 0, F16, dev16(p16))
+    for bad_inv in (-1.0, float("inf"), float("nan")):
+        with pytest.raises(ZeroError) as e:
+            s.zero_reduce_grads([g], bad_inv)
+        assert e.value.status == ZERO_EINVAL
+    with pytest.raises(ZeroError) as e:
+        s.zero_reduce_grads([g], ZERO_DEVICE_LOSS_SCALE)     # not enabled
+    assert e.value.status == ZERO_EINVAL
+    with pytest.raises(ZeroError) as e:
+        s.zero_loss_scale()
+    assert e.value.status == ZERO_ESTATE
+    for cfg in [dict(init_scale=0.0), dict(growth_factor=0.5), dict(backoff_factor=1.5), dict(growth_interval=0),
+                dict(min_scale=0.0)]:
+        with pytest.raises(ZeroError) as e:
+            s.zero_enable_dynamic_loss_scale(**cfg)
+        assert e.value.status == ZERO_EINVAL
+    s.zero_reduce_grads([g], 1.0)
+    with pytest.raises(ZeroError) as e:
+        s.zero_enable_dynamic_loss_scale()                   # inside a step
+    assert e.value.status == ZERO_ESTATE
+    s.zero_check_overflow(False)
+    s.zero_grad_norm(0.0, 1.0)
+    s.zero_adam_step(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    s.zero_enable_dynamic_loss_scale(init_scale=256.0)       # between steps
+    assert s.zero_loss_scale() == (256.0, 0)
+    with pytest.raises(ZeroError) as e:
+        s.zero_reduce_grads([g], 1.0)                        # a host scale while dynamic
+    assert e.value.status == ZERO_EINVAL
+    s.zero_reduce_grads([g], ZERO_DEVICE_LOSS_SCALE)
+    s.zero_check_overflow(False)
+    s.zero_grad_norm(0.0, 1.0)
+    s.zero_adam_step(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    assert s.query()["t"] == 2
+    assert s.zero_loss_scale() == (256.0, 1)

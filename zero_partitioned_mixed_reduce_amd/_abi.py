@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libzero_shard.so")
 ZERO_OK, ZERO_EINVAL, ZERO_EHIP, ZERO_ESTATE = 0, -1, -3, -4
 ZERO_F16, ZERO_BF16 = 1, 2
 ZERO_ACCUMULATED = -1
+ZERO_DEVICE_LOSS_SCALE = 0.0
 
 c_i64p = ctypes.POINTER(ctypes.c_int64)
 
@@ -35,6 +36,11 @@ class zero_shard_bufs_t(ctypes.Structure):
                 ("workspace_capacity", ctypes.c_int64)]
 
 
+class zero_loss_scaler_t(ctypes.Structure):
+    _fields_ = [("init_scale", ctypes.c_float), ("growth_factor", ctypes.c_float), ("backoff_factor", ctypes.c_float),
+                ("growth_interval", ctypes.c_int32), ("min_scale", ctypes.c_float)]
+
+
 class zero_adam_hparams_t(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
@@ -55,6 +61,9 @@ _PROTOS = {
     "zero_adam_step": [ctypes.c_void_p, ctypes.POINTER(zero_adam_hparams_t), ctypes.c_int32, ctypes.c_void_p],
     "zero_cast_params": [ctypes.c_void_p, ctypes.c_void_p],
     "zero_shard_info": [ctypes.c_void_p, ctypes.POINTER(zero_shard_info_t)],
+    "zero_enable_dynamic_loss_scale": [ctypes.c_void_p, ctypes.POINTER(zero_loss_scaler_t), ctypes.c_void_p],
+    "zero_loss_scale": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32),
+                        ctypes.c_void_p],
     "zero_shard_pieces": [ctypes.c_void_p, c_i64p, ctypes.c_int64],
     "zero_shard_query": [ctypes.c_void_p, c_i64p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
                          ctypes.POINTER(ctypes.c_float), ctypes.c_void_p],
@@ -151,6 +160,16 @@ def zero_adam_step(h, hp, fuse_cast, stream):
 
 def zero_cast_params(h, stream):
     _call("zero_cast_params", h, stream)
+
+
+def zero_enable_dynamic_loss_scale(h, cfg, stream):
+    _call("zero_enable_dynamic_loss_scale", h, ctypes.byref(cfg), stream)
+
+
+def zero_loss_scale(h, stream):
+    sc, good = ctypes.c_float(), ctypes.c_int32()
+    _call("zero_loss_scale", h, ctypes.byref(sc), ctypes.byref(good), stream)
+    return sc.value, good.value
 
 
 def zero_shard_info(h):

@@ -290,13 +290,20 @@ struct StatsArgs {
   int64_t n_chunks;
   const uint16_t* flat_g;  // flat [psi] gradient, or null to use chunk.g16
   float inv;
+  int32_t dyn_slot;        // >= 0: unscale by 1 / sc->slot[dyn_slot].scale instead of inv
   DevScalars* sc;
   StatsPart* parts;
 };
 
+// The unscale factor of an intake pass: the call's inv, or 1 / the device-resident
+// dynamic loss scale (fp32, correctly rounded) of the given slot.
+__device__ __forceinline__ float intake_inv(float inv, int32_t dyn_slot, const DevScalars* sc) {
+  return dyn_slot >= 0 ? 1.0f / sc->slot[dyn_slot].scale : inv;
+}
+
 template <int DT>
 __global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
-  Stats16Op<DT> op{nullptr, a.inv, SumSq{}};
+  Stats16Op<DT> op{nullptr, intake_inv(a.inv, a.dyn_slot, a.sc), SumSq{}};
   for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
     const Chunk ch = a.chunks[c];
     op.g = a.flat_g ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
@@ -318,6 +325,7 @@ struct ReduceArgs {
   const uint16_t* ranks[kMaxRanks];
   int32_t n_ranks;
   float inv;
+  int32_t dyn_slot;        // as in StatsArgs
   float* red;
   DevScalars* sc;
   StatsPart* parts;
@@ -424,7 +432,7 @@ struct ReduceOp {
 
 template <int DT, int NR, bool ACC>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
-  ReduceOp<DT, NR, ACC> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, a.inv, SumSq{}};
+  ReduceOp<DT, NR, ACC> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc), SumSq{}};
   for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
     const Chunk ch = a.chunks[c];
     op.gs.flat_off = ch.flat_off;
@@ -576,6 +584,9 @@ struct AdamArgs {
   float max_norm;
   float inv;
   float lr, beta1, beta2, eps, wd;
+  int32_t dyn;             // dynamic loss scale: unscale by 1 / slot.scale and update it
+  float growth, backoff, min_scale;
+  int32_t interval;
 };
 
 // Step scalars, computed identically by every block from the device scalar
@@ -596,7 +607,21 @@ __device__ __forceinline__ int step_scalars(const AdamArgs& a, AdamScalars& s, S
     next.p1 = cur.p1 * (double)a.beta1;
     next.p2 = cur.p2 * (double)a.beta2;
   }
-  s.inv = a.inv;
+  if (a.dyn) {
+    // backoff on an overflow step (not below the floor), growth after `interval` good steps
+    if (skip) {
+      const float b = cur.scale * a.backoff;
+      next.scale = b < a.min_scale ? a.min_scale : b;
+      next.good = 0;
+    } else {
+      next.good = cur.good + 1;
+      if (next.good == a.interval) {
+        next.scale = cur.scale * a.growth;
+        next.good = 0;
+      }
+    }
+  }
+  s.inv = a.dyn ? 1.0f / cur.scale : a.inv;
   s.clip = clip;
   s.b1 = a.beta1;
   s.b2 = a.beta2;
@@ -745,12 +770,12 @@ static unsigned stats_grid(int64_t n_chunks, int64_t grid_cap) {
 }
 
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
-                          DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st) {
+                          int32_t dyn_slot, DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st) {
   if (n_chunks == 0) {
     hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc);
     return hipGetLastError();
   }
-  StatsArgs a{chunks, n_chunks, flat_g, inv, sc, parts};
+  StatsArgs a{chunks, n_chunks, flat_g, inv, dyn_slot, sc, parts};
   const unsigned g = stats_grid(n_chunks, grid_cap);
   if (dtype == ZERO_BF16)
     hipLaunchKernelGGL(stats16_kernel<ZERO_BF16>, dim3(g), dim3(kBlock), 0, st, a);
@@ -785,7 +810,7 @@ static void launch_accum_first(const ReduceArgs& a, int src, unsigned g, hipStre
 }
 
 static ReduceArgs make_reduce_args(const Chunk* chunks, int64_t n_chunks, const void* const* ranks, int32_t n_ranks,
-                                   float inv, float* red, DevScalars* sc, StatsPart* parts) {
+                                   float inv, int32_t dyn_slot, float* red, DevScalars* sc, StatsPart* parts) {
   ReduceArgs a;
   a.chunks = chunks;
   a.n_chunks = n_chunks;
@@ -793,6 +818,7 @@ static ReduceArgs make_reduce_args(const Chunk* chunks, int64_t n_chunks, const 
     a.ranks[q] = (ranks && q < n_ranks) ? static_cast<const uint16_t*>(ranks[q]) : nullptr;
   a.n_ranks = n_ranks > 0 ? n_ranks : 1;
   a.inv = inv;
+  a.dyn_slot = dyn_slot;
   a.red = red;
   a.sc = sc;
   a.parts = parts;
@@ -811,13 +837,13 @@ static int src_code(int32_t n_ranks) {
 // Intake with statistics into red: u = (accumulate ? red + s : s) * inv, or red * inv
 // when n_ranks < 0; the local flag and sum of squares go to the scalar block.
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                         int32_t n_ranks, bool accumulate, float inv, float* red, DevScalars* sc, StatsPart* parts,
-                         int64_t grid_cap, hipStream_t st) {
+                         int32_t n_ranks, bool accumulate, float inv, int32_t dyn_slot, float* red, DevScalars* sc,
+                         StatsPart* parts, int64_t grid_cap, hipStream_t st) {
   if (n_chunks == 0) {
     hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc);
     return hipGetLastError();
   }
-  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, inv, red, sc, parts);
+  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, inv, dyn_slot, red, sc, parts);
   const unsigned g = stats_grid(n_chunks, grid_cap);
   const int src = src_code(n_ranks);
   if (dtype == ZERO_BF16) {
@@ -834,7 +860,7 @@ hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const
 hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
                              int32_t n_ranks, bool first, float* red, int64_t grid_cap, hipStream_t st) {
   if (n_chunks == 0) return hipSuccess;
-  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, 1.0f, red, nullptr, nullptr);
+  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, 1.0f, -1, red, nullptr, nullptr);
   const unsigned g = clamp_grid(n_chunks * ZS_ADAM_SPLIT, grid_cap);
   const int src = src_code(n_ranks);
   if (dtype == ZERO_BF16) {
@@ -874,7 +900,8 @@ hipError_t launch_adam(int dtype, int grad_source, bool cast, const AdamArgs& a,
 hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* chunks, int64_t n_chunks,
                             const uint16_t* flat_g, const float* red, float* master, float* m, float* v,
                             DevScalars* sc, int32_t slot, int32_t other_flag, double other_sumsq, float max_norm,
-                            float inv, const zero_adam_hparams_t* hp, int64_t grid_cap, hipStream_t st) {
+                            float inv, const zero_adam_hparams_t* hp, const zero_loss_scaler_t* dyn,
+                            int64_t grid_cap, hipStream_t st) {
   AdamArgs a;
   a.chunks = chunks;
   a.n_chunks = n_chunks;
@@ -894,6 +921,11 @@ hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* 
   a.beta2 = hp->beta2;
   a.eps = hp->eps;
   a.wd = hp->weight_decay;
+  a.dyn = dyn != nullptr;
+  a.growth = dyn ? dyn->growth_factor : 1.0f;
+  a.backoff = dyn ? dyn->backoff_factor : 1.0f;
+  a.min_scale = dyn ? dyn->min_scale : 1.0f;
+  a.interval = dyn ? dyn->growth_interval : 1;
   return launch_adam(dtype, grad_source, cast, a, grid_cap, st);
 }
 

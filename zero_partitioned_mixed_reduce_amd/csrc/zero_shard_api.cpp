@@ -3,6 +3,8 @@
 // block and kernel launches.  The arithmetic is in kernels.hip.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <cmath>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -15,10 +17,10 @@
 
 namespace zs {
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
-                          DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st);
+                          int32_t dyn_slot, DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st);
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                         int32_t n_ranks, bool accumulate, float inv, float* red, DevScalars* sc, StatsPart* parts,
-                         int64_t grid_cap, hipStream_t st);
+                         int32_t n_ranks, bool accumulate, float inv, int32_t dyn_slot, float* red, DevScalars* sc,
+                         StatsPart* parts, int64_t grid_cap, hipStream_t st);
 hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
                              int32_t n_ranks, bool first, float* red, int64_t grid_cap, hipStream_t st);
 struct AdamArgs;
@@ -31,7 +33,8 @@ hipError_t launch_export(const Chunk* chunks, int64_t n_chunks, const float* src
 hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* chunks, int64_t n_chunks,
                             const uint16_t* flat_g, const float* red, float* master, float* m, float* v,
                             DevScalars* sc, int32_t slot, int32_t other_flag, double other_sumsq, float max_norm,
-                            float inv, const zero_adam_hparams_t* hp, int64_t grid_cap, hipStream_t st);
+                            float inv, const zero_adam_hparams_t* hp, const zero_loss_scaler_t* dyn,
+                            int64_t grid_cap, hipStream_t st);
 }  // namespace zs
 
 namespace {
@@ -75,6 +78,8 @@ struct zero_shard {
   bool cast_pending;
   bool accumulating;   // micro-steps summed into red since the last intake
   int64_t dp_size;
+  bool dynamic;        // device-resident dynamic loss scale enabled
+  zero_loss_scaler_t dyn_cfg;
   // current step
   int grad_source;
   const uint16_t* step_flat_g;
@@ -184,12 +189,14 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
   h->cast_pending = false;
   h->accumulating = false;
   h->dp_size = desc->dp_size;
+  h->dynamic = false;
+  memset(&h->dyn_cfg, 0, sizeof(h->dyn_cfg));
   h->adam_calls = 0;
 
   zs::DevScalars init_sc;
   memset(&init_sc, 0, sizeof(init_sc));
-  init_sc.slot[0] = zs::Slot{0, 1.0, 1.0};
-  init_sc.slot[1] = zs::Slot{0, 1.0, 1.0};
+  init_sc.slot[0] = zs::Slot{0, 1.0, 1.0, 1.0f, 0};
+  init_sc.slot[1] = zs::Slot{0, 1.0, 1.0, 1.0f, 0};
   init_sc.clip = 1.0f;
   zero_status_t rs = ZERO_OK;
   do {
@@ -260,6 +267,15 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
   if (!h) return fail(ZERO_EINVAL, "null handle");
   if (h->phase == kStepped && h->cast_pending)
     return fail(ZERO_ESTATE, "zero_cast_params of the previous step is pending");
+  int32_t dyn_slot = -1;
+  if (inv_loss_scale == ZERO_DEVICE_LOSS_SCALE) {
+    if (!h->dynamic) return fail(ZERO_EINVAL, "ZERO_DEVICE_LOSS_SCALE needs zero_enable_dynamic_loss_scale");
+    dyn_slot = (int32_t)(h->adam_calls & 1);
+  } else if (h->dynamic) {
+    return fail(ZERO_EINVAL, "with dynamic loss scaling pass inv_loss_scale = ZERO_DEVICE_LOSS_SCALE");
+  } else if (!(inv_loss_scale > 0.0f) || !std::isfinite(inv_loss_scale)) {
+    return fail(ZERO_EINVAL, "inv_loss_scale must be finite and positive");
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   DeviceGuard dg(h->device);
   hipError_t e;
@@ -269,8 +285,8 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
       zero_status_t s = check_sources(h, rank_grads, n_ranks);
       if (s != ZERO_OK) return s;
     }
-    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, true, inv_loss_scale, h->red,
-                          h->sc, h->parts, h->grid_stats, st);
+    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, true, inv_loss_scale, dyn_slot,
+                          h->red, h->sc, h->parts, h->grid_stats, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
     h->grad_source = kGradRed;
     h->step_flat_g = nullptr;
@@ -279,7 +295,7 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     return fail(ZERO_ESTATE, "ZERO_ACCUMULATED without zero_accumulate_grads in this step");
   } else if (n_ranks == 0) {
     if (!h->has_registered_grads) return fail(ZERO_EINVAL, "n_ranks == 0 needs gradients registered at init");
-    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, nullptr, inv_loss_scale, h->sc, h->parts,
+    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, nullptr, inv_loss_scale, dyn_slot, h->sc, h->parts,
                            h->grid_stats, st);
     if (e != hipSuccess) return hip_fail("statistics kernel", e);
     h->grad_source = kGradChunk16;
@@ -287,7 +303,8 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
   } else if (n_ranks == 1) {
     if (!rank_grads || !rank_grads[0]) return fail(ZERO_EINVAL, "rank_grads[0] is null");
     const uint16_t* g = static_cast<const uint16_t*>(rank_grads[0]);
-    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, g, inv_loss_scale, h->sc, h->parts, h->grid_stats, st);
+    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, g, inv_loss_scale, dyn_slot, h->sc, h->parts,
+                           h->grid_stats, st);
     if (e != hipSuccess) return hip_fail("statistics kernel", e);
     h->grad_source = kGradFlat16;
     h->step_flat_g = g;
@@ -297,8 +314,8 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     for (int q = 0; q < n_ranks; ++q)
       if (!rank_grads[q]) return fail(ZERO_EINVAL, "rank_grads[" + std::to_string(q) + "] is null");
     if (!h->red) return fail(ZERO_EINVAL, "reducing N_d >= 2 buffers needs bufs.red");
-    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, false, inv_loss_scale, h->red,
-                          h->sc, h->parts, h->grid_stats, st);
+    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, false, inv_loss_scale, dyn_slot,
+                          h->red, h->sc, h->parts, h->grid_stats, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
     h->grad_source = kGradRed;
     h->step_flat_g = nullptr;
@@ -367,7 +384,8 @@ zero_status_t zero_adam_step(zero_shard_t h, const zero_adam_hparams_t* hp, int3
   hipError_t e = zs::launch_adam_step(h->dtype, h->grad_source, fuse_cast != 0, h->chunks, h->n_chunks,
                                       h->step_flat_g, h->red, h->master, h->m, h->v, h->sc,
                                       (int32_t)(h->adam_calls & 1), h->other_flag, h->other_sumsq, h->max_norm,
-                                      h->inv, hp, h->grid_main, static_cast<hipStream_t>(stream));
+                                      h->inv, hp, h->dynamic ? &h->dyn_cfg : nullptr, h->grid_main,
+                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("adam kernel", e);
   h->adam_calls += 1;
   h->phase = kStepped;
@@ -384,6 +402,44 @@ zero_status_t zero_cast_params(zero_shard_t h, void* stream) {
                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("cast kernel", e);
   h->cast_pending = false;
+  return ZERO_OK;
+}
+
+zero_status_t zero_enable_dynamic_loss_scale(zero_shard_t h, const zero_loss_scaler_t* cfg, void* stream) {
+  if (!h || !cfg) return fail(ZERO_EINVAL, "null handle or configuration");
+  if (h->phase != kReady && h->phase != kStepped) return fail(ZERO_ESTATE, "enable loss scaling between steps");
+  if (h->phase == kStepped && h->cast_pending) return fail(ZERO_ESTATE, "zero_cast_params is pending");
+  if (h->accumulating) return fail(ZERO_ESTATE, "enable loss scaling before accumulating micro-steps");
+  if (!(cfg->init_scale > 0.0f) || !std::isfinite(cfg->init_scale) || !(cfg->growth_factor >= 1.0f) ||
+      !(cfg->backoff_factor > 0.0f && cfg->backoff_factor <= 1.0f) || cfg->growth_interval < 1 ||
+      !(cfg->min_scale > 0.0f))
+    return fail(ZERO_EINVAL, "need init_scale > 0, growth_factor >= 1, 0 < backoff_factor <= 1, "
+                             "growth_interval >= 1, min_scale > 0");
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int cur = (int)(h->adam_calls & 1);
+  struct {
+    float scale;
+    int32_t good;
+  } v = {cfg->init_scale, 0};
+  static_assert(sizeof(v) == 8, "scale and good are adjacent in the slot");
+  ZS_HIP(hipMemcpyAsync(&h->sc->slot[cur].scale, &v, sizeof(v), hipMemcpyHostToDevice, st));
+  ZS_HIP(hipStreamSynchronize(st));
+  h->dynamic = true;
+  h->dyn_cfg = *cfg;
+  return ZERO_OK;
+}
+
+zero_status_t zero_loss_scale(zero_shard_t h, float* host_scale, int32_t* host_good, void* stream) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (!h->dynamic) return fail(ZERO_ESTATE, "dynamic loss scaling is not enabled");
+  DeviceGuard dg(h->device);
+  zs::DevScalars sc;
+  zero_status_t s = sync_read_scalars(h, static_cast<hipStream_t>(stream), &sc);
+  if (s != ZERO_OK) return s;
+  const zs::Slot& cur = sc.slot[h->adam_calls & 1];
+  if (host_scale) *host_scale = cur.scale;
+  if (host_good) *host_good = cur.good;
   return ZERO_OK;
 }
 

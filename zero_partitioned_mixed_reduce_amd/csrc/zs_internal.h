@@ -37,7 +37,10 @@ static_assert(sizeof(Chunk) == 48, "chunk layout");
 struct Slot {
   int64_t t;      // applied steps
   double p1, p2;  // beta1^t, beta2^t (fp64 running products)
+  float scale;    // dynamic loss scale
+  int32_t good;   // consecutive steps without overflow since the last scale change
 };
+static_assert(sizeof(Slot) == 32, "slot layout");
 
 // Device-resident scalars of the step (first 256 bytes of the workspace).
 struct alignas(256) DevScalars {

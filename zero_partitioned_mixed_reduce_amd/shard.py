@@ -113,6 +113,15 @@ class ZeroShard:
     def zero_cast_params(self):
         abi.zero_cast_params(self.h, _stream())
 
+    def zero_enable_dynamic_loss_scale(self, init_scale=65536.0, growth_factor=2.0, backoff_factor=0.5,
+                                       growth_interval=1000, min_scale=1.0):
+        cfg = abi.zero_loss_scaler_t(init_scale, growth_factor, backoff_factor, growth_interval, min_scale)
+        abi.zero_enable_dynamic_loss_scale(self.h, cfg, _stream())
+
+    def zero_loss_scale(self):
+        """(current dynamic loss scale, good steps since it last changed)."""
+        return abi.zero_loss_scale(self.h, _stream())
+
     def query(self):
         return abi.zero_shard_query(self.h, _stream())
 
