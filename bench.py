@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--micro-steps", type=int, default=1,
                    help="gradient-accumulation micro-steps per optimizer step (K - 1 accumulations, then the "
                         "step's own intake)")
+    p.add_argument("--dynamic-loss-scale", action="store_true",
+                   help="device-resident dynamic loss scale starting at the workload's loss scale (growth 2, "
+                        "backoff 0.5, interval 1000, floor 1)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1 << 26, help="elements of the oracle's timed sample")
     p.add_argument("--cpu-steps", type=int, default=7)
@@ -61,7 +64,7 @@ def kernel_source_sha():
 class Workload:
     """Device-resident inputs and the library handle for one rank."""
 
-    def __init__(self, w, rank, micro_steps=1):
+    def __init__(self, w, rank, micro_steps=1, dynamic_loss_scale=False):
         import torch
         import synth
         from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
@@ -113,6 +116,11 @@ class Workload:
         torch.cuda.empty_cache()
         self.info = self.shard.info
         self.inv = 1.0 / w.loss_scale
+        self.intake_inv = self.inv
+        if dynamic_loss_scale:
+            from zero_partitioned_mixed_reduce_amd import ZERO_DEVICE_LOSS_SCALE
+            self.shard.zero_enable_dynamic_loss_scale(w.loss_scale, 2.0, 0.5, 1000, 1.0)
+            self.intake_inv = ZERO_DEVICE_LOSS_SCALE
         # the other ranks' sum of squares: the expected value under the synthetic distribution
         sig_u = w.grad_sigma * self.inv * (w.nd ** 0.5 if w.grad_mode == "reduce" else 1.0)
         self.other_sumsq = float(psi - valid) * sig_u * sig_u
@@ -123,7 +131,7 @@ class Workload:
             s.zero_accumulate_grads(self.rank_grads)      # the same gradient buffers every micro-step
         if ev:
             ev[0].record()
-        s.zero_reduce_grads(self.rank_grads, self.inv)
+        s.zero_reduce_grads(self.rank_grads, self.intake_inv)
         if ev:
             ev[1].record()
         s.zero_check_overflow(False)
@@ -217,7 +225,7 @@ def main():
     rank = a.rank if a.rank is not None else w.ranks[0]
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
-    wl = Workload(w, rank, a.micro_steps)
+    wl = Workload(w, rank, a.micro_steps, a.dynamic_loss_scale)
     setup_s = time.perf_counter() - t_setup
     valid = wl.info.valid_elems
     step_b, adam_b = bytes_per_param(w, a.micro_steps)
@@ -269,6 +277,7 @@ def main():
         "config": {"workload": w.name, "psi": w.psi, "dp_size": w.nd, "dp_rank": rank, "shard_params": valid,
                    "param_grad_dtype": DTYPE_NAME[w.dtype], "grad_source": w.grad_mode,
                    "tensors": len(w.numel), "loss_scale": w.loss_scale, "max_norm": w.max_norm,
+                   "loss_scale_mode": "dynamic, device-resident" if a.dynamic_loss_scale else "static",
                    "micro_steps": a.micro_steps,
                    "adam": w.hp},
         "hbm_gbps_step": step_b * valid / (ms_step * 1e-3) / 1e9,
