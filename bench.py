@@ -40,6 +40,12 @@ def parse():
     p.add_argument("--dynamic-loss-scale", action="store_true",
                    help="device-resident dynamic loss scale starting at the workload's loss scale (growth 2, "
                         "backoff 0.5, interval 1000, floor 1)")
+    p.add_argument("--segments", type=int, default=0,
+                   help="track the write-back in this many segments; a second stream waits for each segment and "
+                        "copies it out (a stand-in for the segment's all-gather)")
+    p.add_argument("--segment-consumer", default="copy", choices=["copy", "wait", "none"],
+                   help="with --segments: per segment, wait and copy it out; only wait; or no consumer (the "
+                        "tracking cost alone)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1 << 26, help="elements of the oracle's timed sample")
     p.add_argument("--cpu-steps", type=int, default=7)
@@ -64,7 +70,7 @@ def kernel_source_sha():
 class Workload:
     """Device-resident inputs and the library handle for one rank."""
 
-    def __init__(self, w, rank, micro_steps=1, dynamic_loss_scale=False):
+    def __init__(self, w, rank, micro_steps=1, dynamic_loss_scale=False, segments=0, consumer="copy"):
         import torch
         import synth
         from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
@@ -121,12 +127,22 @@ class Workload:
             from zero_partitioned_mixed_reduce_amd import ZERO_DEVICE_LOSS_SCALE
             self.shard.zero_enable_dynamic_loss_scale(w.loss_scale, 2.0, 0.5, 1000, 1.0)
             self.intake_inv = ZERO_DEVICE_LOSS_SCALE
+        self.segments = []
+        if segments:
+            n = self.shard.zero_set_segments(segments)
+            self.segments = [self.shard.zero_segment_range(k) for k in range(n)]
+            self.consumer = torch.cuda.Stream()
+            self.consumer_mode = consumer
+            self.gather = torch.empty(max(valid, 1), dtype=torch.int16, device="cuda")
         # the other ranks' sum of squares: the expected value under the synthetic distribution
         sig_u = w.grad_sigma * self.inv * (w.nd ** 0.5 if w.grad_mode == "reduce" else 1.0)
         self.other_sumsq = float(psi - valid) * sig_u * sig_u
 
     def step(self, ev=None):
         s, w = self.shard, self.w
+        if self.segments:
+            import torch
+            torch.cuda.current_stream().wait_stream(self.consumer)   # the previous step's gathers are done
         for _ in range(self.micro_steps - 1):
             s.zero_accumulate_grads(self.rank_grads)      # the same gradient buffers every micro-step
         if ev:
@@ -140,6 +156,24 @@ class Workload:
                          fuse_cast=True)
         if ev:
             ev[2].record()
+        if self.segments and self.consumer_mode != "none":
+            self._consume(ev)
+
+    def _consume(self, ev):
+        """Per segment: wait for its write-back, then copy its 16-bit slice out (the
+        all-gather of that segment would start here)."""
+        import torch
+        b = self.info.shard_begin
+        flat = self.params if not isinstance(self.params, list) else None
+        with torch.cuda.stream(self.consumer):
+            for k, (lo, ln) in enumerate(self.segments):
+                self.shard.zero_wait_segment(k, self.consumer)
+                if ev and k == 0:
+                    ev[3].record(self.consumer)
+                if flat is not None and self.consumer_mode == "copy":
+                    self.gather[lo:lo + ln].copy_(flat[b + lo:b + lo + ln])
+            if ev:
+                ev[4].record(self.consumer)
 
 
 def bytes_per_param(w, micro_steps=1):
@@ -225,7 +259,7 @@ def main():
     rank = a.rank if a.rank is not None else w.ranks[0]
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
-    wl = Workload(w, rank, a.micro_steps, a.dynamic_loss_scale)
+    wl = Workload(w, rank, a.micro_steps, a.dynamic_loss_scale, a.segments, a.segment_consumer)
     setup_s = time.perf_counter() - t_setup
     valid = wl.info.valid_elems
     step_b, adam_b = bytes_per_param(w, a.micro_steps)
@@ -245,7 +279,7 @@ def main():
     q = wl.shard.query()
     assert not q["skipped"] and q["t"] == a.warmup, q
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(a.steps):
@@ -292,6 +326,19 @@ def main():
                      "avg_launch_ms": adam_ms},
         "setup_s": setup_s,
     }
+    if wl.segments:
+        out["config"]["segments"] = len(wl.segments)
+        copies = a.segment_consumer == "copy" and not isinstance(wl.params, list)
+        out["pipeline"] = {
+            "segments": len(wl.segments),
+            "consumer": {"copy": "wait per segment, then copy its 16-bit slice" if copies else "wait per segment",
+                         "wait": "wait per segment", "none": "none"}[a.segment_consumer],
+            "adam_ms": adam_ms,
+            "timeouts": wl.shard.zero_segment_timeouts(),
+        }
+        if a.segment_consumer != "none":
+            out["pipeline"]["first_segment_ready_ms"] = sum(e[1].elapsed_time(e[3]) for e in evs) / a.steps
+            out["pipeline"]["last_segment_done_ms"] = sum(e[1].elapsed_time(e[4]) for e in evs) / a.steps
     if not a.no_cpu_baseline:
         n = min(a.cpu_sample, valid)
         rate, secs = cpu_baseline(w, n, a.cpu_steps)

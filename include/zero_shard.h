@@ -124,6 +124,41 @@ zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* 
 zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
                               const float* master_init, void* stream, zero_shard_t* out);
 
+/* Chunk-pipelined step ("DeepSpeed ZeRO", ZeRO Stage 1, 通信与计算重叠: the
+ * all-gather of updated parameters can start on each part as soon as it is
+ * updated, alongside the update of the rest).  The shard's chunks are split
+ * into up to 256 contiguous segments; the kernel that writes the 16-bit slice
+ * (zero_adam_step with fuse_cast, else zero_cast_params) marks each segment
+ * complete on the device as soon as its last element is written, and a consumer
+ * stream can wait for one segment and then start that segment's all-gather
+ * while later segments are still being updated.  A skipped step marks every
+ * segment complete at once (nothing is written). */
+
+/* Splits the write-back into min(n_segments, num_chunks) segments of equal
+ * chunk counts (0 turns tracking off; the default).  Between steps only
+ * (ESTATE otherwise); EINVAL unless 0 <= n_segments <= 256.  *out_segments
+ * (nullable) receives the number of segments. */
+zero_status_t zero_set_segments(zero_shard_t h, int32_t n_segments, int32_t* out_segments);
+
+/* Segment k covers the logical shard elements [*shard_begin, *shard_begin +
+ * *len) (valid elements only; flat model index = shard_begin of the shard plus
+ * these).  EINVAL if there is no segment k. */
+zero_status_t zero_segment_range(zero_shard_t h, int32_t k, int64_t* shard_begin, int64_t* len);
+
+/* Enqueues on `stream` a wait that ends when segment k of the latest step's
+ * 16-bit write-back is complete; work enqueued after it on `stream` sees the
+ * segment's 16-bit parameters of that step.  `stream` first waits (event) until
+ * the step's own stream reaches the write-back kernel; then one polling lane
+ * watches the segment's flag.  Call it after the write-back was enqueued with
+ * segments on (ESTATE otherwise), typically on a stream other than the
+ * step's.  If the segment is not complete within about 2 s of polling the wait
+ * gives up and the count returned by zero_segment_timeouts increases; after
+ * that, waits on this handle return at once. */
+zero_status_t zero_wait_segment(zero_shard_t h, int32_t k, void* stream);
+
+/* Number of segment waits that gave up since init (synchronises the stream). */
+zero_status_t zero_segment_timeouts(zero_shard_t h, int64_t* timeouts, void* stream);
+
 /* Dynamic loss scale kept on the device ("DeepSpeed ZeRO" 配置说明: fp16.loss_scale
  * = 0 selects dynamic scaling, starting at 2^initial_scale_power).  The pages give
  * no update rule; the one applied, by zero_adam_step on the device, is: after a

@@ -104,7 +104,7 @@ class Sim:
     """N_d ranks of the HIP path plus the oracle, stepped together."""
 
     def __init__(self, numel, nd, dtype, p16_full, master_full, grad_mode, per_tensor_params=False,
-                 param_misalign=(0,), grad_misalign=(0,), ranks=None, with_red=None):
+                 param_misalign=(0,), grad_misalign=(0,), ranks=None, with_red=None, segments=0):
         self.numel, self.nd, self.dtype, self.grad_mode = list(numel), nd, dtype, grad_mode
         self.psi = sum(numel)
         self.ranks = list(range(nd)) if ranks is None else ranks
@@ -138,6 +138,8 @@ class Sim:
             red = (grad_mode == "reduce") if with_red is None else with_red
             self.shards[r] = ZeroShard(numel, nd, r, dtype, views if views is not None else store, grads=grads,
                                        master_init=mi, with_red=red)
+            if segments:
+                self.shards[r].zero_set_segments(segments)
 
     def enable_dynamic(self, init_scale, growth, backoff, interval, min_scale):
         """Device-resident dynamic loss scale on every simulated rank, mirrored by

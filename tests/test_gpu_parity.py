@@ -421,3 +421,110 @@ def test_dynamic_loss_scale_errors():
     s.zero_adam_step(1e-3, 0.9, 0.999, 1e-8, 0.0)
     assert s.query()["t"] == 2
     assert s.zero_loss_scale() == (256.0, 1)
+
+
+# --------------------------------------------------------------------------
+# chunk-pipelined step: per-segment completion of the 16-bit write-back
+
+
+@pytest.mark.parametrize("fuse,segments", [(True, 3), (False, 7), (True, 256)])
+def test_segmented_write_back_tiny_all_ranks(fuse, segments):
+    """Tracking segments changes no result (the inf at step 2 skips)."""
+    w = recipes.tiny()
+    psi = w.psi
+    master, p16 = master_of(w, psi)
+    sim = Sim(w.numel, w.nd, w.dtype, p16, master, "reduce", segments=segments)
+    sim.p16_initial = p16.copy()
+    S = sim.plans[0][1]
+    for step in range(1, 4):
+        g = grads_for(w, step, psi, w.nd)
+        if step == 2:
+            _poison(g[1], 2 * S + 99, w.dtype)
+        sim.step(g, 1.0 / w.loss_scale, w.max_norm, hp_of(w.hp), fuse=fuse)
+        sim.compare()
+    assert all(s.zero_segment_timeouts() == 0 for s in sim.shards.values())
+
+
+def _segment_ranges(s, n):
+    return [s.zero_segment_range(k) for k in range(n)]
+
+
+@pytest.mark.parametrize("mode,nd,rank,segments", [("flat", 1, 0, 16), ("ragged", 3, 1, 9), ("flat", 5, 4, 256)])
+def test_segment_consumer_sees_each_step(mode, nd, rank, segments):
+    """A consumer stream waits for each segment, then copies it (standing in for the
+    segment's all-gather): every copy equals the step's final 16-bit slice, also for
+    a skipped step and for the unfused write-back."""
+    w = recipes.ragged_mini(nd) if mode == "ragged" else recipes.gpt2_shard()
+    psi = w.psi if mode == "ragged" else 3_000_017
+    numel = w.numel if mode == "ragged" else [psi]
+    master, p16 = master_of(w, psi)
+    sim = Sim(numel, nd, w.dtype, p16, None, mode, per_tensor_params=(mode == "ragged"), ranks=[rank])
+    s = sim.shards[rank]
+    n = s.zero_set_segments(segments)
+    assert n == min(segments, s.info.num_chunks)
+    _, _, b, valid = sim.plans[rank]
+    ranges = _segment_ranges(s, n)
+    assert ranges[0][0] == 0 and sum(ln for _, ln in ranges) == valid
+    assert all(ranges[k][0] + ranges[k][1] == ranges[k + 1][0] for k in range(n - 1))
+    store, views = sim.params[rank]
+    consumer = torch.cuda.Stream()
+    for step in range(1, 5):
+        g = grads_for(w, step, psi, 1)
+        if step == 3:
+            _poison(g[0], b + valid // 2, w.dtype)
+        fuse = step != 2
+        sim.step(g, 1.0, w.max_norm, hp_of(w.hp), fuse=fuse)
+        flat_params = store if views is None else None
+        got = torch.zeros(valid, dtype=torch.int16, device="cuda")
+        main = torch.cuda.current_stream()
+        consumer.wait_stream(main)         # the consumer's own inputs (got) are ready
+        with torch.cuda.stream(consumer):
+            for k, (lo, ln) in enumerate(ranges):
+                s.zero_wait_segment(k, consumer)
+                if flat_params is not None:
+                    got[lo:lo + ln].copy_(flat_params[b + lo:b + lo + ln])
+        torch.cuda.synchronize()
+        exp = sim.ostates[rank].p16
+        if flat_params is not None:
+            assert (host16(got) == exp).all(), step
+        sim.compare()
+    assert s.zero_segment_timeouts() == 0
+
+
+def test_segment_api_errors():
+    from zero_partitioned_mixed_reduce_amd import ZeroError
+    from zero_partitioned_mixed_reduce_amd._abi import ZERO_ESTATE, ZERO_EINVAL
+    from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
+    psi = 100_000
+    w = recipes.tiny()
+    _, p16 = master_of(w, psi)
+    g = dev16(grads_for(w, 1, psi, 1)[0])
+    s = ZeroShard([psi], 1, 0, F16, dev16(p16))
+    assert s.zero_set_segments(0) == 0
+    for bad in (-1, 257):
+        with pytest.raises(ZeroError) as e:
+            s.zero_set_segments(bad)
+        assert e.value.status == ZERO_EINVAL
+    n = s.zero_set_segments(4)
+    assert n == 4
+    with pytest.raises(ZeroError) as e:
+        s.zero_segment_range(4)
+    assert e.value.status == ZERO_EINVAL
+    with pytest.raises(ZeroError) as e:
+        s.zero_wait_segment(0)                       # no step yet
+    assert e.value.status == ZERO_ESTATE
+    s.zero_reduce_grads([g], 1.0)
+    with pytest.raises(ZeroError) as e:
+        s.zero_set_segments(2)                       # inside a step
+    assert e.value.status == ZERO_ESTATE
+    s.zero_check_overflow(False)
+    s.zero_grad_norm(0.0, 1.0)
+    s.zero_adam_step(1e-3, 0.9, 0.999, 1e-8, 0.0, fuse_cast=False)
+    with pytest.raises(ZeroError) as e:
+        s.zero_wait_segment(0)                       # write-back not enqueued yet
+    assert e.value.status == ZERO_ESTATE
+    s.zero_cast_params()
+    for k in range(n):
+        s.zero_wait_segment(k)
+    torch.cuda.synchronize()
+    assert s.zero_segment_timeouts() == 0

@@ -64,6 +64,10 @@ _PROTOS = {
     "zero_enable_dynamic_loss_scale": [ctypes.c_void_p, ctypes.POINTER(zero_loss_scaler_t), ctypes.c_void_p],
     "zero_loss_scale": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32),
                         ctypes.c_void_p],
+    "zero_set_segments": [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
+    "zero_segment_range": [ctypes.c_void_p, ctypes.c_int32, c_i64p, c_i64p],
+    "zero_wait_segment": [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+    "zero_segment_timeouts": [ctypes.c_void_p, c_i64p, ctypes.c_void_p],
     "zero_shard_pieces": [ctypes.c_void_p, c_i64p, ctypes.c_int64],
     "zero_shard_query": [ctypes.c_void_p, c_i64p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
                          ctypes.POINTER(ctypes.c_float), ctypes.c_void_p],
@@ -160,6 +164,28 @@ def zero_adam_step(h, hp, fuse_cast, stream):
 
 def zero_cast_params(h, stream):
     _call("zero_cast_params", h, stream)
+
+
+def zero_set_segments(h, n_segments):
+    n = ctypes.c_int32()
+    _call("zero_set_segments", h, n_segments, ctypes.byref(n))
+    return n.value
+
+
+def zero_segment_range(h, k):
+    b, n = ctypes.c_int64(), ctypes.c_int64()
+    _call("zero_segment_range", h, k, ctypes.byref(b), ctypes.byref(n))
+    return b.value, n.value
+
+
+def zero_wait_segment(h, k, stream):
+    _call("zero_wait_segment", h, k, stream)
+
+
+def zero_segment_timeouts(h, stream):
+    n = ctypes.c_int64()
+    _call("zero_segment_timeouts", h, ctypes.byref(n), stream)
+    return n.value
 
 
 def zero_enable_dynamic_loss_scale(h, cfg, stream):

@@ -11,6 +11,7 @@
 
 #include <new>
 #include <string>
+#include <vector>
 
 #include "zero_shard.h"
 #include "zs_internal.h"
@@ -25,7 +26,9 @@ hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, c
                              int32_t n_ranks, bool first, float* red, int64_t grid_cap, hipStream_t st);
 struct AdamArgs;
 hipError_t launch_cast(int dtype, const Chunk* chunks, int64_t n_chunks, const float* master,
-                       const DevScalars* sc, int64_t grid_cap, hipStream_t st);
+                       const DevScalars* sc, const SegArgs* seg, int64_t grid_cap, hipStream_t st);
+hipError_t launch_seg_wait(const SegState* seg, int32_t k, uint64_t epoch, int64_t max_polls, DevScalars* sc,
+                           hipStream_t st);
 hipError_t launch_init(int dtype, const Chunk* chunks, int64_t n_chunks, float* master, float* m, float* v,
                        int64_t state_elems, const float* master_init, int64_t grid_cap, hipStream_t st);
 hipError_t launch_export(const Chunk* chunks, int64_t n_chunks, const float* src, float* dst, int64_t grid_cap,
@@ -34,7 +37,7 @@ hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* 
                             const uint16_t* flat_g, const float* red, float* master, float* m, float* v,
                             DevScalars* sc, int32_t slot, int32_t other_flag, double other_sumsq, float max_norm,
                             float inv, const zero_adam_hparams_t* hp, const zero_loss_scaler_t* dyn,
-                            int64_t grid_cap, hipStream_t st);
+                            const SegArgs* seg, int64_t grid_cap, hipStream_t st);
 }  // namespace zs
 
 namespace {
@@ -73,6 +76,12 @@ struct zero_shard {
   zs::StatsPart* parts;
   zs::Chunk* chunks;
   int64_t n_chunks;
+  std::vector<int64_t> chunk_begin;  // logical shard offset of each chunk, plus the end
+  zs::SegState* seg;
+  int32_t n_seg;                     // segments of the write-back (0: not tracked)
+  int64_t seg_per;                   // chunks per segment
+  bool seg_tracked;                  // the latest write-back tracked the current segments
+  hipEvent_t wb_event;               // recorded just before each tracked write-back launch
   int64_t grid_stats, grid_main;
   Phase phase;
   bool cast_pending;
@@ -182,6 +191,14 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
   h->parts = reinterpret_cast<zs::StatsPart*>(ws + zs::kPartsOff);
   h->chunks = reinterpret_cast<zs::Chunk*>(ws + zs::kChunksOff);
   h->n_chunks = (int64_t)p.chunks.size();
+  h->seg = reinterpret_cast<zs::SegState*>(ws + zs::kSegOff);
+  h->n_seg = 0;
+  h->seg_per = 1;
+  h->seg_tracked = false;
+  h->wb_event = nullptr;
+  h->chunk_begin.resize(p.chunks.size() + 1);
+  for (size_t c = 0; c < p.chunks.size(); ++c) h->chunk_begin[c] = p.chunks[c].shard_off;
+  h->chunk_begin[p.chunks.size()] = p.chunks.empty() ? 0 : p.chunks.back().shard_off + p.chunks.back().len;
   h->grid_main = (int64_t)cus * blocks_per_cu();
   // statistics passes stay persistent: at most 8 resident blocks per CU (and the partial slots)
   h->grid_stats = (int64_t)cus * 8 < zs::kMaxStatsBlocks ? (int64_t)cus * 8 : zs::kMaxStatsBlocks;
@@ -204,6 +221,15 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
       rs = hip_fail("hipMemcpyAsync(scalars)", e);
       break;
     }
+    if ((e = hipEventCreateWithFlags(&h->wb_event, hipEventDisableTiming)) != hipSuccess) {
+      rs = hip_fail("hipEventCreateWithFlags", e);
+      break;
+    }
+    static const zs::SegState zero_segs[zs::kMaxSegments] = {};
+    if ((e = hipMemcpyAsync(h->seg, zero_segs, sizeof(zero_segs), hipMemcpyHostToDevice, st)) != hipSuccess) {
+      rs = hip_fail("hipMemcpyAsync(segments)", e);
+      break;
+    }
     if (!p.chunks.empty() &&
         (e = hipMemcpyAsync(h->chunks, p.chunks.data(), p.chunks.size() * sizeof(zs::Chunk), hipMemcpyHostToDevice,
                             st)) != hipSuccess) {
@@ -221,6 +247,7 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
     }
   } while (0);
   if (rs != ZERO_OK) {
+    if (h->wb_event) (void)hipEventDestroy(h->wb_event);
     delete h;
     return rs;
   }
@@ -376,17 +403,27 @@ zero_status_t zero_grad_norm(zero_shard_t h, double other_ranks_sumsq, float max
   return ZERO_OK;
 }
 
+namespace {
+zs::SegArgs seg_args(const zero_shard* h, int64_t epoch) {
+  return zs::SegArgs{h->seg, h->seg_per, h->n_chunks, h->n_seg, (uint64_t)epoch};
+}
+}  // namespace
+
 zero_status_t zero_adam_step(zero_shard_t h, const zero_adam_hparams_t* hp, int32_t fuse_cast, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
   if (!hp) return fail(ZERO_EINVAL, "null hyperparameters");
   if (h->phase != kNormed) return fail(ZERO_ESTATE, "zero_adam_step must follow zero_grad_norm");
   DeviceGuard dg(h->device);
+  const zs::SegArgs seg = seg_args(h, h->adam_calls + 1);
+  const bool track = h->n_seg > 0 && fuse_cast != 0;
+  if (track) ZS_HIP(hipEventRecord(h->wb_event, static_cast<hipStream_t>(stream)));
   hipError_t e = zs::launch_adam_step(h->dtype, h->grad_source, fuse_cast != 0, h->chunks, h->n_chunks,
                                       h->step_flat_g, h->red, h->master, h->m, h->v, h->sc,
                                       (int32_t)(h->adam_calls & 1), h->other_flag, h->other_sumsq, h->max_norm,
-                                      h->inv, hp, h->dynamic ? &h->dyn_cfg : nullptr, h->grid_main,
-                                      static_cast<hipStream_t>(stream));
+                                      h->inv, hp, h->dynamic ? &h->dyn_cfg : nullptr, h->n_seg ? &seg : nullptr,
+                                      h->grid_main, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("adam kernel", e);
+  h->seg_tracked = track;
   h->adam_calls += 1;
   h->phase = kStepped;
   h->cast_pending = fuse_cast == 0;
@@ -398,10 +435,70 @@ zero_status_t zero_cast_params(zero_shard_t h, void* stream) {
   if (h->phase != kStepped) return fail(ZERO_ESTATE, "zero_cast_params must follow zero_adam_step");
   if (!h->cast_pending) return ZERO_OK;
   DeviceGuard dg(h->device);
-  hipError_t e = zs::launch_cast(h->dtype, h->chunks, h->n_chunks, h->master, h->sc, h->grid_main,
-                                 static_cast<hipStream_t>(stream));
+  const zs::SegArgs seg = seg_args(h, h->adam_calls);
+  if (h->n_seg > 0) ZS_HIP(hipEventRecord(h->wb_event, static_cast<hipStream_t>(stream)));
+  hipError_t e = zs::launch_cast(h->dtype, h->chunks, h->n_chunks, h->master, h->sc, h->n_seg ? &seg : nullptr,
+                                 h->grid_main, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("cast kernel", e);
+  h->seg_tracked = h->n_seg > 0;
   h->cast_pending = false;
+  return ZERO_OK;
+}
+
+zero_status_t zero_set_segments(zero_shard_t h, int32_t n_segments, int32_t* out_segments) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (n_segments < 0 || n_segments > zs::kMaxSegments) return fail(ZERO_EINVAL, "n_segments must be 0..256");
+  if (h->phase != kReady && h->phase != kStepped) return fail(ZERO_ESTATE, "set segments between steps");
+  if (h->phase == kStepped && h->cast_pending) return fail(ZERO_ESTATE, "zero_cast_params is pending");
+  // every counter is re-armed once a write-back completes, so the layout may change between steps
+  if (n_segments == 0 || h->n_chunks == 0) {
+    h->n_seg = 0;
+    h->seg_per = 1;
+  } else {
+    h->seg_per = (h->n_chunks + n_segments - 1) / n_segments;
+    h->n_seg = (int32_t)((h->n_chunks + h->seg_per - 1) / h->seg_per);
+  }
+  h->seg_tracked = false;
+  if (out_segments) *out_segments = h->n_seg;
+  return ZERO_OK;
+}
+
+zero_status_t zero_segment_range(zero_shard_t h, int32_t k, int64_t* shard_begin, int64_t* len) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (k < 0 || k >= h->n_seg) return fail(ZERO_EINVAL, "no segment " + std::to_string(k));
+  const int64_t c0 = (int64_t)k * h->seg_per;
+  const int64_t c1 = c0 + h->seg_per < h->n_chunks ? c0 + h->seg_per : h->n_chunks;
+  if (shard_begin) *shard_begin = h->chunk_begin[c0];
+  if (len) *len = h->chunk_begin[c1] - h->chunk_begin[c0];
+  return ZERO_OK;
+}
+
+zero_status_t zero_wait_segment(zero_shard_t h, int32_t k, void* stream) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (k < 0 || k >= h->n_seg) return fail(ZERO_EINVAL, "no segment " + std::to_string(k));
+  if (h->adam_calls == 0 || h->phase != kStepped || h->cast_pending)
+    return fail(ZERO_ESTATE, "the write-back of this step has not been enqueued");
+  if (!h->seg_tracked) return fail(ZERO_ESTATE, "the latest write-back did not track these segments");
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // The polling lane starts only once the step's stream has reached the write-back kernel, so
+  // it spins for at most that kernel's run time; about 2 s of polls (s_sleep 32 is about 2048
+  // clocks each) bound it in any case.
+  ZS_HIP(hipStreamWaitEvent(st, h->wb_event, 0));
+  const int64_t max_polls = 1000000;
+  hipError_t e = zs::launch_seg_wait(h->seg, k, (uint64_t)h->adam_calls, max_polls, h->sc,
+                                     st);
+  if (e != hipSuccess) return hip_fail("segment wait kernel", e);
+  return ZERO_OK;
+}
+
+zero_status_t zero_segment_timeouts(zero_shard_t h, int64_t* timeouts, void* stream) {
+  if (!h || !timeouts) return fail(ZERO_EINVAL, "null handle or output");
+  DeviceGuard dg(h->device);
+  zs::DevScalars sc;
+  zero_status_t s = sync_read_scalars(h, static_cast<hipStream_t>(stream), &sc);
+  if (s != ZERO_OK) return s;
+  *timeouts = sc.wait_timeouts;
   return ZERO_OK;
 }
 
@@ -488,6 +585,7 @@ zero_status_t zero_export_state(zero_shard_t h, int32_t which, float* dst, void*
 }
 
 zero_status_t zero_shard_destroy(zero_shard_t h) {
+  if (h && h->wb_event) (void)hipEventDestroy(h->wb_event);
   delete h;
   return ZERO_OK;
 }

@@ -52,8 +52,36 @@ struct alignas(256) DevScalars {
   float clip;
   int32_t skipped;
   int64_t report_t;
+  uint32_t wait_timeouts;  // segment waits that gave up (see SegState)
 };
 static_assert(sizeof(DevScalars) == 256, "scalar block");
+
+// Completion of one segment of the 16-bit write-back (chunk-pipelined step).
+// A segment is a run of consecutive chunks.  Work item i of the kernel that
+// writes the 16-bit slice arrives, once its stores are complete, on sub-counter
+// i % kSegSubs of its segment (spreading the atomics over several addresses);
+// the last arrival on a sub-counter re-arms it and arrives on `count`, and the
+// last of those re-arms `count` and publishes the step's number in `epoch`.
+constexpr int kMaxSegments = 256;
+constexpr int kSegSubs = 16;
+struct alignas(64) SegSub {
+  uint32_t count;  // work items of this sub-counter that have arrived
+};
+struct alignas(64) SegState {
+  uint64_t epoch;  // 1-based zero_adam_step call whose write-back of this segment is complete
+  uint32_t count;  // sub-counters of the current write-back that have completed
+  SegSub sub[kSegSubs];
+};
+static_assert(sizeof(SegSub) == 64 && sizeof(SegState) == 64 * (kSegSubs + 1), "segment layout");
+
+// Segment configuration passed to the kernel that writes the 16-bit slice.
+struct SegArgs {
+  SegState* seg;       // null: no completion tracking
+  int64_t per_seg;     // chunks per segment (the last one may hold fewer)
+  int64_t n_chunks;
+  int32_t n_seg;
+  uint64_t epoch;      // number of this zero_adam_step call (1-based)
+};
 
 struct StatsPart {
   uint64_t sumsq_bits;  // fp64 partial sum of squares of one block, as bits
@@ -61,7 +89,8 @@ struct StatsPart {
 };
 
 constexpr int64_t kPartsOff = sizeof(DevScalars);
-constexpr int64_t kChunksOff = kPartsOff + kMaxStatsBlocks * (int64_t)sizeof(StatsPart);
+constexpr int64_t kSegOff = kPartsOff + kMaxStatsBlocks * (int64_t)sizeof(StatsPart);
+constexpr int64_t kChunksOff = kSegOff + kMaxSegments * (int64_t)sizeof(SegState);
 
 struct Piece {
   int64_t tensor, tensor_off, shard_off, state_off, len;

@@ -113,6 +113,24 @@ class ZeroShard:
     def zero_cast_params(self):
         abi.zero_cast_params(self.h, _stream())
 
+    def zero_set_segments(self, n_segments):
+        """Track completion of the 16-bit write-back in up to n_segments segments; returns
+        the number of segments (0 turns tracking off)."""
+        return abi.zero_set_segments(self.h, n_segments)
+
+    def zero_segment_range(self, k):
+        """(first logical shard element, number of elements) of segment k."""
+        return abi.zero_segment_range(self.h, k)
+
+    def zero_wait_segment(self, k, stream=None):
+        """Enqueue on `stream` (a torch stream; default: the current one) a wait for
+        segment k of the latest step's write-back."""
+        s = _stream() if stream is None else ctypes.c_void_p(stream.cuda_stream)
+        abi.zero_wait_segment(self.h, k, s)
+
+    def zero_segment_timeouts(self):
+        return abi.zero_segment_timeouts(self.h, _stream())
+
     def zero_enable_dynamic_loss_scale(self, init_scale=65536.0, growth_factor=2.0, backoff_factor=0.5,
                                        growth_interval=1000, min_scale=1.0):
         cfg = abi.zero_loss_scaler_t(init_scale, growth_factor, backoff_factor, growth_interval, min_scale)
