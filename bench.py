@@ -46,6 +46,10 @@ def parse():
     p.add_argument("--segment-consumer", default="copy", choices=["copy", "wait", "none"],
                    help="with --segments: per segment, wait and copy it out; only wait; or no consumer (the "
                         "tracking cost alone)")
+    p.add_argument("--offload", action="store_true",
+                   help="ZeRO-Offload: fp32 state in host memory, the step on the host cores, the gradient slice "
+                        "copied to the host and the 16-bit slice back to the device (pre-reduced gradients only)")
+    p.add_argument("--host-threads", type=int, default=0, help="with --offload: host worker threads (0: all)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1 << 26, help="elements of the oracle's timed sample")
     p.add_argument("--cpu-steps", type=int, default=7)
@@ -245,6 +249,183 @@ def traffic_from_profiles(cfg, rank, adam_launch_bytes):
     return int(kv["traffic_bytes_per_launch"])
 
 
+def host_probe_gbps(threads, nbytes=1 << 31):
+    """Measured host memory bandwidth with `threads` threads over nbytes buffers, best of
+    three each: a copy split over the threads (numpy's copy, i.e. the C library's memcpy;
+    bytes read + written), torch's read-only sum and torch's write-only fill.  The host has
+    no published per-VM figure, so the best of these stands for its peak."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+    torch.set_num_threads(threads)
+    src = np.ones(nbytes // 4, np.float32)
+    dst = np.empty_like(src)
+    edges = np.linspace(0, src.size, threads + 1).astype(np.int64)
+    parts = list(zip(edges[:-1], edges[1:]))
+    ts, td = torch.from_numpy(src), torch.from_numpy(dst)
+
+    def cp(b):
+        np.copyto(dst[b[0]:b[1]], src[b[0]:b[1]])
+
+    best = {"copy": 0.0, "read": 0.0, "write": 0.0}
+    with ThreadPoolExecutor(threads) as ex:
+        for _ in range(3):
+            t0 = time.perf_counter()
+            list(ex.map(cp, parts))
+            t1 = time.perf_counter()
+            float(ts.sum())
+            t2 = time.perf_counter()
+            td.fill_(2.0)
+            t3 = time.perf_counter()
+            best["copy"] = max(best["copy"], 2 * nbytes / (t1 - t0) / 1e9)
+            best["read"] = max(best["read"], nbytes / (t2 - t1) / 1e9)
+            best["write"] = max(best["write"], nbytes / (t3 - t2) / 1e9)
+    del src, dst, ts, td
+    return best
+
+
+def bench_offload(a, w, rank):
+    """The offloaded step: fetch (device to host, 2 B/param) -> host statistics ->
+    host Adam + 16-bit cast with the host-to-device copy of each finished block
+    (2 B/param), then the stream synchronised.  Inputs are resident (16-bit
+    parameters and gradients on the device, fp32 state on the host) before timing."""
+    import torch
+    import synth
+    from zero_partitioned_mixed_reduce_amd.offload import ZeroOffload
+
+    if w.grad_mode == "reduce":
+        print(json.dumps({"error": "--offload takes an already-reduced gradient (not the N_d-buffer reduce)"}),
+              flush=True)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    dt = w.dtype
+    starts = [0]
+    for n in w.numel:
+        starts.append(starts[-1] + n)
+    mstream = synth.stream_id(synth.MASTER)
+    gstream = synth.stream_id(synth.GRAD, 0, 0)
+
+    def filled16(n, first, sigma, stream):
+        t = torch.empty(n, dtype=torch.int16, device="cuda")
+        synth.gpu_normal_16(t, dt, w.seed, stream, first=first, sigma=sigma)
+        return t
+
+    t_setup = time.perf_counter()
+    if w.param_mode == "flat":
+        params = filled16(w.psi, 0, w.master_sigma, mstream)
+    else:
+        params = [filled16(n, starts[k], w.master_sigma, mstream) for k, n in enumerate(w.numel)]
+    if w.grad_mode == "flat":
+        grads = filled16(w.psi, 0, w.grad_sigma, gstream)
+    else:
+        grads = [filled16(n, starts[k], w.grad_sigma, gstream) for k, n in enumerate(w.numel)]
+    from zero_partitioned_mixed_reduce_amd import shard as shmod
+    import zero_partitioned_mixed_reduce_amd as zpm
+    info = zpm.zero_shard_plan(shmod.make_desc(w.numel, w.nd, rank, dt, params, grads))
+    b, valid = info.shard_begin, info.valid_elems
+    master = synth.normal_f32(valid, w.seed, mstream, b, w.master_sigma) if w.master_given else None
+    h = ZeroOffload(w.numel, w.nd, rank, dt, params=params, grads=grads, master_init=master,
+                    num_threads=a.host_threads)
+    del master
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    threads = a.host_threads if a.host_threads > 0 else os.cpu_count()
+    inv = 1.0 / w.loss_scale
+    sig_u = w.grad_sigma * inv
+    other = float(w.psi - valid) * sig_u * sig_u
+    hp = w.hp
+
+    def step(times=None):
+        t0 = time.perf_counter()
+        h.zero_offload_fetch_grads()
+        h.zero_offload_grad_stats(inv)
+        t1 = time.perf_counter()
+        h.zero_offload_adam_step(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], False, other,
+                                 w.max_norm, push=True)
+        t2 = time.perf_counter()
+        torch.cuda.current_stream().synchronize()
+        t3 = time.perf_counter()
+        if times is not None:
+            times["stats"] += t1 - t0
+            times["adam"] += t2 - t1
+            times["drain"] += t3 - t2
+
+    for _ in range(a.warmup):
+        step()
+    q = h.query()
+    assert not q["skipped"] and q["t"] == a.warmup, q
+    times = {"stats": 0.0, "adam": 0.0, "drain": 0.0}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step(times)
+    wall = time.perf_counter() - t0
+    q = h.query()
+    assert not q["skipped"] and q["t"] == a.warmup + a.steps, q
+    # device-to-host rate on its own: the fetch alone, timed with events on its stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    h.zero_offload_fetch_grads()
+    ev[1].record()
+    h.zero_offload_grad_stats(inv)
+    d2h_ms = ev[0].elapsed_time(ev[1])
+    h.zero_offload_adam_step(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], False, other,
+                             w.max_norm, push=False)
+    ev[0].record()
+    h.zero_offload_push_params()
+    ev[1].record()
+    torch.cuda.synchronize()
+    h2d_ms = ev[0].elapsed_time(ev[1])
+    h.close()
+    ms_step = wall * 1e3 / a.steps
+    stats_ms, adam_ms, drain_ms = (times[k] * 1e3 / a.steps for k in ("stats", "adam", "drain"))
+    probes = host_probe_gbps(threads)
+    host_peak = max(probes.values())
+    adam_bytes = 28 * valid
+    achieved = adam_bytes / (adam_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": valid / (ms_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name + "_offload", "psi": w.psi, "dp_size": w.nd, "dp_rank": rank,
+                   "shard_params": valid, "param_grad_dtype": DTYPE_NAME[dt], "grad_source": w.grad_mode,
+                   "tensors": len(w.numel), "loss_scale": w.loss_scale, "max_norm": w.max_norm,
+                   "offload": "fp32 master/m/v on the host; host step; gradient to host, 16-bit slice to device",
+                   "host_threads": threads, "adam": w.hp},
+        "breakdown_ms": {"fetch_and_host_stats": stats_ms, "host_adam_cast_and_push": adam_ms,
+                         "push_drain": drain_ms},
+        "pcie": {"d2h_gbps": 2 * valid / (d2h_ms * 1e-3) / 1e9, "h2d_gbps": 2 * valid / (h2d_ms * 1e-3) / 1e9,
+                 "d2h_ms": d2h_ms, "h2d_ms": h2d_ms, "bytes_each_way": 2 * valid,
+                 "peak_gbps": 64.0, "peak_source": "PCIe 5.0 x16, one direction"},
+        "roofline": {"kernel": "host Adam + 16-bit cast (AVX-512, all worker threads)", "bound": "host-dram",
+                     "achieved": achieved, "peak": host_peak, "unit": "GB/s", "frac": achieved / host_peak,
+                     "traffic": None, "algorithmic_bytes_per_launch": adam_bytes, "bytes_per_param": 28,
+                     "avg_launch_ms": adam_ms,
+                     "peak_source": f"measured on this host with {threads} threads over 2 GiB: the best of a "
+                                    "threaded memcpy, a read-only sum and a write-only fill (no published "
+                                    "per-VM figure)",
+                     "host_probes_gbps": probes},
+        "setup_s": setup_s,
+    }
+    if not a.no_cpu_baseline:
+        n = min(a.cpu_sample, valid)
+        rate, secs = cpu_baseline(w, n, a.cpu_steps)
+        out["cpu_baseline"] = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {n} elements of the shard's workload, {a.cpu_steps} steps "
+                                         f"(statistics, clip, Adam, cast), {secs:.1f} s single-threaded"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -257,6 +438,9 @@ def main():
 
     w = recipes.ALL[a.config]()
     rank = a.rank if a.rank is not None else w.ranks[0]
+    if a.offload:
+        bench_offload(a, w, rank)
+        return
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
     wl = Workload(w, rank, a.micro_steps, a.dynamic_loss_scale, a.segments, a.segment_consumer)

@@ -15,14 +15,21 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "zero_shard.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:zero_status_t|const char\*)\s+(zero_\w+)\s*\(", text, re.M)))
+    """Every function declared in include/*.h."""
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            names |= set(re.findall(r"^\s*(?:zero_status_t|const char\*)\s+(zero_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_step_calls():
     names = header_functions()
     for required in ("zero_shard_init", "zero_reduce_grads", "zero_check_overflow", "zero_grad_norm",
-                     "zero_adam_step", "zero_cast_params"):
+                     "zero_adam_step", "zero_cast_params", "zero_offload_init", "zero_offload_grad_stats",
+                     "zero_offload_adam_step"):
         assert required in names
 
 

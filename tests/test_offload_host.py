@@ -1,0 +1,268 @@
+"""The offloaded (host) optimizer step of the C ABI (include/zero_offload.h), on
+the CPU: host-only handles of every simulated rank stepped next to the oracle
+on the same seeded inputs, element by element.
+
+The exchange between ranks (OR of flags, the other ranks' sums of squares in
+rank order) is done here for both sides, each from its own local results.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import zero_partitioned_mixed_reduce_amd as zpm
+from zero_partitioned_mixed_reduce_amd import _abi
+from zero_partitioned_mixed_reduce_amd.offload import ZeroOffload
+from tests.gpu_harness import assert_16_close, assert_f32_close
+
+F16, BF16 = oracle.F16, oracle.BF16
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def sumsq_tol(n):
+    """Relative bound on the difference between two fp64 sums of the same n non-negative
+    terms added in different orders: each is within (n - 1) * 2^-53 of the exact sum."""
+    return max(2.0 * n * 2.0 ** -53, 1e-15)
+
+
+class HostSim:
+    """N_d host-only offload handles plus the oracle, stepped together."""
+
+    def __init__(self, numel, nd, dtype, seed, threads=(0,), master_given=True):
+        self.numel, self.nd, self.dtype = list(numel), nd, dtype
+        self.psi = sum(numel)
+        self.plans = [oracle.plan(numel, nd, r) for r in range(nd)]
+        self.p16_full = synth.normal_16(self.psi, dtype, seed, synth.stream_id(synth.MASTER), 0, 0.02)
+        self.master_full = synth.normal_f32(self.psi, seed, synth.stream_id(synth.MASTER), 0, 0.02)
+        self.ostates, self.handles = [], []
+        for r in range(nd):
+            _, _, b, valid = self.plans[r]
+            mst = self.master_full[b:b + valid] if master_given else None
+            self.ostates.append(oracle.RankState(dtype, self.p16_full[b:b + valid], mst))
+            self.handles.append(ZeroOffload(numel, nd, r, dtype, master_init=mst,
+                                            num_threads=threads[r % len(threads)],
+                                            param16_init=None if master_given else self.p16_full[b:b + valid]))
+        if master_given:
+            for r, h in enumerate(self.handles):
+                h.host16("param16")[:] = self.ostates[r].p16
+
+    def step(self, g_full, inv, max_norm, hp=HP, extra_found_inf=False):
+        hpo = oracle.HParams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
+        begins = [p[2] for p in self.plans]
+        res = oracle.step_ranks(self.ostates, [g_full], begins, inv, max_norm, hpo, extra_found_inf)
+        loc = []
+        for r, h in enumerate(self.handles):
+            _, _, b, valid = self.plans[r]
+            h.host16("grad16")[:] = g_full[b:b + valid]
+            loc.append(h.zero_offload_grad_stats(inv))
+        for r, h in enumerate(self.handles):
+            other_flag = any(loc[q][0] for q in range(self.nd) if q != r) or extra_found_inf
+            other_ss = 0.0
+            for q in range(self.nd):
+                if q != r:
+                    other_ss = other_ss + loc[q][1]
+            h.zero_offload_adam_step(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"],
+                                     other_ranks_found_inf=other_flag, other_ranks_sumsq=other_ss,
+                                     max_norm=max_norm, push=False)
+            q = h.query()
+            valid = self.plans[r][3]
+            assert loc[r][0] == res[r]["flag"], (r, loc[r], res[r])
+            if np.isfinite(res[r]["local_sumsq"]):
+                assert abs(loc[r][1] - res[r]["local_sumsq"]) <= sumsq_tol(valid) * max(res[r]["local_sumsq"], 1e-300)
+            if np.isfinite(res[r]["norm"]):
+                assert abs(q["norm"] - res[r]["norm"]) <= sumsq_tol(self.psi) * res[r]["norm"]
+            assert q["skipped"] == res[r]["skipped"]
+            if not q["skipped"]:
+                assert q["clip"] == res[r]["clip"], (r, q, res[r])
+            assert q["t"] == self.ostates[r].counters.t
+        return res
+
+    def compare(self, exact=True):
+        nonexact = 0
+        for r, (h, o) in enumerate(zip(self.handles, self.ostates)):
+            for name, exp in (("master", o.w), ("m", o.m), ("v", o.v)):
+                got = h.host(name)
+                nonexact += assert_f32_close(got, exp, f"rank {r} {name}")
+                if exact:
+                    assert (got.view(np.uint32) == exp.view(np.uint32)).all(), f"rank {r} {name} not bit-exact"
+            got16 = h.host16("param16")
+            nonexact += assert_16_close(got16, o.p16, f"rank {r} p16")
+            if exact:
+                assert (got16 == o.p16).all(), f"rank {r} p16 not bit-exact"
+        return nonexact
+
+    def close(self):
+        for h in self.handles:
+            h.close()
+
+
+def grads(psi, dtype, seed, step, sigma):
+    return synth.normal_16(psi, dtype, seed, synth.stream_id(synth.GRAD, 0, step), 0, sigma)
+
+
+CASES = [
+    # (numel, nd, dtype): flat, ragged with tails that are not multiples of 16 or of a tile,
+    # a shard boundary inside a tensor, a last rank with padding, an empty last rank
+    ([1 << 18], 4, F16),
+    ([1000, 37, 70001, 5, 16385], 3, BF16),
+    ([100003], 7, F16),
+    ([3 * 16384 + 17, 1], 2, BF16),
+    ([130], 64, F16),
+]
+
+
+@pytest.mark.parametrize("numel,nd,dtype", CASES)
+def test_offload_steps_match_oracle(numel, nd, dtype):
+    """5 steps, an inf injected into one rank's slice in step 2 (every rank skips)."""
+    seed = 0x5EED0100 + nd
+    sim = HostSim(numel, nd, dtype, seed, threads=(0, 3, 1))
+    scale = 1024.0 if dtype == F16 else 1.0
+    for step in range(1, 6):
+        g = grads(sim.psi, dtype, seed, step, 1e-3 * scale)
+        if step == 2:
+            g[sim.psi // 2] = 0x7C00 if dtype == F16 else 0x7F80
+        res = sim.step(g, 1.0 / scale, 1.0)
+        assert all(x["skipped"] for x in res) == (step == 2)
+        sim.compare()
+    assert all(o.counters.t == 4 for o in sim.ostates)
+    sim.close()
+
+
+def test_offload_clip_active_and_nan():
+    """Large gradients (clip < 1), then a NaN that only another rank sees."""
+    numel, nd, dtype, seed = [40000, 123], 3, BF16, 0x5EED0200
+    sim = HostSim(numel, nd, dtype, seed)
+    g = grads(sim.psi, dtype, seed, 1, 0.5)
+    res = sim.step(g, 1.0, 1.0)
+    assert all(x["clip"] < 1.0 for x in res)
+    sim.compare()
+    g = grads(sim.psi, dtype, seed, 2, 0.5)
+    b0, v0 = sim.plans[0][2], sim.plans[0][3]
+    g[b0 + v0 // 3] = 0x7FC1  # NaN inside rank 0's slice
+    before = [(h.host("master").copy(), h.host("m").copy(), h.host16("param16").copy()) for h in sim.handles]
+    res = sim.step(g, 1.0, 1.0)
+    assert all(x["skipped"] for x in res)
+    for h, (w, m, p) in zip(sim.handles, before):
+        assert (h.host("master").view(np.uint32) == w.view(np.uint32)).all()
+        assert (h.host("m").view(np.uint32) == m.view(np.uint32)).all()
+        assert (h.host16("param16") == p).all()
+    sim.compare()
+    sim.close()
+
+
+def test_offload_other_rank_flag_alone_skips():
+    numel, nd, dtype, seed = [5000], 2, F16, 0x5EED0300
+    sim = HostSim(numel, nd, dtype, seed)
+    res = sim.step(grads(sim.psi, dtype, seed, 1, 1e-3), 1.0, 1.0, extra_found_inf=True)
+    assert all(x["skipped"] for x in res)
+    assert all(h.query()["t"] == 0 for h in sim.handles)
+    sim.compare()
+    # leading skip: the next applied step is a fresh t = 1 step, moments were still exactly zero
+    sim.step(grads(sim.psi, dtype, seed, 2, 1e-3), 1.0, 1.0)
+    assert all(h.query()["t"] == 1 for h in sim.handles)
+    sim.compare()
+    sim.close()
+
+
+def test_offload_master_from_16bit_params():
+    """No master given: the master is the exact upcast of the 16-bit slice."""
+    numel, nd, dtype, seed = [7777, 3333], 2, BF16, 0x5EED0400
+    sim = HostSim(numel, nd, dtype, seed, master_given=False)
+    for r, h in enumerate(sim.handles):
+        assert (h.host("master").view(np.uint32) == sim.ostates[r].w.view(np.uint32)).all()
+        assert not h.host("m").any() and not h.host("v").any()
+    for step in (1, 2):
+        sim.step(grads(sim.psi, dtype, seed, step, 1e-3), 1.0, 1.0)
+        sim.compare()
+    sim.close()
+
+
+def test_offload_results_do_not_depend_on_thread_count():
+    n, dtype, seed = 3 * (1 << 14) * 5 + 77, F16, 0x5EED0500
+    master = synth.normal_f32(n, seed, synth.stream_id(synth.MASTER), 0, 0.02)
+    g = grads(n, dtype, seed, 1, 1e-3 * 1024)
+    outs = []
+    for th in (1, 2, 5, 8):
+        h = ZeroOffload([n], 1, 0, dtype, master_init=master, num_threads=th)
+        h.host16("grad16")[:] = g
+        flag, ss = h.zero_offload_grad_stats(1.0 / 1024)
+        h.zero_offload_adam_step(**HP, max_norm=1.0, push=False)
+        outs.append((flag, np.float64(ss).tobytes(), h.host("master").copy(), h.host16("param16").copy()))
+        h.close()
+    for o in outs[1:]:
+        assert o[0] == outs[0][0] and o[1] == outs[0][1]
+        assert (o[2].view(np.uint32) == outs[0][2].view(np.uint32)).all() and (o[3] == outs[0][3]).all()
+
+
+def _encode_patterns(dtype):
+    """Finite float32 values that exercise the 16-bit rounding: random bit patterns over
+    every exponent, and for each finite 16-bit value the two neighbours' midpoint and the
+    floats on either side of it (ties to even), plus the overflow thresholds."""
+    rng = np.random.default_rng(0x5EED0600 + dtype)
+    bits = rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    pats = [x[np.isfinite(x)]]
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.decode16(dtype, h)
+    fin = np.isfinite(vals)
+    lo = vals[fin].astype(np.float64)
+    lo = np.unique(lo)
+    mids = ((lo[:-1] + lo[1:]) / 2).astype(np.float32)  # exact: neighbours differ in the last 16-bit place
+    pats += [mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(-np.inf)),
+             lo.astype(np.float32)]
+    if dtype == F16:
+        pats.append(np.array([65504, 65519.996, 65520, -65520, 70000, 1e-8, 2 ** -25, 2 ** -24, 3 * 2 ** -26],
+                             np.float32))
+    else:
+        big = np.float32(np.ldexp(2.0 - 2.0 ** -8, 127))
+        pats.append(np.array([big, np.nextafter(big, np.float32(0)), -big, np.float32(3.4e38), 1e-40, -1e-45],
+                             np.float32))
+    return np.concatenate(pats).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_offload_16bit_write_back_matches_oracle_encoding(dtype):
+    """lr = wd = 0 and zero gradients leave every finite master unchanged, so the written
+    16-bit slice is the encoding of the master itself: compared with the oracle's encoder
+    (pinned exhaustively) on rounding ties, subnormals and overflow thresholds."""
+    w = _encode_patterns(dtype)
+    h = ZeroOffload([w.size], 1, 0, dtype, master_init=w, num_threads=0)
+    h.host16("grad16")[:] = 0
+    assert h.zero_offload_grad_stats(1.0) == (False, 0.0)
+    h.zero_offload_adam_step(0.0, 0.9, 0.999, 1e-8, 0.0, max_norm=1.0, push=False)
+    assert (h.host("master").view(np.uint32) == w.view(np.uint32)).all()
+    assert (h.host16("param16") == oracle.encode16(dtype, w)).all()
+    h.close()
+
+
+def test_offload_call_order_and_errors():
+    valid = oracle.plan([1000], 2, 1)[3]
+    h = ZeroOffload([1000], 2, 1, F16, master_init=np.zeros(valid, np.float32))
+    assert h.info.valid_elems == valid == 488
+    with pytest.raises(zpm.ZeroError) as e:
+        h.zero_offload_adam_step(**HP)
+    assert e.value.status == _abi.ZERO_ESTATE
+    with pytest.raises(zpm.ZeroError) as e:
+        h.zero_offload_fetch_grads()
+    assert e.value.status == _abi.ZERO_EINVAL and "host-only" in str(e.value)
+    with pytest.raises(zpm.ZeroError):
+        h.zero_offload_grad_stats(float("inf"))
+    with pytest.raises(zpm.ZeroError):
+        h.zero_offload_grad_stats(0.0)
+    h.host16("grad16")[:] = 0
+    h.zero_offload_grad_stats(1.0)
+    with pytest.raises(zpm.ZeroError) as e:
+        _abi.zero_offload_adam_step(h.h, _abi.zero_adam_hparams_t(**{"lr": 1e-3, "beta1": 0.9, "beta2": 0.999,
+                                                                     "eps": 1e-8, "weight_decay": 0.0}),
+                                    False, 0.0, 1.0, True, None)
+    assert e.value.status == _abi.ZERO_EINVAL and "push" in str(e.value)
+    h.zero_offload_adam_step(**HP, push=False)
+    with pytest.raises(zpm.ZeroError):
+        h.zero_offload_push_params()
+    assert h.query()["t"] == 1
+    h.close()
+    # bad buffers and capacities are rejected before anything is written
+    d = _abi.zero_shard_desc_t()
+    with pytest.raises(zpm.ZeroError):
+        _abi.zero_offload_init(d, _abi.zero_offload_bufs_t(), None, 0, None)
+    assert _abi.lib().zero_offload_destroy(None) == _abi.ZERO_EINVAL

@@ -41,6 +41,11 @@ class zero_loss_scaler_t(ctypes.Structure):
                 ("growth_interval", ctypes.c_int32), ("min_scale", ctypes.c_float)]
 
 
+class zero_offload_bufs_t(ctypes.Structure):
+    _fields_ = [("master", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("grad16", ctypes.c_void_p), ("param16", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
+
+
 class zero_adam_hparams_t(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
@@ -73,6 +78,18 @@ _PROTOS = {
                          ctypes.POINTER(ctypes.c_float), ctypes.c_void_p],
     "zero_export_state": [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p],
     "zero_shard_destroy": [ctypes.c_void_p],
+    # offloaded (host) step, include/zero_offload.h
+    "zero_offload_init": [ctypes.POINTER(zero_shard_desc_t), ctypes.POINTER(zero_offload_bufs_t), ctypes.c_void_p,
+                          ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)],
+    "zero_offload_fetch_grads": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
+    "zero_offload_grad_stats": [ctypes.c_void_p, ctypes.c_float, ctypes.POINTER(ctypes.c_int32),
+                                ctypes.POINTER(ctypes.c_double)],
+    "zero_offload_adam_step": [ctypes.c_void_p, ctypes.POINTER(zero_adam_hparams_t), ctypes.c_int32, ctypes.c_double,
+                               ctypes.c_float, ctypes.c_int32, ctypes.c_void_p],
+    "zero_offload_push_params": [ctypes.c_void_p, ctypes.c_void_p],
+    "zero_offload_query": [ctypes.c_void_p, c_i64p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
+                           ctypes.POINTER(ctypes.c_float)],
+    "zero_offload_destroy": [ctypes.c_void_p],
 }
 
 _lib = None
@@ -222,6 +239,42 @@ def zero_export_state(h, which, dst_ptr, stream):
 
 def zero_shard_destroy(h):
     _call("zero_shard_destroy", h)
+
+
+def zero_offload_init(desc, bufs, master_init_ptr, num_threads, stream):
+    h = ctypes.c_void_p()
+    _call("zero_offload_init", ctypes.byref(desc), ctypes.byref(bufs), master_init_ptr, num_threads, stream,
+          ctypes.byref(h))
+    return h
+
+
+def zero_offload_fetch_grads(h, flat_grad16_ptr, stream):
+    _call("zero_offload_fetch_grads", h, flat_grad16_ptr, stream)
+
+
+def zero_offload_grad_stats(h, inv_loss_scale):
+    f, s = ctypes.c_int32(), ctypes.c_double()
+    _call("zero_offload_grad_stats", h, inv_loss_scale, ctypes.byref(f), ctypes.byref(s))
+    return bool(f.value), s.value
+
+
+def zero_offload_adam_step(h, hp, other_ranks_found_inf, other_ranks_sumsq, max_norm, push, stream):
+    _call("zero_offload_adam_step", h, ctypes.byref(hp), int(bool(other_ranks_found_inf)), other_ranks_sumsq,
+          max_norm, int(bool(push)), stream)
+
+
+def zero_offload_push_params(h, stream):
+    _call("zero_offload_push_params", h, stream)
+
+
+def zero_offload_query(h):
+    t, sk, nrm, clip = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_double(), ctypes.c_float()
+    _call("zero_offload_query", h, ctypes.byref(t), ctypes.byref(sk), ctypes.byref(nrm), ctypes.byref(clip))
+    return dict(t=t.value, skipped=bool(sk.value), norm=nrm.value, clip=clip.value)
+
+
+def zero_offload_destroy(h):
+    _call("zero_offload_destroy", h)
 
 
 def zero_last_error():

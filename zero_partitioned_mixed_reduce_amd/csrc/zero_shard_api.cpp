@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "zero_shard.h"
+#include "zs_host.h"
 #include "zs_internal.h"
 
 namespace zs {
@@ -64,6 +65,8 @@ enum Phase { kReady, kReduced, kChecked, kNormed, kStepped };
 enum { kGradFlat16 = 0, kGradChunk16 = 1, kGradRed = 2 };
 
 }  // namespace
+
+zero_status_t zs::set_error(zero_status_t s, const std::string& msg) { return fail(s, msg); }
 
 struct zero_shard {
   zero_shard_info_t info;

@@ -15,7 +15,7 @@ def _stream():
 
 
 def make_desc(numel, dp_size, dp_rank, dtype, params, grads=None, align=0):
-    """params / grads: one flat tensor, or a list of per-tensor tensors (or None)."""
+    """params / grads: one flat tensor, or a list of per-tensor tensors (or None: no device pointers)."""
     numel = [int(n) for n in numel]
     keep = {}
     d = abi.zero_shard_desc_t()
@@ -32,7 +32,7 @@ def make_desc(numel, dp_size, dp_rank, dtype, params, grads=None, align=0):
     if isinstance(params, (list, tuple)):
         keep["p"] = ptrs(params)
         d.param16 = ctypes.cast(keep["p"], ctypes.POINTER(ctypes.c_void_p))
-    else:
+    elif params is not None:
         d.flat_param16 = params.data_ptr()
     if grads is not None:
         if isinstance(grads, (list, tuple)):
