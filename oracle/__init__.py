@@ -59,6 +59,8 @@ def lib():
         L.orc_grad_stats.restype = ctypes.c_int
         L.orc_accumulate.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
                                      ctypes.c_void_p, ctypes.c_int]
+        L.orc_reduce_to16.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
+                                      ctypes.c_void_p]
         L.orc_stats_f32.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
                                     ctypes.POINTER(ctypes.c_double)]
         L.orc_stats_f32.restype = ctypes.c_int
@@ -153,6 +155,25 @@ def grad_stats(dtype, srcs, inv_loss_scale, sumsq_acc=0.0):
     return u, bool(flag), acc.value
 
 
+def reduce_to16(dtype, srcs):
+    """16-bit output of the local reduce: RNE16 of the rank-order fp32 sum of srcs."""
+    srcs = [_u16(np.ascontiguousarray(x)) for x in srcs]
+    n = srcs[0].size
+    assert all(x.size == n for x in srcs)
+    arr = (ctypes.c_void_p * len(srcs))(*[x.ctypes.data for x in srcs])
+    out = np.empty(n, np.uint16)
+    lib().orc_reduce_to16(dtype, arr, len(srcs), n, _ptr(out))
+    return out
+
+
+def _intake_sources(dtype, srcs, reduce_out16):
+    """The sources as the step takes them in: with a 16-bit reduce output, N_d >= 2
+    rank buffers become the one 16-bit reduce-scatter result."""
+    if reduce_out16 and len(srcs) >= 2:
+        return [reduce_to16(dtype, srcs)]
+    return srcs
+
+
 def accumulate(dtype, srcs, acc, first):
     """acc (float32, in place) = s or acc + s, with s the rank-order fp32 sum of srcs."""
     srcs = [_u16(np.ascontiguousarray(x)) for x in srcs]
@@ -241,23 +262,27 @@ class RankState:
         self.counters = Counters.fresh()
 
 
-def step_ranks_accumulated(states, micro_grads, begins, inv_loss_scale, max_norm, hp, extra_found_inf=False):
+def step_ranks_accumulated(states, micro_grads, begins, inv_loss_scale, max_norm, hp, extra_found_inf=False,
+                           reduce_out16=False):
     """One optimizer step over K micro-steps: micro_grads[k] is the list of flat
     uint16 buffers of micro-step k (one already-reduced buffer, or one per rank).
     Each rank accumulates its slice over the micro-steps in fp32, then the step
-    proceeds as in step_ranks on the accumulated gradient."""
+    proceeds as in step_ranks on the accumulated gradient.  reduce_out16: each
+    micro-step's reduce delivers its sum in 16 bits, which is what gets accumulated."""
     nd = len(states)
     locs = []
     for r, st in enumerate(states):
         n, b = st.w.size, begins[r]
         acc = np.zeros(n, np.float32)
         for k, grads in enumerate(micro_grads):
-            accumulate(st.dtype, [g[b:b + n] for g in grads], acc, first=(k == 0))
+            srcs = _intake_sources(st.dtype, [g[b:b + n] for g in grads], reduce_out16)
+            accumulate(st.dtype, srcs, acc, first=(k == 0))
         locs.append(stats_f32(acc, inv_loss_scale))
     return _finish_step(states, locs, nd, max_norm, hp, extra_found_inf)
 
 
-def step_ranks(states, rank_grads, begins, inv_loss_scale, max_norm, hp, extra_found_inf=False):
+def step_ranks(states, rank_grads, begins, inv_loss_scale, max_norm, hp, extra_found_inf=False,
+               reduce_out16=False):
     """One optimizer step of every simulated rank.
 
     states[r] holds rank r's shard (valid elements from begins[r]).  rank_grads
@@ -265,13 +290,16 @@ def step_ranks(states, rank_grads, begins, inv_loss_scale, max_norm, hp, extra_f
     rank to be summed.  Each rank computes its local flag and sum of squares;
     the exchange gives rank r the OR of the other ranks' flags and the sum of
     the other ranks' sums of squares in rank order; global = local + others.
+    reduce_out16: the reduce of N_d >= 2 buffers delivers its sum in 16 bits
+    (reduce_to16), which the step then takes in.
     Returns a list of per-rank dicts (flag, local_sumsq, norm, clip, skipped)."""
     nd = len(states)
     locs = []
     for r, st in enumerate(states):
         n = st.w.size
         b = begins[r]
-        u, flag, ss = grad_stats(st.dtype, [g[b:b + n] for g in rank_grads], inv_loss_scale)
+        srcs = _intake_sources(st.dtype, [g[b:b + n] for g in rank_grads], reduce_out16)
+        u, flag, ss = grad_stats(st.dtype, srcs, inv_loss_scale)
         locs.append((u, flag, ss))
     return _finish_step(states, locs, nd, max_norm, hp, extra_found_inf)
 

@@ -151,6 +151,20 @@ int orc_grad_stats(int dtype, const uint16_t* const* src, int n_src, int64_t n, 
   return flag;
 }
 
+/* 16-bit output of the local reduce.  "DeepSpeed ZeRO", ZeRO Stage 2 基本思想: the
+ * rank's fp32 gradient shard is taken from the reduce-scatter's bf16 result.  The
+ * reduction is the rank-order fp32 sum of orc_grad_stats; its result is delivered in
+ * the 16-bit type, rounded once to nearest even:
+ *   out16[i] = RNE16(g_0[i] + g_1[i] + ... + g_{n_src-1}[i]).
+ * The step then takes this 16-bit slice in as an already-reduced gradient. */
+void orc_reduce_to16(int dtype, const uint16_t* const* src, int n_src, int64_t n, uint16_t* out16) {
+  for (int64_t i = 0; i < n; ++i) {
+    float s = dec16(dtype, src[0][i]);
+    for (int q = 1; q < n_src; ++q) s = s + dec16(dtype, src[q][i]);
+    out16[i] = enc16(dtype, s);
+  }
+}
+
 /* Gradient accumulation over micro-steps ("DeepSpeed ZeRO", ZeRO Stage 2: with
  * gradient accumulation every backward reduce-scatters and the rank adds its
  * 1/N_d slice to what it has accumulated).  s = g_0 + g_1 + ... in fp32 rank

@@ -691,3 +691,96 @@ def test_loss_scale_closed_forms():
     ls.update(True)
     assert ls.scale.value == 32.0 and ls.good.value == 0
     assert oracle.LossScaler(init_scale=1000.0).inv == np.float32(1) / np.float32(1000)
+
+
+# --------------------------------------------------------------------------
+# 16-bit output of the local reduce ("DeepSpeed ZeRO", ZeRO Stage 2 基本思想: the fp32
+# gradient shard comes from the bf16 reduce-scatter result)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_reduce16_is_the_rounded_fp32_sum(dtype):
+    """Against library routines: the rank-order sum in numpy float32, then torch's
+    round-to-nearest-even conversion of each sum to the 16-bit type."""
+    nd, n = 8, 20_000
+    bufs = [rand16(dtype, n, 1.0, 900 + q) for q in range(nd)]
+    s = oracle.decode16(dtype, bufs[0]).astype(np.float32)
+    for q in range(1, nd):
+        s = (s + oracle.decode16(dtype, bufs[q])).astype(np.float32)
+    tdt = torch.float16 if dtype == F16 else torch.bfloat16
+    exp = torch.from_numpy(s).to(tdt).view(torch.int16).numpy().view(np.uint16)
+    assert (oracle.reduce_to16(dtype, bufs) == exp).all()
+
+
+def test_reduce16_rounds_once_at_the_end():
+    # bf16 has 7 fraction bits: 1 + 2^-8 is a tie that rounds to 1.  Rounded once,
+    # 1 + 2^-8 + 2^-8 = 1 + 2^-7 is kept; rounding after each addition would give 1.
+    one = oracle.encode16(BF16, np.array([1.0], np.float32))
+    e = oracle.encode16(BF16, np.array([2.0 ** -8], np.float32))
+    assert oracle.decode16(BF16, oracle.reduce_to16(BF16, [one, e, e]))[0] == np.float32(1 + 2.0 ** -7)
+    assert oracle.decode16(BF16, oracle.reduce_to16(BF16, [one, e]))[0] == np.float32(1.0)
+    # ties go to even: 1 + 2^-7 + 2^-8 -> 1 + 2^-6
+    o7 = oracle.encode16(BF16, np.array([1 + 2.0 ** -7], np.float32))
+    assert oracle.decode16(BF16, oracle.reduce_to16(BF16, [o7, e]))[0] == np.float32(1 + 2.0 ** -6)
+
+
+def test_reduce16_exact_grid_and_single_source():
+    nd, n = 8, 4000
+    ks = rng.integers(-64, 65, size=(nd, n))
+    bufs = [oracle.encode16(F16, (k * 2.0 ** -6).astype(np.float32)) for k in ks]
+    # |sum| <= 512 on a 2^-6 grid needs at most 16 significant bits -- not exact in fp16 (11),
+    # so compare with integer arithmetic rounded by torch; sums below 32 in magnitude are exact
+    out = oracle.decode16(F16, oracle.reduce_to16(F16, bufs)).astype(np.float64)
+    tot = ks.sum(0) * 2.0 ** -6
+    small = np.abs(tot) < 32
+    assert (out[small] == tot[small]).all()
+    assert (out == torch.tensor(tot, dtype=torch.float64).to(torch.float16).double().numpy()).all()
+    one = rand16(BF16, n, 1.0, 77)
+    assert (oracle.reduce_to16(BF16, [one]) == one).all()
+
+
+def test_reduce16_fp16_overflow_skips():
+    """Eight ranks of 10000 sum to 80000 > 65504: the fp16 reduce output is +inf, so the
+    step is skipped; with the fp32 reduce output the same buffers are finite."""
+    big = oracle.encode16(F16, np.array([10000.0], np.float32))
+    bufs = [np.repeat(big, 64) for _ in range(8)]
+    assert not oracle.grad_stats(F16, bufs, 1.0 / 65536)[1]
+    red = oracle.reduce_to16(F16, bufs)
+    assert (red == 0x7C00).all() and oracle.grad_stats(F16, [red], 1.0 / 65536)[1]
+    states, begins, _, _ = make_states(F16, 2, [64], 31)
+    before = snapshot(states)
+    res = oracle.step_ranks(states, bufs, begins, 1.0 / 65536, 1.0, hp_of(), reduce_out16=True)
+    assert all(r["skipped"] for r in res)
+    assert all((a[0].view(np.uint32) == b[0].view(np.uint32)).all() for a, b in zip(before, snapshot(states)))
+
+
+@pytest.mark.parametrize("nd", [2, 3, 7])
+def test_partition_invariance_reduce16(nd):
+    dtype, psi, steps = BF16, 9001, 3
+    hp = hp_of()
+    states, begins, p16_full, master = make_states(dtype, nd, [psi], 41)
+    whole = oracle.RankState(dtype, p16_full, master)
+    for s in range(steps):
+        grads = [rand16(dtype, psi, 0.3, 700 + 10 * s + q) for q in range(nd)]
+        res = oracle.step_ranks(states, grads, begins, 1.0, 1.0, hp, reduce_out16=True)
+        u, flag, _ = oracle.grad_stats(dtype, [oracle.reduce_to16(dtype, grads)], 1.0)
+        oracle.adam(flag, u, res[0]["clip"], hp, whole.counters, whole.w, whole.m, whole.v)
+        oracle.cast(dtype, whole.w, whole.p16)
+    for name in ("w", "m", "v", "p16"):
+        cat = np.concatenate([getattr(st, name) for st in states])
+        assert (cat.view(np.uint8) == getattr(whole, name).view(np.uint8)).all(), name
+
+
+def test_accumulation_of_16bit_reduce_outputs():
+    # each micro-step's reduce result is rounded to 16 bits, then added in fp32:
+    # micro-step sums 1 + 2^-8 + 2^-8 (kept as 1 + 2^-7) twice accumulate to 2 + 2^-6
+    one = oracle.encode16(BF16, np.array([1.0], np.float32))
+    e = oracle.encode16(BF16, np.array([2.0 ** -8], np.float32))
+    states, begins, _, _ = make_states(BF16, 1, [1], 5)
+    micro = [[one, e, e], [one, e, e]]
+    acc = np.zeros(1, np.float32)
+    for k, srcs in enumerate(micro):
+        oracle.accumulate(BF16, [oracle.reduce_to16(BF16, srcs)], acc, first=(k == 0))
+    assert acc[0] == np.float32(2 + 2.0 ** -6)
+    res = oracle.step_ranks_accumulated(states, micro, begins, 1.0, 0.0, hp_of(), reduce_out16=True)
+    assert not res[0]["skipped"] and res[0]["local_sumsq"] == (2 + 2.0 ** -6) ** 2
