@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--dynamic-loss-scale", action="store_true",
                    help="device-resident dynamic loss scale starting at the workload's loss scale (growth 2, "
                         "backoff 0.5, interval 1000, floor 1)")
+    p.add_argument("--reduce-output16", action="store_true",
+                   help="the local reduce delivers its sum rounded to the 16-bit dtype (the reduce-scatter's "
+                        "16-bit result), which the step then takes in")
     p.add_argument("--segments", type=int, default=0,
                    help="track the write-back in this many segments; a second stream waits for each segment and "
                         "copies it out (a stand-in for the segment's all-gather)")
@@ -74,7 +77,8 @@ def kernel_source_sha():
 class Workload:
     """Device-resident inputs and the library handle for one rank."""
 
-    def __init__(self, w, rank, micro_steps=1, dynamic_loss_scale=False, segments=0, consumer="copy"):
+    def __init__(self, w, rank, micro_steps=1, dynamic_loss_scale=False, segments=0, consumer="copy",
+                 reduce_out16=False):
         import torch
         import synth
         from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
@@ -125,6 +129,8 @@ class Workload:
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         self.info = self.shard.info
+        if reduce_out16 and w.grad_mode == "reduce":
+            self.shard.zero_set_reduce_output(True)
         self.inv = 1.0 / w.loss_scale
         self.intake_inv = self.inv
         if dynamic_loss_scale:
@@ -180,15 +186,18 @@ class Workload:
                 ev[4].record(self.consumer)
 
 
-def bytes_per_param(w, micro_steps=1):
+def bytes_per_param(w, micro_steps=1, reduce_out16=False):
     """Dependency-minimal HBM bytes per shard parameter for the whole step, and for the Adam pass.
 
     One micro-step reads its sources (2 B per rank buffer, or 2 B of already-reduced
     gradient); the first accumulation writes the fp32 accumulator (4 B), later ones
     read and write it (8 B); the step's intake on top of an accumulation reads it and
-    writes u (8 B); the Adam pass then reads u (4 B) instead of the 16-bit gradient."""
+    writes u (8 B); the Adam pass then reads u (4 B) instead of the 16-bit gradient.
+    With a 16-bit reduce output the reduce writes, and the Adam pass reads, 2 B."""
     src = 2 * w.nd if w.grad_mode == "reduce" else 2
     if micro_steps <= 1:
+        if w.grad_mode == "reduce" and reduce_out16:
+            return src + 2 + 2 + 26, 2 + 12 + 12 + 2      # write the 16-bit result; Adam reads it
         if w.grad_mode == "reduce":
             return src + 4 + 4 + 26, 4 + 12 + 12 + 2      # write fp32 u; Adam reads u
         return src + 2 + 12 + 12 + 2, 2 + 12 + 12 + 2    # statistics pass, then Adam re-reads the gradient
@@ -443,10 +452,10 @@ def main():
         return
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
-    wl = Workload(w, rank, a.micro_steps, a.dynamic_loss_scale, a.segments, a.segment_consumer)
+    wl = Workload(w, rank, a.micro_steps, a.dynamic_loss_scale, a.segments, a.segment_consumer, a.reduce_output16)
     setup_s = time.perf_counter() - t_setup
     valid = wl.info.valid_elems
-    step_b, adam_b = bytes_per_param(w, a.micro_steps)
+    step_b, adam_b = bytes_per_param(w, a.micro_steps, a.reduce_output16)
 
     if a.copy_calibration:
         # a plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB), used to scale
@@ -497,6 +506,7 @@ def main():
                    "tensors": len(w.numel), "loss_scale": w.loss_scale, "max_norm": w.max_norm,
                    "loss_scale_mode": "dynamic, device-resident" if a.dynamic_loss_scale else "static",
                    "micro_steps": a.micro_steps,
+                   "reduce_output": "16-bit" if a.reduce_output16 and w.grad_mode == "reduce" else "fp32",
                    "adam": w.hp},
         "hbm_gbps_step": step_b * valid / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": step_b * valid / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

@@ -201,6 +201,22 @@ zero_status_t zero_loss_scale(zero_shard_t h, float* host_scale, int32_t* host_g
  * bad sources or without bufs.red. */
 zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks, void* stream);
 
+/* 16-bit output of the local reduce ("DeepSpeed ZeRO", ZeRO Stage 2 基本思想:
+ * the rank's fp32 gradient shard is taken from the reduce-scatter's bf16
+ * result).  With out_16bit = 1, the rank-order fp32 sum of N_d >= 2 rank
+ * buffers (zero_reduce_grads, zero_accumulate_grads) is delivered rounded once,
+ * to nearest even, in the handle's 16-bit dtype, and the step takes that
+ * value in: without accumulation the 16-bit result is stored in bufs.red
+ * (2 bytes per element of the state layout) and the unscale, flag, sum of
+ * squares and Adam read it (for fp16 a sum beyond 65504 becomes inf and skips
+ * the step); with accumulation each micro-step's rounded result is added to
+ * the fp32 accumulator.  Sources of one already-reduced buffer are 16-bit
+ * already and are taken in unchanged.  out_16bit = 0 (the default) keeps the
+ * fp32 sum.  Between steps only (ESTATE otherwise, also while micro-steps are
+ * accumulated); EINVAL unless out_16bit is 0 or 1, or for 1 without bufs.red.
+ * After a 16-bit intake, zero_export_state of red (3) returns ESTATE. */
+zero_status_t zero_set_reduce_output(zero_shard_t h, int32_t out_16bit);
+
 /* n_ranks value for zero_reduce_grads: no new gradient, use the accumulated one. */
 #define ZERO_ACCUMULATED (-1)
 
@@ -215,7 +231,9 @@ zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grad
  *                 this rank's slice is summed in fp32 in rank order
  *                 g_0 + g_1 + ... + g_{N_d-1} (the local half of the
  *                 reduce-scatter, "DeepSpeed ZeRO" ZeRO Stage 2) and the
- *                 unscaled sum is kept in bufs.red.  N_d <= 64.
+ *                 unscaled sum is kept in bufs.red (or, after
+ *                 zero_set_reduce_output(h, 1), the sum rounded to 16 bits).
+ *                 N_d <= 64.
  *   after zero_accumulate_grads: the sources above (or none, n_ranks =
  *                 ZERO_ACCUMULATED) are added to the accumulated gradient in
  *                 bufs.red first: acc + s.

@@ -141,6 +141,15 @@ class Sim:
             if segments:
                 self.shards[r].zero_set_segments(segments)
 
+    reduce_out16 = False
+
+    def set_reduce_out16(self, on=True):
+        """The local reduce delivers its sum in the 16-bit dtype on every simulated rank
+        (and in the oracle)."""
+        self.reduce_out16 = on
+        for s in self.shards.values():
+            s.zero_set_reduce_output(on)
+
     def enable_dynamic(self, init_scale, growth, backoff, interval, min_scale):
         """Device-resident dynamic loss scale on every simulated rank, mirrored by
         an oracle LossScaler; each step then unscales by the current scale."""
@@ -191,7 +200,8 @@ class Sim:
         every micro-step is accumulated and the intake uses ZERO_ACCUMULATED."""
         from zero_partitioned_mixed_reduce_amd._abi import ZERO_ACCUMULATED
         inv, dev_inv = self._intake_inv(inv)
-        res = oracle.step_ranks_accumulated(self.ostates, micro, self.begins, inv, max_norm, hp)
+        res = oracle.step_ranks_accumulated(self.ostates, micro, self.begins, inv, max_norm, hp,
+                                            reduce_out16=self.reduce_out16)
         loc = {}
         for k, grads in enumerate(micro):
             last = k == len(micro) - 1
@@ -214,7 +224,8 @@ class Sim:
     def step(self, grads, inv, max_norm, hp, fuse=True, extra_found_inf=False):
         """grads: list of flat uint16 arrays (N_d for 'reduce', else one)."""
         inv, dev_inv = self._intake_inv(inv)
-        res = oracle.step_ranks(self.ostates, grads, self.begins, inv, max_norm, hp, extra_found_inf)
+        res = oracle.step_ranks(self.ostates, grads, self.begins, inv, max_norm, hp, extra_found_inf,
+                                reduce_out16=self.reduce_out16)
         dg = self._device_grads(grads)
         # every simulated rank's own flag and sum (others from the oracle when not simulated on the GPU)
         loc = {}

@@ -15,6 +15,9 @@ def test_bytes_per_param():
     assert bench.bytes_per_param(recipes.zero1_7p5b()) == (30, 28)
     assert bench.bytes_per_param(recipes.reduce8()) == (50, 30)       # 2*8 + 4 + 4 + 26
     assert bench.bytes_per_param(recipes.tiny()) == (42, 30)
+    # 16-bit reduce output: the reduce writes 2 B and the Adam pass reads 2 B
+    assert bench.bytes_per_param(recipes.reduce8(), 1, True) == (16 + 2 + 2 + 26, 28)
+    assert bench.bytes_per_param(recipes.full7p5b(), 1, True) == (30, 28)
     # micro-steps: first accumulation writes the accumulator, later ones read and write it
     assert bench.bytes_per_param(recipes.reduce8(), 2) == ((16 + 4) + (16 + 8) + 30, 30)
     assert bench.bytes_per_param(recipes.reduce8(), 4) == ((16 + 4) + 2 * (16 + 8) + (16 + 8) + 30, 30)

@@ -38,9 +38,11 @@ def host_grad(w, q, idx_or_range):
     return synth.gather_16(idx_or_range, w.dtype, w.seed, stream, w.grad_sigma, zs, zm)
 
 
-def oracle_u(w, srcs, inv, micro_steps):
+def oracle_u(w, srcs, inv, micro_steps, r16=False):
     """The oracle's unscaled gradient for one run of elements: the benchmark feeds the
-    same sources to every micro-step."""
+    same sources to every micro-step.  r16: the reduce delivers its sum in 16 bits."""
+    if r16 and len(srcs) >= 2:
+        srcs = [oracle.reduce_to16(w.dtype, srcs)]
     if micro_steps <= 1:
         return oracle.grad_stats(w.dtype, srcs, inv)
     acc = np.zeros(srcs[0].size, np.float32)
@@ -49,7 +51,7 @@ def oracle_u(w, srcs, inv, micro_steps):
     return oracle.stats_f32(acc, inv)
 
 
-def oracle_local_sumsq(w, b, valid, inv, micro_steps=1):
+def oracle_local_sumsq(w, b, valid, inv, micro_steps=1, r16=False):
     nsrc = w.nd if w.grad_mode == "reduce" else 1
     step = 1 << 24
     blocks = [(lo, min(step, valid - lo)) for lo in range(0, valid, step)]
@@ -57,7 +59,7 @@ def oracle_local_sumsq(w, b, valid, inv, micro_steps=1):
     def part(blk):
         lo, n = blk
         srcs = [host_grad(w, q, (b + lo, n)) for q in range(nsrc)]
-        _, flag, ss = oracle_u(w, srcs, inv, micro_steps)
+        _, flag, ss = oracle_u(w, srcs, inv, micro_steps, r16)
         return flag, ss
 
     synth.set_host_threads(1)          # the pool below already uses every core
@@ -111,14 +113,15 @@ def gpu_params_at(wl, flat_idx):
     return out
 
 
-@pytest.mark.parametrize("cfg,rank,micro", [("zero1_7p5b", 0, 1), ("zero1_7p5b", 63, 1), ("gpt2", 7, 1), ("gpt2", 3, 1),
-                                            ("reduce8", 7, 1), ("reduce8", 0, 1), ("full7p5b", 0, 1),
-                                            ("reduce8", 7, 3), ("zero1_7p5b", 0, 2)])
-def test_full_size_sampled(cfg, rank, micro):
+@pytest.mark.parametrize("cfg,rank,micro,r16", [
+    ("zero1_7p5b", 0, 1, False), ("zero1_7p5b", 63, 1, False), ("gpt2", 7, 1, False), ("gpt2", 3, 1, False),
+    ("reduce8", 7, 1, False), ("reduce8", 0, 1, False), ("full7p5b", 0, 1, False),
+    ("reduce8", 7, 3, False), ("zero1_7p5b", 0, 2, False), ("reduce8", 7, 1, True), ("reduce8", 0, 2, True)])
+def test_full_size_sampled(cfg, rank, micro, r16):
     import bench
     w = recipes.ALL[cfg]()
-    print(f"\n[fullsize] {cfg} rank {rank} micro-steps {micro}: setting up", flush=True)
-    wl = bench.Workload(w, rank, micro)
+    print(f"\n[fullsize] {cfg} rank {rank} micro-steps {micro} 16-bit reduce output {r16}: setting up", flush=True)
+    wl = bench.Workload(w, rank, micro, reduce_out16=r16)
     info = wl.info
     b, valid = info.shard_begin, info.valid_elems
     pieces = wl.shard.pieces()
@@ -129,7 +132,7 @@ def test_full_size_sampled(cfg, rank, micro):
     assert q["t"] == 2 and not q["skipped"]
 
     print(f"[fullsize] {cfg}: oracle sum of squares over {valid} elements", flush=True)
-    flag, local = oracle_local_sumsq(w, b, valid, wl.inv, micro)
+    flag, local = oracle_local_sumsq(w, b, valid, wl.inv, micro, r16)
     assert not flag
     clip, norm = oracle.clip_coef(local + wl.other_sumsq, w.max_norm)
     assert q["clip"] == clip, (q, clip)
@@ -139,7 +142,7 @@ def test_full_size_sampled(cfg, rank, micro):
     pos = sample_positions(info, pieces, rng)
     flat = b + pos
     nsrc = w.nd if w.grad_mode == "reduce" else 1
-    u, _, _ = oracle_u(w, [host_grad(w, qq, flat) for qq in range(nsrc)], wl.inv, micro)
+    u, _, _ = oracle_u(w, [host_grad(w, qq, flat) for qq in range(nsrc)], wl.inv, micro, r16)
     mstream = synth.stream_id(synth.MASTER)
     if w.master_given:
         wv = synth.gather_f32(flat, w.seed, mstream, w.master_sigma)

@@ -528,3 +528,123 @@ def test_segment_api_errors():
         s.zero_wait_segment(k)
     torch.cuda.synchronize()
     assert s.zero_segment_timeouts() == 0
+
+
+# --------------------------------------------------------------------------
+# 16-bit output of the local reduce ("DeepSpeed ZeRO", ZeRO Stage 2 基本思想: the fp32
+# gradient shard comes from the reduce-scatter's bf16 result)
+
+
+@pytest.mark.parametrize("bad,at_step", [(np.inf, 2), (np.nan, 1)])
+def test_reduce16_tiny_all_ranks(bad, at_step):
+    """The tiny workload with the 16-bit reduce output: fp16, loss scale 1024, 5 steps."""
+    w = recipes.tiny()
+    psi = w.psi
+    master, p16 = master_of(w, psi)
+    sim = Sim(w.numel, w.nd, w.dtype, p16, master, "reduce")
+    sim.p16_initial = p16.copy()
+    sim.set_reduce_out16()
+    hp = hp_of(w.hp)
+    S = sim.plans[0][1]
+    for step in range(1, w.steps + 1):
+        g = grads_for(w, step, psi, w.nd)
+        if step == at_step:
+            g[2][1 * S + 4321] = oracle.encode16(F16, np.array([bad], np.float32))[0]
+        res = sim.step(g, 1.0 / w.loss_scale, w.max_norm, hp)
+        assert all(x["skipped"] == (step == at_step) for x in res)
+        sim.compare()
+
+
+@pytest.mark.parametrize("nd,dtype,per_tensor", [(2, BF16, False), (3, F16, True), (8, BF16, False),
+                                                 (11, F16, False)])
+def test_reduce16_fan_in_and_layouts(nd, dtype, per_tensor):
+    """Specialised (2, 8) and generic (3, 11) fan-ins; per-tensor parameters at odd
+    offsets make the 16-bit result's alignment differ from the flat rank buffers'."""
+    w = recipes.reduce8()
+    numel = [40_000 * nd + 13] if not per_tensor else [5000, 1, 8193, 64, 12345, 3]
+    psi = sum(numel)
+    master, p16 = master_of(w, psi)
+    sim = Sim(numel, nd, dtype, p16, master, "reduce", per_tensor_params=per_tensor, param_misalign=(1, 3, 2),
+              ranks=None if nd <= 3 else [0, nd - 1])
+    sim.p16_initial = p16.copy()
+    sim.set_reduce_out16()
+    for step in range(1, 3):
+        g = [synth.normal_16(psi, dtype, w.seed, synth.stream_id(synth.GRAD, q, step), 0, 0.5) for q in range(nd)]
+        sim.step(g, 1.0, 1.0, hp_of(w.hp))
+        sim.compare()
+
+
+def test_reduce16_fp16_overflow_skips():
+    """A sum beyond 65504 becomes inf in the fp16 reduce output: every rank skips,
+    while the fp32 reduce output of the same gradients steps normally."""
+    w = recipes.tiny()
+    psi, nd = 5000, 8
+    master, p16 = master_of(w, psi)
+    g = [synth.normal_16(psi, F16, w.seed, synth.stream_id(synth.GRAD, q, 1), 0, 1.0) for q in range(nd)]
+    big = oracle.encode16(F16, np.array([10000.0], np.float32))[0]
+    for q in range(nd):
+        g[q][77] = big
+    sim = Sim([psi], nd, F16, p16, master, "reduce", ranks=[0, nd - 1])
+    sim.p16_initial = p16.copy()
+    sim.set_reduce_out16()
+    res = sim.step(g, 1.0 / 65536, 1.0, hp_of(w.hp))
+    assert all(x["skipped"] for x in res) and res[0]["flag"]
+    sim.compare()
+    sim.set_reduce_out16(False)
+    res = sim.step(g, 1.0 / 65536, 1.0, hp_of(w.hp))
+    assert not any(x["skipped"] for x in res)
+    sim.compare()
+
+
+@pytest.mark.parametrize("last_fused", [True, False])
+def test_reduce16_with_accumulation(last_fused):
+    """Each micro-step's sum is rounded to 16 bits, then accumulated in fp32."""
+    w = recipes.tiny()
+    psi, nd = 150_001, 4
+    master, p16 = master_of(w, psi)
+    sim = Sim([psi], nd, F16, p16, master, "reduce")
+    sim.p16_initial = p16.copy()
+    sim.set_reduce_out16()
+    for step in range(1, 3):
+        micro = micro_grads(w, step, psi, nd, 3)
+        sim.step_accumulated(micro, 1.0 / w.loss_scale, w.max_norm, hp_of(w.hp), last_fused=last_fused)
+        sim.compare()
+
+
+def test_reduce16_api():
+    from zero_partitioned_mixed_reduce_amd import ZeroError
+    from zero_partitioned_mixed_reduce_amd._abi import ZERO_ESTATE, ZERO_EINVAL
+    from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
+    psi = 4096
+    w = recipes.tiny()
+    _, p16 = master_of(w, psi)
+    g = [dev16(x) for x in grads_for(w, 1, psi, 2)]
+    s = ZeroShard([psi], 2, 0, F16, dev16(p16))
+    with pytest.raises(ZeroError) as e:
+        s.zero_set_reduce_output(True)                  # no bufs.red
+    assert e.value.status == ZERO_EINVAL
+    s.close()
+    s = ZeroShard([psi], 2, 0, F16, dev16(p16), with_red=True)
+    s.zero_set_reduce_output(True)
+    s.zero_accumulate_grads(g)
+    with pytest.raises(ZeroError) as e:
+        s.zero_set_reduce_output(False)                 # while micro-steps are accumulated
+    assert e.value.status == ZERO_ESTATE
+    s.zero_reduce_grads(g, 1.0)
+    with pytest.raises(ZeroError) as e:
+        s.zero_set_reduce_output(False)                 # inside a step
+    assert e.value.status == ZERO_ESTATE
+    s.zero_check_overflow(False)
+    s.zero_grad_norm(0.0, 1.0)
+    s.zero_adam_step(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    s.export("red")                                     # an accumulated intake keeps fp32 values
+    s.zero_reduce_grads(g, 1.0)
+    with pytest.raises(ZeroError) as e:
+        s.export("red")                                 # red now holds the 16-bit result
+    assert e.value.status == ZERO_ESTATE
+    s.zero_check_overflow(False)
+    s.zero_grad_norm(0.0, 1.0)
+    s.zero_adam_step(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    s.zero_set_reduce_output(False)
+    torch.cuda.synchronize()
+    s.close()

@@ -58,6 +58,7 @@ _PROTOS = {
     "zero_reduce_grads": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_float,
                           ctypes.c_void_p],
     "zero_accumulate_grads": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_void_p],
+    "zero_set_reduce_output": [ctypes.c_void_p, ctypes.c_int32],
     "zero_local_stats": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
                          ctypes.c_void_p],
     "zero_check_overflow": [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p],
@@ -149,6 +150,10 @@ def zero_reduce_grads(h, rank_grad_ptrs, inv_loss_scale, stream):
     n = len(rank_grad_ptrs)
     arr = (ctypes.c_void_p * max(n, 1))(*rank_grad_ptrs)
     _call("zero_reduce_grads", h, arr if n else None, n, inv_loss_scale, stream)
+
+
+def zero_set_reduce_output(h, out_16bit):
+    _call("zero_set_reduce_output", h, int(bool(out_16bit)))
 
 
 def zero_accumulate_grads(h, rank_grad_ptrs, stream):

@@ -347,6 +347,13 @@ struct ReduceArgs {
 // chunk); kSrcNone: no new gradient (the accumulated one alone).
 enum { kSrcRanksN = 0, kSrcChunk = -1, kSrcNone = -2 };
 
+// The 16-bit output of the local reduce: the fp32 sum rounded once to the 16-bit
+// type (nearest even), as the step then takes it in.
+template <int DT>
+__device__ __forceinline__ float round16(float s) { return dec16<DT>(enc16<DT>(s)); }
+template <int DT>
+__device__ __forceinline__ f32x4 round16x4(f32x4 s) { return dec16x4<DT>(enc16x4<DT>(s)); }
+
 // s = the rank-order fp32 sum of this element's sources (g_0 + g_1 + ...).
 template <int DT, int NR>
 struct GradSum {
@@ -400,8 +407,9 @@ struct GradSum {
 };
 
 // Intake with statistics: u = (ACC ? red + s : s) * inv stored in red, plus the
-// fp64 sum of squares.  With kSrcNone, u = red * inv.
-template <int DT, int NR, bool ACC>
+// fp64 sum of squares.  With kSrcNone, u = red * inv.  R16: the new sources' sum s
+// arrives as a 16-bit reduce output (rounded once) before it is added.
+template <int DT, int NR, bool ACC, bool R16 = false>
 struct ReduceOp {
   GradSum<DT, NR> gs;
   float* red;
@@ -410,8 +418,8 @@ struct ReduceOp {
   __device__ __forceinline__ void elem(int64_t j) {
     float r;
     if constexpr (NR == kSrcNone) r = red[j];
-    else if constexpr (ACC) r = red[j] + gs.one(j);
-    else r = gs.one(j);
+    else if constexpr (ACC) r = red[j] + (R16 ? round16<DT>(gs.one(j)) : gs.one(j));
+    else r = R16 ? round16<DT>(gs.one(j)) : gs.one(j);
     const float u = r * inv;
     ss.add(0, u);
     red[j] = u;
@@ -420,6 +428,9 @@ struct ReduceOp {
   __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
     f32x4 s[U];
     if constexpr (NR != kSrcNone) gs.template quads<U>(j, stride, s);
+    if constexpr (R16 && NR != kSrcNone)
+#pragma unroll
+      for (int k = 0; k < U; ++k) s[k] = round16x4<DT>(s[k]);
     if constexpr (ACC || NR == kSrcNone) {
       f32x4 acc[U];
 #pragma unroll
@@ -440,9 +451,10 @@ struct ReduceOp {
   }
 };
 
-template <int DT, int NR, bool ACC>
+template <int DT, int NR, bool ACC, bool R16 = false>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
-  ReduceOp<DT, NR, ACC> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc), SumSq{}};
+  ReduceOp<DT, NR, ACC, R16> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc),
+                                SumSq{}};
   for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
     const Chunk ch = a.chunks[c];
     op.gs.flat_off = ch.flat_off;
@@ -454,19 +466,67 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
   finish_stats(op.ss.total(), a.sc, a.parts);
 }
 
+// Intake with a 16-bit reduce output: h = RNE16(s) is stored in red16 (this rank's
+// reduce-scatter result, in the state layout), then u = f32(h) * inv and the fp64
+// sum of squares of u.  The Adam pass re-reads h.
+template <int DT, int NR>
+struct Reduce16Op {
+  GradSum<DT, NR> gs;
+  uint16_t* red16;
+  float inv;
+  SumSq ss;
+  __device__ __forceinline__ void elem(int64_t j) {
+    const uint32_t h = enc16<DT>(gs.one(j));
+    red16[j] = (uint16_t)h;
+    ss.add(0, dec16<DT>(h) * inv);
+  }
+  template <int U>
+  __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
+    f32x4 s[U];
+    gs.template quads<U>(j, stride, s);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const u32x2 h = enc16x4<DT>(s[k]);
+      st16x4_nt(red16 + j + k * stride, h);
+      const f32x4 u = dec16x4<DT>(h) * inv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss.add(k, u[e]);
+    }
+  }
+};
+
+template <int DT, int NR>
+__global__ void __launch_bounds__(kBlock) reduce16_kernel(ReduceArgs a) {
+  Reduce16Op<DT, NR> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc), SumSq{}};
+  for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
+    const Chunk ch = a.chunks[c];
+    op.gs.flat_off = ch.flat_off;
+    op.red16 = reinterpret_cast<uint16_t*>(a.red) + ch.state_off;
+    const int head = head16(op.gs.src(0));
+    bool ok = aligned(op.red16 + head, 8);
+    for (int q = 0; q < op.gs.nranks(); ++q) ok = ok && aligned(op.gs.src(q) + head, 8);
+    run_chunk<ZS_REDUCE_U, 4>(op, ch.len, head, ok);
+  }
+  finish_stats(op.ss.total(), a.sc, a.parts);
+}
+
 // One micro-step into the accumulator, no statistics: red = FIRST ? s : red + s.
-template <int DT, int NR, bool FIRST>
+// R16: s arrives as a 16-bit reduce output (rounded once) before it is added.
+template <int DT, int NR, bool FIRST, bool R16 = false>
 struct AccumOp {
   GradSum<DT, NR> gs;
   float* red;
   __device__ __forceinline__ void elem(int64_t j) {
-    const float s = gs.one(j);
+    const float s = R16 ? round16<DT>(gs.one(j)) : gs.one(j);
     red[j] = FIRST ? s : red[j] + s;
   }
   template <int U>
   __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
     f32x4 s[U];
     gs.template quads<U>(j, stride, s);
+    if constexpr (R16)
+#pragma unroll
+      for (int k = 0; k < U; ++k) s[k] = round16x4<DT>(s[k]);
     if constexpr (!FIRST) {
       f32x4 acc[U];
 #pragma unroll
@@ -480,9 +540,9 @@ struct AccumOp {
 };
 
 // One short-lived block per part of a chunk, as in the Adam pass.
-template <int DT, int NR, bool FIRST>
+template <int DT, int NR, bool FIRST, bool R16 = false>
 __global__ void __launch_bounds__(kBlock) accum_kernel(ReduceArgs a) {
-  AccumOp<DT, NR, FIRST> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr};
+  AccumOp<DT, NR, FIRST, R16> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr};
   const int64_t n_items = a.n_chunks * ZS_ADAM_SPLIT;
   for (int64_t i = blockIdx.x; i < n_items; i += gridDim.x) {
     const Chunk ch = a.chunks[i / ZS_ADAM_SPLIT];
@@ -519,7 +579,9 @@ __device__ __forceinline__ void adam_elem(float u, float& w, float& m, float& v,
   v = vi;
 }
 
-enum { kGradFlat16 = 0, kGradChunk16 = 1, kGradRed = 2 };
+// Gradient sources of the Adam pass: the flat or registered 16-bit gradient, the fp32
+// u of a reduce or accumulation, or the 16-bit reduce output (in red, state layout).
+enum { kGradFlat16 = 0, kGradChunk16 = 1, kGradRed = 2, kGradRed16 = 3 };
 
 template <int DT, int GS, bool CAST, bool WT>
 struct AdamOp {
@@ -589,7 +651,7 @@ struct AdamArgs {
   const Chunk* chunks;
   int64_t n_chunks;
   const uint16_t* flat_g;  // kGradFlat16 source
-  const float* red;        // kGradRed source
+  const float* red;        // kGradRed source (kGradRed16: 16-bit values in the same buffer)
   float* master;
   float* m;
   float* v;
@@ -759,7 +821,10 @@ __global__ void __launch_bounds__(ZS_ADAM_BLOCK) adam_kernel(AdamArgs a) {
       head = head16(op.p16);
       ok = aligned(op.w + head, 16) && aligned(op.gred + head, 16);
     } else {
-      op.g16 = (GS == kGradFlat16 ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16)) + lo;
+      op.g16 = (GS == kGradFlat16    ? a.flat_g + ch.flat_off
+                : GS == kGradRed16 ? reinterpret_cast<const uint16_t*>(a.red) + ch.state_off
+                                   : reinterpret_cast<const uint16_t*>(ch.g16)) +
+               lo;
       head = head16(op.g16);
       ok = aligned(op.w + head, 16) && aligned(op.g16 + head, 8);
     }
@@ -884,6 +949,40 @@ hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, cons
   return hipGetLastError();
 }
 
+// Rank-buffer reduces whose micro-step sum arrives as a 16-bit reduce output (R16);
+// a single source needs no rounding (a 16-bit value rounds to itself).
+template <int DT>
+static void launch_reduce_acc_r16(const ReduceArgs& a, int src, unsigned g, hipStream_t st) {
+  switch (src) {
+    case 2: hipLaunchKernelGGL((reduce_kernel<DT, 2, true, true>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((reduce_kernel<DT, 4, true, true>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((reduce_kernel<DT, 8, true, true>), dim3(g), dim3(kBlock), 0, st, a); break;
+    default: hipLaunchKernelGGL((reduce_kernel<DT, kSrcRanksN, true, true>), dim3(g), dim3(kBlock), 0, st, a); break;
+  }
+}
+
+template <int DT>
+static void launch_reduce16_src(const ReduceArgs& a, int src, unsigned g, hipStream_t st) {
+  switch (src) {
+    case 2: hipLaunchKernelGGL((reduce16_kernel<DT, 2>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((reduce16_kernel<DT, 4>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((reduce16_kernel<DT, 8>), dim3(g), dim3(kBlock), 0, st, a); break;
+    default: hipLaunchKernelGGL((reduce16_kernel<DT, kSrcRanksN>), dim3(g), dim3(kBlock), 0, st, a); break;
+  }
+}
+
+template <int DT, bool FIRST>
+static void launch_accum_r16(const ReduceArgs& a, int src, unsigned g, hipStream_t st) {
+  switch (src) {
+    case 2: hipLaunchKernelGGL((accum_kernel<DT, 2, FIRST, true>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((accum_kernel<DT, 4, FIRST, true>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((accum_kernel<DT, 8, FIRST, true>), dim3(g), dim3(kBlock), 0, st, a); break;
+    default: hipLaunchKernelGGL((accum_kernel<DT, kSrcRanksN, FIRST, true>), dim3(g), dim3(kBlock), 0, st, a); break;
+  }
+}
+
+static bool is_rank_reduce(int src) { return src == 2 || src == 4 || src == 8 || src == kSrcRanksN; }
+
 template <int DT, bool ACC>
 static void launch_reduce_acc(const ReduceArgs& a, int src, unsigned g, hipStream_t st) {
   switch (src) {
@@ -936,9 +1035,13 @@ static int src_code(int32_t n_ranks) {
 
 // Intake with statistics into red: u = (accumulate ? red + s : s) * inv, or red * inv
 // when n_ranks < 0; the local flag and sum of squares go to the scalar block.
+//
+// r16: the rank buffers' sum arrives as a 16-bit reduce output.  Without
+// accumulation the 16-bit result itself is stored, in red (state layout, 2 bytes
+// per element), and u is taken from it; with accumulation the rounded sum is added.
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                         int32_t n_ranks, bool accumulate, float inv, int32_t dyn_slot, float* red, DevScalars* sc,
-                         StatsPart* parts, int64_t grid_cap, hipStream_t st) {
+                         int32_t n_ranks, bool accumulate, bool r16, float inv, int32_t dyn_slot, float* red,
+                         DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st) {
   if (n_chunks == 0) {
     hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc);
     return hipGetLastError();
@@ -946,6 +1049,16 @@ hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const
   const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, inv, dyn_slot, red, sc, parts);
   const unsigned g = stats_grid(n_chunks, grid_cap);
   const int src = src_code(n_ranks);
+  if (r16 && is_rank_reduce(src)) {
+    if (dtype == ZERO_BF16) {
+      if (accumulate) launch_reduce_acc_r16<ZERO_BF16>(a, src, g, st);
+      else launch_reduce16_src<ZERO_BF16>(a, src, g, st);
+    } else {
+      if (accumulate) launch_reduce_acc_r16<ZERO_F16>(a, src, g, st);
+      else launch_reduce16_src<ZERO_F16>(a, src, g, st);
+    }
+    return hipGetLastError();
+  }
   if (dtype == ZERO_BF16) {
     if (accumulate) launch_reduce_acc<ZERO_BF16, true>(a, src, g, st);
     else launch_reduce_acc<ZERO_BF16, false>(a, src, g, st);
@@ -956,13 +1069,24 @@ hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const
   return hipGetLastError();
 }
 
-// One micro-step into the accumulator: red = first ? s : red + s.
+// One micro-step into the accumulator: red = first ? s : red + s (r16: s rounded to
+// the 16-bit type first, the reduce-scatter's 16-bit result).
 hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                             int32_t n_ranks, bool first, float* red, int64_t grid_cap, hipStream_t st) {
+                             int32_t n_ranks, bool first, bool r16, float* red, int64_t grid_cap, hipStream_t st) {
   if (n_chunks == 0) return hipSuccess;
   const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, 1.0f, -1, red, nullptr, nullptr);
   const unsigned g = clamp_grid(n_chunks * ZS_ADAM_SPLIT, grid_cap);
   const int src = src_code(n_ranks);
+  if (r16 && is_rank_reduce(src)) {
+    if (dtype == ZERO_BF16) {
+      if (first) launch_accum_r16<ZERO_BF16, true>(a, src, g, st);
+      else launch_accum_r16<ZERO_BF16, false>(a, src, g, st);
+    } else {
+      if (first) launch_accum_r16<ZERO_F16, true>(a, src, g, st);
+      else launch_accum_r16<ZERO_F16, false>(a, src, g, st);
+    }
+    return hipGetLastError();
+  }
   if (dtype == ZERO_BF16) {
     if (first) launch_accum_first<ZERO_BF16, true>(a, src, g, st);
     else launch_accum_first<ZERO_BF16, false>(a, src, g, st);
@@ -987,7 +1111,8 @@ template <int DT>
 static void launch_adam_dt(const AdamArgs& a, int gs, bool cast, unsigned g, hipStream_t st) {
   if (gs == kGradFlat16) launch_adam_gs<DT, kGradFlat16>(a, cast, g, st);
   else if (gs == kGradChunk16) launch_adam_gs<DT, kGradChunk16>(a, cast, g, st);
-  else launch_adam_gs<DT, kGradRed>(a, cast, g, st);
+  else if (gs == kGradRed) launch_adam_gs<DT, kGradRed>(a, cast, g, st);
+  else launch_adam_gs<DT, kGradRed16>(a, cast, g, st);
 }
 
 hipError_t launch_adam(int dtype, int grad_source, bool cast, const AdamArgs& a, int64_t grid_cap, hipStream_t st) {

@@ -21,10 +21,10 @@ namespace zs {
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
                           int32_t dyn_slot, DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st);
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                         int32_t n_ranks, bool accumulate, float inv, int32_t dyn_slot, float* red, DevScalars* sc,
-                         StatsPart* parts, int64_t grid_cap, hipStream_t st);
+                         int32_t n_ranks, bool accumulate, bool r16, float inv, int32_t dyn_slot, float* red,
+                         DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st);
 hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                             int32_t n_ranks, bool first, float* red, int64_t grid_cap, hipStream_t st);
+                             int32_t n_ranks, bool first, bool r16, float* red, int64_t grid_cap, hipStream_t st);
 struct AdamArgs;
 hipError_t launch_cast(int dtype, const Chunk* chunks, int64_t n_chunks, const float* master,
                        const DevScalars* sc, const SegArgs* seg, int64_t grid_cap, hipStream_t st);
@@ -62,7 +62,7 @@ zero_status_t hip_fail(const char* what, hipError_t e) {
   } while (0)
 
 enum Phase { kReady, kReduced, kChecked, kNormed, kStepped };
-enum { kGradFlat16 = 0, kGradChunk16 = 1, kGradRed = 2 };
+enum { kGradFlat16 = 0, kGradChunk16 = 1, kGradRed = 2, kGradRed16 = 3 };
 
 }  // namespace
 
@@ -89,6 +89,7 @@ struct zero_shard {
   Phase phase;
   bool cast_pending;
   bool accumulating;   // micro-steps summed into red since the last intake
+  bool reduce_out16;   // the local reduce delivers its sum in the 16-bit type
   int64_t dp_size;
   bool dynamic;        // device-resident dynamic loss scale enabled
   zero_loss_scaler_t dyn_cfg;
@@ -208,6 +209,7 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
   h->phase = kReady;
   h->cast_pending = false;
   h->accumulating = false;
+  h->reduce_out16 = false;
   h->dp_size = desc->dp_size;
   h->dynamic = false;
   memset(&h->dyn_cfg, 0, sizeof(h->dyn_cfg));
@@ -273,6 +275,16 @@ zero_status_t check_sources(zero_shard* h, const void* const* rank_grads, int32_
 }
 }  // namespace
 
+zero_status_t zero_set_reduce_output(zero_shard_t h, int32_t out_16bit) {
+  if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (out_16bit != 0 && out_16bit != 1) return fail(ZERO_EINVAL, "out_16bit must be 0 or 1");
+  if (!(h->phase == kReady || h->phase == kStepped) || h->cast_pending || h->accumulating)
+    return fail(ZERO_ESTATE, "the reduce output is set between steps");
+  if (out_16bit && !h->red) return fail(ZERO_EINVAL, "the 16-bit reduce output is kept in bufs.red");
+  h->reduce_out16 = out_16bit != 0;
+  return ZERO_OK;
+}
+
 zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
   if (h->phase == kReduced || h->phase == kChecked || h->phase == kNormed)
@@ -284,7 +296,7 @@ zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grad
   if (s != ZERO_OK) return s;
   DeviceGuard dg(h->device);
   hipError_t e = zs::launch_accumulate(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, !h->accumulating,
-                                       h->red, h->grid_main, static_cast<hipStream_t>(stream));
+                                       h->reduce_out16, h->red, h->grid_main, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("accumulate kernel", e);
   h->accumulating = true;
   h->phase = kReady;
@@ -315,8 +327,8 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
       zero_status_t s = check_sources(h, rank_grads, n_ranks);
       if (s != ZERO_OK) return s;
     }
-    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, true, inv_loss_scale, dyn_slot,
-                          h->red, h->sc, h->parts, h->grid_stats, st);
+    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, true, h->reduce_out16,
+                          inv_loss_scale, dyn_slot, h->red, h->sc, h->parts, h->grid_stats, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
     h->grad_source = kGradRed;
     h->step_flat_g = nullptr;
@@ -344,10 +356,10 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     for (int q = 0; q < n_ranks; ++q)
       if (!rank_grads[q]) return fail(ZERO_EINVAL, "rank_grads[" + std::to_string(q) + "] is null");
     if (!h->red) return fail(ZERO_EINVAL, "reducing N_d >= 2 buffers needs bufs.red");
-    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, false, inv_loss_scale, dyn_slot,
-                          h->red, h->sc, h->parts, h->grid_stats, st);
+    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, false, h->reduce_out16,
+                          inv_loss_scale, dyn_slot, h->red, h->sc, h->parts, h->grid_stats, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
-    h->grad_source = kGradRed;
+    h->grad_source = h->reduce_out16 ? kGradRed16 : kGradRed;
     h->step_flat_g = nullptr;
   }
   h->inv = inv_loss_scale;
@@ -580,6 +592,8 @@ zero_status_t zero_export_state(zero_shard_t h, int32_t which, float* dst, void*
   if (!h) return fail(ZERO_EINVAL, "null handle");
   const float* src = which == 0 ? h->master : which == 1 ? h->m : which == 2 ? h->v : which == 3 ? h->red : nullptr;
   if (!src) return fail(ZERO_EINVAL, "which must be 0 (master), 1 (m), 2 (v) or 3 (red, when allocated)");
+  if (which == 3 && h->grad_source == kGradRed16)
+    return fail(ZERO_ESTATE, "bufs.red holds the last intake's 16-bit reduce output, not fp32 values");
   if (!dst && h->info.valid_elems > 0) return fail(ZERO_EINVAL, "null destination");
   DeviceGuard dg(h->device);
   hipError_t e = zs::launch_export(h->chunks, h->n_chunks, src, dst, h->grid_main, static_cast<hipStream_t>(stream));

@@ -93,6 +93,10 @@ class ZeroShard:
         ptrs = [g.data_ptr() for g in rank_grads] if rank_grads else []
         abi.zero_reduce_grads(self.h, ptrs, inv_loss_scale, _stream())
 
+    def zero_set_reduce_output(self, out_16bit):
+        """Deliver the local reduce's sum in the 16-bit dtype (True) or keep it in fp32 (False)."""
+        abi.zero_set_reduce_output(self.h, out_16bit)
+
     def zero_accumulate_grads(self, rank_grads):
         ptrs = [g.data_ptr() for g in rank_grads] if rank_grads else []
         abi.zero_accumulate_grads(self.h, ptrs, _stream())
