@@ -26,6 +26,8 @@
 //   ZS_STATS_NT non-temporal gradient loads in the statistics pass
 //   ZS_STATS_MIN_CHUNKS  minimum chunks per block of a statistics pass
 //   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
+//   ZS_STATS_PF request the next chunk's table entry before streaming the current chunk
+//               (persistent statistics and reduce passes)
 //   ZS_NT_LOAD  non-temporal loads of the fp32 state (read once per step)
 //   ZS_NT_STORE non-temporal stores of the fp32 state and 16-bit parameters
 //   ZS_ADAM_SPLIT    parts per chunk in the Adam pass (one block per part)
@@ -47,6 +49,9 @@
 #endif
 #ifndef ZS_REDUCE_U
 #define ZS_REDUCE_U 2
+#endif
+#ifndef ZS_STATS_PF
+#define ZS_STATS_PF 1
 #endif
 #ifndef ZS_ADAM_BLOCK
 #define ZS_ADAM_BLOCK 256
@@ -311,18 +316,47 @@ __device__ __forceinline__ float intake_inv(float inv, int32_t dyn_slot, const D
   return dyn_slot >= 0 ? 1.0f / sc->slot[dyn_slot].scale : inv;
 }
 
+// The table fields an intake pass needs, held in scalar registers.
+struct ChunkRef {
+  int64_t state_off, flat_off;
+  uint64_t g16;
+  int64_t len;
+};
+__device__ __forceinline__ ChunkRef chunk_ref(const Chunk* c) { return ChunkRef{c->state_off, c->flat_off, c->g16, c->len}; }
+
+// Walks chunks c, c + G, ... of a persistent block, calling body(ref).  With
+// ZS_STATS_PF the next chunk's table entry is requested before the current
+// chunk's data is streamed, so the entry's latency hides under that work.
+template <class Body>
+__device__ __forceinline__ void walk_chunks(const Chunk* chunks, int64_t n_chunks, Body body) {
+#if ZS_STATS_PF
+  int64_t c = blockIdx.x;
+  if (c >= n_chunks) return;
+  ChunkRef ch = chunk_ref(chunks + c);
+  for (;;) {
+    const int64_t cn = c + gridDim.x;
+    const ChunkRef nx = chunk_ref(chunks + (cn < n_chunks ? cn : c));  // unconditional: nothing waits for it here
+    body(ch);
+    if (cn >= n_chunks) break;
+    ch = nx;
+    c = cn;
+  }
+#else
+  for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) body(chunk_ref(chunks + c));
+#endif
+}
+
 template <int DT>
 __global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
   Stats16Op<DT> op{nullptr, intake_inv(a.inv, a.dyn_slot, a.sc), SumSq{}};
-  for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
-    const Chunk ch = a.chunks[c];
+  walk_chunks(a.chunks, a.n_chunks, [&](const ChunkRef ch) {
     op.g = a.flat_g ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
 #if ZS_STATS_V == 8
     run_chunk<ZS_STATS_U, 8>(op, ch.len, head16x8(op.g), true);
 #else
     run_chunk<ZS_STATS_U, 4>(op, ch.len, head16(op.g), true);
 #endif
-  }
+  });
   finish_stats(op.ss.total(), a.sc, a.parts);
 }
 
@@ -455,14 +489,13 @@ template <int DT, int NR, bool ACC, bool R16 = false>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
   ReduceOp<DT, NR, ACC, R16> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc),
                                 SumSq{}};
-  for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
-    const Chunk ch = a.chunks[c];
+  walk_chunks(a.chunks, a.n_chunks, [&](const ChunkRef ch) {
     op.gs.flat_off = ch.flat_off;
     op.gs.src0 = reinterpret_cast<const uint16_t*>(ch.g16);
     op.red = a.red + ch.state_off;
     const int head = op.gs.head(op.red);
     run_chunk<ZS_REDUCE_U, 4>(op, ch.len, head, op.gs.aligned_at(head, op.red));
-  }
+  });
   finish_stats(op.ss.total(), a.sc, a.parts);
 }
 
@@ -498,15 +531,14 @@ struct Reduce16Op {
 template <int DT, int NR>
 __global__ void __launch_bounds__(kBlock) reduce16_kernel(ReduceArgs a) {
   Reduce16Op<DT, NR> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc), SumSq{}};
-  for (int64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
-    const Chunk ch = a.chunks[c];
+  walk_chunks(a.chunks, a.n_chunks, [&](const ChunkRef ch) {
     op.gs.flat_off = ch.flat_off;
     op.red16 = reinterpret_cast<uint16_t*>(a.red) + ch.state_off;
     const int head = head16(op.gs.src(0));
     bool ok = aligned(op.red16 + head, 8);
     for (int q = 0; q < op.gs.nranks(); ++q) ok = ok && aligned(op.gs.src(q) + head, 8);
     run_chunk<ZS_REDUCE_U, 4>(op, ch.len, head, ok);
-  }
+  });
   finish_stats(op.ss.total(), a.sc, a.parts);
 }
 
