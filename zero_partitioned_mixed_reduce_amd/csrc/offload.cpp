@@ -360,10 +360,10 @@ void run_upcast(zero_offload* h) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-zero_status_t zero_offload_init(const zero_shard_desc_t* desc, const zero_offload_bufs_t* bufs,
-                                const float* master_init, int32_t num_threads, void* stream, zero_offload_t* out) {
+zero_status_t offload_init(const zero_shard_desc_t* desc, const zero_offload_bufs_t* bufs, const float* master_init,
+                           int32_t num_threads, void* stream, zero_offload_t* out) {
   if (!desc || !bufs || !out) return fail(ZERO_EINVAL, "null description, buffers or output handle");
   *out = nullptr;
   if (!host_has_avx512()) return fail(ZERO_EINVAL, "the offloaded step needs host AVX-512 (F, BW, VL)");
@@ -500,6 +500,20 @@ zero_status_t zero_offload_init(const zero_shard_desc_t* desc, const zero_offloa
   return ZERO_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+// Host allocations and thread creation may throw; no exception leaves the C ABI.
+zero_status_t zero_offload_init(const zero_shard_desc_t* desc, const zero_offload_bufs_t* bufs,
+                                const float* master_init, int32_t num_threads, void* stream, zero_offload_t* out) {
+  try {
+    return offload_init(desc, bufs, master_init, num_threads, stream, out);
+  } catch (const std::exception& e) {
+    return fail(ZERO_EINVAL, std::string("host resources: ") + e.what());
+  }
+}
+
 zero_status_t zero_offload_fetch_grads(zero_offload_t h, const void* flat_grad16, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
   if (!h->has_device) return fail(ZERO_EINVAL, "host-only handle: no device gradient to fetch");
@@ -580,6 +594,9 @@ zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t
   if (!hp) return fail(ZERO_EINVAL, "null hparams");
   if (push && !h->has_device) return fail(ZERO_EINVAL, "push needs device parameters (host-only handle)");
   if (h->phase != kStats) return fail(ZERO_ESTATE, "zero_offload_adam_step needs zero_offload_grad_stats first");
+  // per copy block: tiles finished (allocated before any state changes)
+  std::unique_ptr<std::atomic<int64_t>[]> done(new (std::nothrow) std::atomic<int64_t>[h->n_blocks > 0 ? h->n_blocks : 1]);
+  if (!done) return fail(ZERO_EINVAL, "out of host memory");
   DeviceGuard dg(h->device, h->has_device);
   zero_status_t rs = wait_push(h);
   if (rs != ZERO_OK) return rs;
@@ -613,7 +630,6 @@ zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t
   s.wd = hp->weight_decay;
 
   std::atomic<int64_t> next{0};
-  std::unique_ptr<std::atomic<int64_t>[]> done(new std::atomic<int64_t>[h->n_blocks > 0 ? h->n_blocks : 1]);
   for (int64_t k = 0; k < h->n_blocks; ++k) done[k].store(0, std::memory_order_relaxed);
   const int dt = h->dtype;
   h->pool->start([&](int) {

@@ -140,7 +140,11 @@ extern "C" {
 
 const char* zero_last_error(void) { return g_err.c_str(); }
 
-zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* out) {
+}  // extern "C"
+
+namespace {
+
+zero_status_t shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* out) {
   if (!out) return fail(ZERO_EINVAL, "null output");
   zs::Plan p;
   zero_status_t s = zs::build_plan(desc, &p, &g_err);
@@ -149,8 +153,8 @@ zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* 
   return ZERO_OK;
 }
 
-zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
-                              const float* master_init, void* stream, zero_shard_t* out) {
+zero_status_t shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs, const float* master_init,
+                         void* stream, zero_shard_t* out) {
   if (!bufs || !out) return fail(ZERO_EINVAL, "null buffers or output handle");
   *out = nullptr;
   zs::Plan p;
@@ -258,6 +262,28 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
   }
   *out = h;
   return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+// The plan's host tables may not fit in host memory: no exception leaves the C ABI.
+zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* out) {
+  try {
+    return shard_plan(desc, out);
+  } catch (const std::exception& e) {
+    return fail(ZERO_EINVAL, std::string("host resources: ") + e.what());
+  }
+}
+
+zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
+                              const float* master_init, void* stream, zero_shard_t* out) {
+  try {
+    return shard_init(desc, bufs, master_init, stream, out);
+  } catch (const std::exception& e) {
+    return fail(ZERO_EINVAL, std::string("host resources: ") + e.what());
+  }
 }
 
 namespace {
