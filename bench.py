@@ -438,7 +438,7 @@ def bench_offload(a, w, rank):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": f"this build runs one data-parallel rank on one GPU; --gpus {a.gpus} "
+        print(json.dumps({"error": f"this benchmark runs one data-parallel rank on one GPU; --gpus {a.gpus} "
                                    "is not supported (the path has no collectives: see the design notes "
                                    "for how it shards)"}), flush=True)
         sys.exit(2)
