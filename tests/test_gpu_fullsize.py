@@ -162,10 +162,11 @@ def test_full_size_sampled(cfg, rank, micro, r16):
 
     sidx = torch.from_numpy(state_index(pieces, pos)).cuda()
     s = wl.shard
-    assert_f32_close(s.master[sidx].cpu().numpy(), wv, f"{cfg} master")
-    assert_f32_close(s.m[sidx].cpu().numpy(), mv, f"{cfg} m")
-    assert_f32_close(s.v[sidx].cpu().numpy(), vv, f"{cfg} v")
-    assert_16_close(gpu_params_at(wl, flat), p16, f"{cfg} p16")
+    nonexact = assert_f32_close(s.master[sidx].cpu().numpy(), wv, f"{cfg} master")
+    nonexact += assert_f32_close(s.m[sidx].cpu().numpy(), mv, f"{cfg} m")
+    nonexact += assert_f32_close(s.v[sidx].cpu().numpy(), vv, f"{cfg} v")
+    nonexact += assert_16_close(gpu_params_at(wl, flat), p16, f"{cfg} p16")
+    assert nonexact == 0, f"{nonexact} sampled values within tolerance but not bit-exact"
     # parameters outside this rank's shard are untouched: check around both shard edges
     outside = np.concatenate([np.arange(max(0, b - 2048), b), np.arange(b + valid, min(w.psi, b + valid + 2048))])
     if outside.size:

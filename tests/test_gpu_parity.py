@@ -4,7 +4,9 @@ Sizes span many chunks and ragged tails; every rank of the data-parallel group
 is simulated so the shard boundaries and the exchange are exercised.
 Tolerance (stated for the method): fp32 master/m/v within 2 ulp or 1e-6
 relative, 16-bit parameters within 1 ulp, flags and skip decisions and t
-exact, norm within 1e-6 relative (local sums of squares within 1e-9).
+exact, norm within 1e-6 relative (local sums of squares within 1e-9).  Past
+that bar the values are also required to be bit-exact: the kernels take the
+oracle's operation order with correctly rounded fp32 arithmetic.
 """
 import numpy as np
 import pytest
