@@ -24,7 +24,8 @@
 //   ZS_STATS_U  quads per lane in flight in the statistics pass
 //   ZS_STATS_V  elements per lane per group in the statistics pass (4: 8-byte loads, 8: 16-byte)
 //   ZS_STATS_NT non-temporal gradient loads in the statistics pass
-//   ZS_STATS_MIN_CHUNKS  minimum chunks per block of a statistics pass
+//   ZS_STATS_SMALL  a statistics pass over fewer chunks than this takes ZS_STATS_SMALL_CPB
+//                   consecutive chunks per block (else one); the reduce passes take one
 //   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
 //   ZS_STATS_PF request the next chunk's table entry before streaming the current chunk
 //               (persistent statistics and reduce passes)
@@ -44,8 +45,11 @@
 #ifndef ZS_STATS_NT
 #define ZS_STATS_NT 0
 #endif
-#ifndef ZS_STATS_MIN_CHUNKS
-#define ZS_STATS_MIN_CHUNKS 32
+#ifndef ZS_STATS_SMALL
+#define ZS_STATS_SMALL 32768
+#endif
+#ifndef ZS_STATS_SMALL_CPB
+#define ZS_STATS_SMALL_CPB 4
 #endif
 #ifndef ZS_REDUCE_U
 #define ZS_REDUCE_U 2
@@ -208,36 +212,57 @@ __device__ __forceinline__ double block_sum(double x, double* lds) {
   return r;
 }
 
-// Called by every block of a statistics pass with its partial sum of squares.
-// The last block to finish adds all partials in block order, publishes the
-// local sum and the local non-finite flag (the sum is non-finite exactly when
-// some u is, see SumSq), and re-arms the completion counter.
-__device__ void finish_stats(double acc, DevScalars* sc, StatsPart* parts) {
+__device__ __forceinline__ void store_part(uint64_t* p, double v) {
+  __hip_atomic_store(p, (uint64_t)__double_as_longlong(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double load_part(const uint64_t* p) {
+  return __longlong_as_double((long long)__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// Waits until this thread's device-scope stores have reached the device's coherence
+// point, so that an arrival counted after it finds them there.
+__device__ __forceinline__ void stores_complete() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Called by every block of an intake pass with its partial sum of squares: a
+// deterministic two-level combine without float atomics or cache-wide fences.
+// Block b stores its partial (device scope), waits for the store to complete and
+// arrives on the counter of its group of kGroup blocks.  The group's last block
+// adds the group's partials in block order (one per lane, fixed butterfly),
+// stores the group sum and arrives on the pass counter; the last group's block
+// adds the group sums in group order and publishes this rank's sum of squares and
+// non-finite flag (the sum is non-finite exactly when some u is, see SumSq).
+// Counters are re-armed by their last arrival.
+__device__ void finish_stats(double acc, DevScalars* sc, const IntakeParts& p) {
   __shared__ double lds[kBlock / 64];
   __shared__ int is_last;
   const double bsum = block_sum(acc, lds);
+  const uint32_t b = blockIdx.x, nb = gridDim.x;
+  const uint32_t g = b / kGroup, g0 = g * kGroup;
+  const uint32_t gsize = nb - g0 < (uint32_t)kGroup ? nb - g0 : (uint32_t)kGroup;
+  const uint32_t ngroups = (nb + kGroup - 1) / kGroup;
   if (threadIdx.x == 0) {
-    __hip_atomic_store(&parts[blockIdx.x].sumsq_bits, (uint64_t)__double_as_longlong(bsum), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t prev = __hip_atomic_fetch_add(&sc->counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == gridDim.x - 1);
+    store_part(p.part + b, bsum);
+    stores_complete();
+    const uint32_t prev = __hip_atomic_fetch_add(&p.gcount[g].count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = prev + 1 == gsize;
   }
   __syncthreads();
   if (!is_last) return;
-  // every load of this thread is issued before any is consumed (one memory round trip,
-  // not one per partial); the partials are then added in block order
-  constexpr int kPer = kMaxStatsBlocks / kBlock;
-  double v[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const uint32_t b = threadIdx.x + i * kBlock;
-    v[i] = b < gridDim.x ? __longlong_as_double((long long)__hip_atomic_load(
-                               &parts[b].sumsq_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                         : 0.0;
+  const double gsum = block_sum(threadIdx.x < gsize ? load_part(p.part + g0 + threadIdx.x) : 0.0, lds);
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(&p.gcount[g].count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store_part(p.gpart + g, gsum);
+    stores_complete();
+    const uint32_t prev = __hip_atomic_fetch_add(&sc->counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = prev + 1 == ngroups;
   }
+  __syncthreads();
+  if (!is_last) return;
   double s = 0.0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) s += v[i];
+  for (uint32_t i = threadIdx.x; i < ngroups; i += kBlock) s += load_part(p.gpart + i);
   const double total = block_sum(s, lds);
   if (threadIdx.x == 0) {
     sc->local_sumsq = total;
@@ -306,8 +331,9 @@ struct StatsArgs {
   const uint16_t* flat_g;  // flat [psi] gradient, or null to use chunk.g16
   float inv;
   int32_t dyn_slot;        // >= 0: unscale by 1 / sc->slot[dyn_slot].scale instead of inv
+  int32_t cpb;             // consecutive chunks per block
   DevScalars* sc;
-  StatsPart* parts;
+  IntakeParts parts;
 };
 
 // The unscale factor of an intake pass: the call's inv, or 1 / the device-resident
@@ -324,32 +350,36 @@ struct ChunkRef {
 };
 __device__ __forceinline__ ChunkRef chunk_ref(const Chunk* c) { return ChunkRef{c->state_off, c->flat_off, c->g16, c->len}; }
 
-// Walks chunks c, c + G, ... of a persistent block, calling body(ref).  With
-// ZS_STATS_PF the next chunk's table entry is requested before the current
-// chunk's data is streamed, so the entry's latency hides under that work.
+// Walks block b's run of `cpb` consecutive chunks, calling body(ref).  The blocks
+// are short-lived and dispatched in order, so the pass streams a compact window of
+// the shard.  With ZS_STATS_PF and more than one chunk per block the next chunk's
+// table entry is requested before the current chunk is streamed.
 template <class Body>
-__device__ __forceinline__ void walk_chunks(const Chunk* chunks, int64_t n_chunks, Body body) {
+__device__ __forceinline__ void walk_chunks(const Chunk* chunks, int64_t n_chunks, int32_t cpb, Body body) {
+  const int64_t c0 = (int64_t)blockIdx.x * cpb;
+  const int64_t c1 = c0 + cpb < n_chunks ? c0 + cpb : n_chunks;
+  if (c0 >= c1) return;
 #if ZS_STATS_PF
-  int64_t c = blockIdx.x;
-  if (c >= n_chunks) return;
-  ChunkRef ch = chunk_ref(chunks + c);
-  for (;;) {
-    const int64_t cn = c + gridDim.x;
-    const ChunkRef nx = chunk_ref(chunks + (cn < n_chunks ? cn : c));  // unconditional: nothing waits for it here
-    body(ch);
-    if (cn >= n_chunks) break;
-    ch = nx;
-    c = cn;
+  if (cpb > 1) {
+    ChunkRef ch = chunk_ref(chunks + c0);
+    for (int64_t c = c0;;) {
+      const int64_t cn = c + 1;
+      const ChunkRef nx = chunk_ref(chunks + (cn < c1 ? cn : c));  // unconditional: nothing waits for it here
+      body(ch);
+      if (cn >= c1) break;
+      ch = nx;
+      c = cn;
+    }
+    return;
   }
-#else
-  for (int64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) body(chunk_ref(chunks + c));
 #endif
+  for (int64_t c = c0; c < c1; ++c) body(chunk_ref(chunks + c));
 }
 
 template <int DT>
 __global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
   Stats16Op<DT> op{nullptr, intake_inv(a.inv, a.dyn_slot, a.sc), SumSq{}};
-  walk_chunks(a.chunks, a.n_chunks, [&](const ChunkRef ch) {
+  walk_chunks(a.chunks, a.n_chunks, a.cpb, [&](const ChunkRef ch) {
     op.g = a.flat_g ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
 #if ZS_STATS_V == 8
     run_chunk<ZS_STATS_U, 8>(op, ch.len, head16x8(op.g), true);
@@ -371,8 +401,9 @@ struct ReduceArgs {
   float inv;
   int32_t dyn_slot;        // as in StatsArgs
   float* red;
+  int32_t cpb;             // consecutive chunks per block of the intake passes
   DevScalars* sc;
-  StatsPart* parts;
+  IntakeParts parts;
 };
 
 // Gradient sources of the intake passes.  NR > 0: that many rank buffers
@@ -489,7 +520,7 @@ template <int DT, int NR, bool ACC, bool R16 = false>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
   ReduceOp<DT, NR, ACC, R16> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc),
                                 SumSq{}};
-  walk_chunks(a.chunks, a.n_chunks, [&](const ChunkRef ch) {
+  walk_chunks(a.chunks, a.n_chunks, a.cpb, [&](const ChunkRef ch) {
     op.gs.flat_off = ch.flat_off;
     op.gs.src0 = reinterpret_cast<const uint16_t*>(ch.g16);
     op.red = a.red + ch.state_off;
@@ -531,7 +562,7 @@ struct Reduce16Op {
 template <int DT, int NR>
 __global__ void __launch_bounds__(kBlock) reduce16_kernel(ReduceArgs a) {
   Reduce16Op<DT, NR> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc), SumSq{}};
-  walk_chunks(a.chunks, a.n_chunks, [&](const ChunkRef ch) {
+  walk_chunks(a.chunks, a.n_chunks, a.cpb, [&](const ChunkRef ch) {
     op.gs.flat_off = ch.flat_off;
     op.red16 = reinterpret_cast<uint16_t*>(a.red) + ch.state_off;
     const int head = head16(op.gs.src(0));
@@ -953,27 +984,20 @@ static unsigned clamp_grid(int64_t n_chunks, int64_t cap) {
   return (unsigned)(g < 1 ? 1 : g);
 }
 
-// Grid of a statistics pass: each block finishes with a device-scope atomic on
-// one counter (plus its release and acquire), so a block should carry at least
-// ZS_STATS_MIN_CHUNKS chunks -- but small shards still get up to 256 blocks (one
-// block per CU) so that no block walks a long serial run of chunks.  Capped by
-// the partial-sum slots and the device.
-static unsigned stats_grid(int64_t n_chunks, int64_t grid_cap) {
-  const int64_t cap = grid_cap < kMaxStatsBlocks ? grid_cap : kMaxStatsBlocks;
-  int64_t want = (n_chunks + ZS_STATS_MIN_CHUNKS - 1) / ZS_STATS_MIN_CHUNKS;
-  const int64_t floor_blocks = n_chunks < 256 ? n_chunks : 256;
-  if (want < floor_blocks) want = floor_blocks;
-  return clamp_grid(want, cap);
+// Grid of an intake pass: one short-lived block per run of cpb chunks.
+static unsigned intake_grid(int64_t n_chunks, int32_t cpb) {
+  return clamp_grid((n_chunks + cpb - 1) / cpb, n_chunks);
 }
 
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
-                          int32_t dyn_slot, DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st) {
+                          int32_t dyn_slot, DevScalars* sc, const IntakeParts& parts, hipStream_t st) {
   if (n_chunks == 0) {
     hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc);
     return hipGetLastError();
   }
-  StatsArgs a{chunks, n_chunks, flat_g, inv, dyn_slot, sc, parts};
-  const unsigned g = stats_grid(n_chunks, grid_cap);
+  const int32_t cpb = n_chunks < ZS_STATS_SMALL ? ZS_STATS_SMALL_CPB : 1;
+  StatsArgs a{chunks, n_chunks, flat_g, inv, dyn_slot, cpb, sc, parts};
+  const unsigned g = intake_grid(n_chunks, cpb);
   if (dtype == ZERO_BF16)
     hipLaunchKernelGGL(stats16_kernel<ZERO_BF16>, dim3(g), dim3(kBlock), 0, st, a);
   else
@@ -1041,7 +1065,8 @@ static void launch_accum_first(const ReduceArgs& a, int src, unsigned g, hipStre
 }
 
 static ReduceArgs make_reduce_args(const Chunk* chunks, int64_t n_chunks, const void* const* ranks, int32_t n_ranks,
-                                   float inv, int32_t dyn_slot, float* red, DevScalars* sc, StatsPart* parts) {
+                                   float inv, int32_t dyn_slot, float* red, DevScalars* sc,
+                                   const IntakeParts& parts) {
   ReduceArgs a;
   a.chunks = chunks;
   a.n_chunks = n_chunks;
@@ -1051,6 +1076,7 @@ static ReduceArgs make_reduce_args(const Chunk* chunks, int64_t n_chunks, const 
   a.inv = inv;
   a.dyn_slot = dyn_slot;
   a.red = red;
+  a.cpb = 1;
   a.sc = sc;
   a.parts = parts;
   return a;
@@ -1073,13 +1099,13 @@ static int src_code(int32_t n_ranks) {
 // per element), and u is taken from it; with accumulation the rounded sum is added.
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
                          int32_t n_ranks, bool accumulate, bool r16, float inv, int32_t dyn_slot, float* red,
-                         DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st) {
+                         DevScalars* sc, const IntakeParts& parts, hipStream_t st) {
   if (n_chunks == 0) {
     hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc);
     return hipGetLastError();
   }
   const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, inv, dyn_slot, red, sc, parts);
-  const unsigned g = stats_grid(n_chunks, grid_cap);
+  const unsigned g = intake_grid(n_chunks, a.cpb);
   const int src = src_code(n_ranks);
   if (r16 && is_rank_reduce(src)) {
     if (dtype == ZERO_BF16) {
@@ -1106,7 +1132,7 @@ hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const
 hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
                              int32_t n_ranks, bool first, bool r16, float* red, int64_t grid_cap, hipStream_t st) {
   if (n_chunks == 0) return hipSuccess;
-  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, 1.0f, -1, red, nullptr, nullptr);
+  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, 1.0f, -1, red, nullptr, IntakeParts{});
   const unsigned g = clamp_grid(n_chunks * ZS_ADAM_SPLIT, grid_cap);
   const int src = src_code(n_ranks);
   if (r16 && is_rank_reduce(src)) {

@@ -130,7 +130,7 @@ zero_status_t build_plan(const zero_shard_desc_t* d, Plan* out, std::string* err
   p.info.state_elems = state_elems;
   p.info.num_pieces = (int64_t)p.pieces.size();
   p.info.num_chunks = (int64_t)p.chunks.size();
-  p.info.workspace_bytes = round_up(kChunksOff + (int64_t)p.chunks.size() * (int64_t)sizeof(Chunk), 256);
+  p.info.workspace_bytes = intake_layout((int64_t)p.chunks.size()).end;
   p.info.model_state_bytes = 2 * psi + 2 * psi + 12 * state_elems;
   *out = std::move(p);
   return ZERO_OK;

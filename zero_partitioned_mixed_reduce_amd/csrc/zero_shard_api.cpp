@@ -19,10 +19,10 @@
 
 namespace zs {
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
-                          int32_t dyn_slot, DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st);
+                          int32_t dyn_slot, DevScalars* sc, const IntakeParts& parts, hipStream_t st);
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
                          int32_t n_ranks, bool accumulate, bool r16, float inv, int32_t dyn_slot, float* red,
-                         DevScalars* sc, StatsPart* parts, int64_t grid_cap, hipStream_t st);
+                         DevScalars* sc, const IntakeParts& parts, hipStream_t st);
 hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
                              int32_t n_ranks, bool first, bool r16, float* red, int64_t grid_cap, hipStream_t st);
 struct AdamArgs;
@@ -34,6 +34,7 @@ hipError_t launch_init(int dtype, const Chunk* chunks, int64_t n_chunks, float* 
                        int64_t state_elems, const float* master_init, int64_t grid_cap, hipStream_t st);
 hipError_t launch_export(const Chunk* chunks, int64_t n_chunks, const float* src, float* dst, int64_t grid_cap,
                          hipStream_t st);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* chunks, int64_t n_chunks,
                             const uint16_t* flat_g, const float* red, float* master, float* m, float* v,
                             DevScalars* sc, int32_t slot, int32_t other_flag, double other_sumsq, float max_norm,
@@ -76,7 +77,7 @@ struct zero_shard {
   bool has_registered_grads;
   float *master, *m, *v, *red;
   zs::DevScalars* sc;
-  zs::StatsPart* parts;
+  zs::IntakeParts parts;       // partial sums of the intake passes (workspace)
   zs::Chunk* chunks;
   int64_t n_chunks;
   std::vector<int64_t> chunk_begin;  // logical shard offset of each chunk, plus the end
@@ -85,7 +86,7 @@ struct zero_shard {
   int64_t seg_per;                   // chunks per segment
   bool seg_tracked;                  // the latest write-back tracked the current segments
   hipEvent_t wb_event;               // recorded just before each tracked write-back launch
-  int64_t grid_stats, grid_main;
+  int64_t grid_main;
   Phase phase;
   bool cast_pending;
   bool accumulating;   // micro-steps summed into red since the last intake
@@ -196,7 +197,10 @@ zero_status_t shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t*
   h->red = bufs->red;
   char* ws = static_cast<char*>(bufs->workspace);
   h->sc = reinterpret_cast<zs::DevScalars*>(ws);
-  h->parts = reinterpret_cast<zs::StatsPart*>(ws + zs::kPartsOff);
+  const zs::IntakeLayout il = zs::intake_layout((int64_t)p.chunks.size());
+  h->parts.part = reinterpret_cast<uint64_t*>(ws + il.part_off);
+  h->parts.gcount = reinterpret_cast<zs::GroupCount*>(ws + il.gcount_off);
+  h->parts.gpart = reinterpret_cast<uint64_t*>(ws + il.gpart_off);
   h->chunks = reinterpret_cast<zs::Chunk*>(ws + zs::kChunksOff);
   h->n_chunks = (int64_t)p.chunks.size();
   h->seg = reinterpret_cast<zs::SegState*>(ws + zs::kSegOff);
@@ -208,8 +212,6 @@ zero_status_t shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t*
   for (size_t c = 0; c < p.chunks.size(); ++c) h->chunk_begin[c] = p.chunks[c].shard_off;
   h->chunk_begin[p.chunks.size()] = p.chunks.empty() ? 0 : p.chunks.back().shard_off + p.chunks.back().len;
   h->grid_main = (int64_t)cus * blocks_per_cu();
-  // statistics passes stay persistent: at most 8 resident blocks per CU (and the partial slots)
-  h->grid_stats = (int64_t)cus * 8 < zs::kMaxStatsBlocks ? (int64_t)cus * 8 : zs::kMaxStatsBlocks;
   h->phase = kReady;
   h->cast_pending = false;
   h->accumulating = false;
@@ -243,6 +245,13 @@ zero_status_t shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t*
         (e = hipMemcpyAsync(h->chunks, p.chunks.data(), p.chunks.size() * sizeof(zs::Chunk), hipMemcpyHostToDevice,
                             st)) != hipSuccess) {
       rs = hip_fail("hipMemcpyAsync(chunk table)", e);
+      break;
+    }
+    // the intake passes' group counters start at zero (and are re-armed by every pass)
+    const int64_t n_groups = (h->n_chunks + zs::kGroup - 1) / zs::kGroup;
+    if ((e = zs::launch_fill_zero(reinterpret_cast<float*>(h->parts.gcount),
+                                  n_groups * (int64_t)(sizeof(zs::GroupCount) / sizeof(float)), st)) != hipSuccess) {
+      rs = hip_fail("group counters", e);
       break;
     }
     if ((e = zs::launch_init(h->dtype, h->chunks, h->n_chunks, h->master, h->m, h->v, h->info.state_elems,
@@ -354,7 +363,7 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
       if (s != ZERO_OK) return s;
     }
     e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, true, h->reduce_out16,
-                          inv_loss_scale, dyn_slot, h->red, h->sc, h->parts, h->grid_stats, st);
+                          inv_loss_scale, dyn_slot, h->red, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
     h->grad_source = kGradRed;
     h->step_flat_g = nullptr;
@@ -363,16 +372,14 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     return fail(ZERO_ESTATE, "ZERO_ACCUMULATED without zero_accumulate_grads in this step");
   } else if (n_ranks == 0) {
     if (!h->has_registered_grads) return fail(ZERO_EINVAL, "n_ranks == 0 needs gradients registered at init");
-    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, nullptr, inv_loss_scale, dyn_slot, h->sc, h->parts,
-                           h->grid_stats, st);
+    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, nullptr, inv_loss_scale, dyn_slot, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("statistics kernel", e);
     h->grad_source = kGradChunk16;
     h->step_flat_g = nullptr;
   } else if (n_ranks == 1) {
     if (!rank_grads || !rank_grads[0]) return fail(ZERO_EINVAL, "rank_grads[0] is null");
     const uint16_t* g = static_cast<const uint16_t*>(rank_grads[0]);
-    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, g, inv_loss_scale, dyn_slot, h->sc, h->parts,
-                           h->grid_stats, st);
+    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, g, inv_loss_scale, dyn_slot, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("statistics kernel", e);
     h->grad_source = kGradFlat16;
     h->step_flat_g = g;
@@ -383,7 +390,7 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
       if (!rank_grads[q]) return fail(ZERO_EINVAL, "rank_grads[" + std::to_string(q) + "] is null");
     if (!h->red) return fail(ZERO_EINVAL, "reducing N_d >= 2 buffers needs bufs.red");
     e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, false, h->reduce_out16,
-                          inv_loss_scale, dyn_slot, h->red, h->sc, h->parts, h->grid_stats, st);
+                          inv_loss_scale, dyn_slot, h->red, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
     h->grad_source = h->reduce_out16 ? kGradRed16 : kGradRed;
     h->step_flat_g = nullptr;

@@ -15,12 +15,13 @@ namespace zs {
 #define ZS_CHUNK 8192
 #endif
 constexpr int64_t kChunk = ZS_CHUNK;
-// Per-block partial slots of the statistics pass (grid cap of that kernel).
-constexpr int kMaxStatsBlocks = 4096;
 // Local-reduce fan-in limit (rank pointers travel as kernel arguments).
 constexpr int kMaxRanks = 64;
 constexpr int kBlock = 256;
-static_assert(kMaxStatsBlocks % kBlock == 0, "partials are read kMaxStatsBlocks / kBlock per thread");
+// Blocks of an intake pass whose partial sums one group combines (a group's last
+// block adds them; the last group adds the group sums).
+constexpr int kGroup = 256;
+static_assert(kGroup == kBlock, "a group's partials are read one per thread");
 
 // One work item: a run of `len` consecutive shard elements inside one tensor.
 struct alignas(16) Chunk {
@@ -46,7 +47,7 @@ static_assert(sizeof(Slot) == 32, "slot layout");
 struct alignas(256) DevScalars {
   double local_sumsq;  // this rank's sum of u^2 (statistics pass)
   int32_t local_flag;  // this rank's non-finite flag
-  uint32_t counter;    // blocks finished in the statistics pass (reset by the last one)
+  uint32_t counter;    // groups of an intake pass that have completed (reset by the last one)
   Slot slot[2];        // step counters; zero_adam_step reads one and writes the other
   double norm;         // report of the last zero_adam_step
   float clip;
@@ -83,14 +84,37 @@ struct SegArgs {
   uint64_t epoch;      // number of this zero_adam_step call (1-based)
 };
 
-struct StatsPart {
-  uint64_t sumsq_bits;  // fp64 partial sum of squares of one block, as bits
-  uint64_t pad;
+// Completion counter of one group of intake blocks, on its own 64-byte line.
+struct alignas(64) GroupCount {
+  uint32_t count;  // blocks of the group that have stored their partial (re-armed by the last)
+};
+static_assert(sizeof(GroupCount) == 64, "group counter layout");
+
+// Where an intake pass leaves its partial sums of squares (fp64, as bits).
+struct IntakeParts {
+  uint64_t* part;      // one per block
+  GroupCount* gcount;  // one per group of kGroup blocks
+  uint64_t* gpart;     // one per group: the sum of its blocks' partials
 };
 
-constexpr int64_t kPartsOff = sizeof(DevScalars);
-constexpr int64_t kSegOff = kPartsOff + kMaxStatsBlocks * (int64_t)sizeof(StatsPart);
+constexpr int64_t kSegOff = sizeof(DevScalars);
 constexpr int64_t kChunksOff = kSegOff + kMaxSegments * (int64_t)sizeof(SegState);
+
+// Workspace after the chunk table: per-block partials, group counters and group
+// sums, sized for the largest intake grid (one block per chunk).
+struct IntakeLayout {
+  int64_t part_off, gcount_off, gpart_off, end;
+};
+inline IntakeLayout intake_layout(int64_t n_chunks) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  const int64_t n_groups = (n_chunks + kGroup - 1) / kGroup;
+  IntakeLayout l;
+  l.part_off = up(kChunksOff + n_chunks * (int64_t)sizeof(Chunk));
+  l.gcount_off = up(l.part_off + 8 * n_chunks);
+  l.gpart_off = up(l.gcount_off + n_groups * (int64_t)sizeof(GroupCount));
+  l.end = up(l.gpart_off + 8 * n_groups);
+  return l;
+}
 
 struct Piece {
   int64_t tensor, tensor_off, shard_off, state_off, len;
