@@ -117,11 +117,12 @@ def test_flat_prereduced_all_ranks(nd, psi):
         sim.compare()
 
 
-@pytest.mark.parametrize("nd", [2, 3, 8, 11])
+@pytest.mark.parametrize("nd", [2, 3, 8, 11, 64])
 def test_reduce_fan_in(nd):
-    """Local reduce with the specialised (2, 8) and the generic (3, 11) fan-ins."""
+    """Local reduce with the specialised (2, 8) and the generic (3, 11, and the maximum
+    64) fan-ins."""
     w = recipes.reduce8()
-    psi = 40_000 * nd + 13
+    psi = (40_000 if nd <= 11 else 4_000) * nd + 13
     w.tensors = [("flat", psi)]
     master, p16 = master_of(w, psi)
     sim = Sim(w.numel, nd, w.dtype, p16, master, "reduce", ranks=[0, nd - 1])
@@ -147,6 +148,42 @@ def test_ranks_without_elements_and_tiny_tensors():
     for step in range(1, 3):
         sim.step(grads_for(w, step, psi, 1), 1.0, 1.0, hp_of(w.hp))
         sim.compare()
+
+
+def test_empty_model():
+    """Every tensor empty (psi = 0): no elements anywhere, yet each step is a step --
+    zero norm, no overflow, t advances -- for every rank."""
+    numel = [0, 0, 0]
+    w = recipes.ragged_mini(3)
+    p16 = np.zeros(0, np.uint16)
+    sim = Sim(numel, 3, BF16, p16, None, "ragged", per_tensor_params=True)
+    assert [p[3] for p in sim.plans] == [0, 0, 0]
+    for step in range(1, 3):
+        res = sim.step([np.zeros(0, np.uint16)], 1.0, 1.0, hp_of(w.hp))
+        assert not any(x["skipped"] for x in res) and all(x["norm"] == 0.0 for x in res)
+        sim.compare()
+    assert all(st.counters.t == 2 for st in sim.ostates)
+
+
+@pytest.mark.parametrize("hp", [dict(lr=1e-3, beta1=0.0, beta2=0.0, eps=1e-8, weight_decay=0.0),
+                                dict(lr=0.0, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1),
+                                dict(lr=1e-2, beta1=0.5, beta2=0.5, eps=1e-3, weight_decay=0.5)])
+def test_degenerate_hyperparameters(hp):
+    """beta = 0 (m = g, v = g^2, no bias correction left), lr = 0 (nothing moves), and
+    large eps / weight decay, on the tiny workload's shapes (4 ranks, fp16, scale 1024)."""
+    w = recipes.tiny()
+    psi = 100_003
+    master, p16 = master_of(w, psi)
+    sim = Sim([psi], w.nd, w.dtype, p16, master, "reduce")
+    sim.p16_initial = p16.copy()
+    for step in range(1, 4):
+        sim.step(grads_for(w, step, psi, w.nd), 1.0 / w.loss_scale, w.max_norm, hp_of(hp))
+        sim.compare()
+    if hp["lr"] == 0.0:
+        for r in sim.ranks:
+            _, _, b, valid = sim.plans[r]
+            assert (sim.shards[r].export("master").cpu().numpy().view(np.uint32) ==
+                    master[b:b + valid].view(np.uint32)).all()
 
 
 @pytest.mark.parametrize("pmis,gmis", [((1, 3, 5, 7), (0,)), ((2,), (1,)), ((3,), (3,)), ((1, 2), (2, 1))])

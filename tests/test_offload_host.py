@@ -108,6 +108,7 @@ CASES = [
     ([100003], 7, F16),
     ([3 * 16384 + 17, 1], 2, BF16),
     ([130], 64, F16),
+    ([0, 0], 2, BF16),                           # no elements at all
 ]
 
 
@@ -119,12 +120,12 @@ def test_offload_steps_match_oracle(numel, nd, dtype):
     scale = 1024.0 if dtype == F16 else 1.0
     for step in range(1, 6):
         g = grads(sim.psi, dtype, seed, step, 1e-3 * scale)
-        if step == 2:
+        if step == 2 and sim.psi:
             g[sim.psi // 2] = 0x7C00 if dtype == F16 else 0x7F80
         res = sim.step(g, 1.0 / scale, 1.0)
-        assert all(x["skipped"] for x in res) == (step == 2)
+        assert all(x["skipped"] for x in res) == (step == 2 and sim.psi > 0)
         sim.compare()
-    assert all(o.counters.t == 4 for o in sim.ostates)
+    assert all(o.counters.t == (4 if sim.psi else 5) for o in sim.ostates)
     sim.close()
 
 
