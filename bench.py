@@ -53,6 +53,9 @@ def parse():
                    help="ZeRO-Offload: fp32 state in host memory, the step on the host cores, the gradient slice "
                         "copied to the host and the 16-bit slice back to the device (pre-reduced gradients only)")
     p.add_argument("--host-threads", type=int, default=0, help="with --offload: host worker threads (0: all)")
+    p.add_argument("--offload-host-stats", action="store_true",
+                   help="with --offload: the host computes the flag and sum of squares from the copied gradient "
+                        "(default: the device does, and the host update overlaps the copy)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1 << 26, help="elements of the oracle's timed sample")
     p.add_argument("--cpu-steps", type=int, default=7)
@@ -335,7 +338,7 @@ def bench_offload(a, w, rank):
     b, valid = info.shard_begin, info.valid_elems
     master = synth.normal_f32(valid, w.seed, mstream, b, w.master_sigma) if w.master_given else None
     h = ZeroOffload(w.numel, w.nd, rank, dt, params=params, grads=grads, master_init=master,
-                    num_threads=a.host_threads)
+                    num_threads=a.host_threads, device_stats=not a.offload_host_stats)
     del master
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
@@ -347,7 +350,7 @@ def bench_offload(a, w, rank):
 
     def step(times=None):
         t0 = time.perf_counter()
-        h.zero_offload_fetch_grads()
+        h.zero_offload_fetch_grads(inv)
         h.zero_offload_grad_stats(inv)
         t1 = time.perf_counter()
         h.zero_offload_adam_step(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], False, other,
@@ -375,10 +378,11 @@ def bench_offload(a, w, rank):
     # device-to-host rate on its own: the fetch alone, timed with events on its stream
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record()
-    h.zero_offload_fetch_grads()
+    h.zero_offload_fetch_grads(inv)
     ev[1].record()
-    h.zero_offload_grad_stats(inv)
+    ev[1].synchronize()
     d2h_ms = ev[0].elapsed_time(ev[1])
+    h.zero_offload_grad_stats(inv)
     h.zero_offload_adam_step(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], False, other,
                              w.max_norm, push=False)
     ev[0].record()
@@ -410,8 +414,10 @@ def bench_offload(a, w, rank):
                    "shard_params": valid, "param_grad_dtype": DTYPE_NAME[dt], "grad_source": w.grad_mode,
                    "tensors": len(w.numel), "loss_scale": w.loss_scale, "max_norm": w.max_norm,
                    "offload": "fp32 master/m/v on the host; host step; gradient to host, 16-bit slice to device",
-                   "host_threads": threads, "adam": w.hp},
-        "breakdown_ms": {"fetch_and_host_stats": stats_ms, "host_adam_cast_and_push": adam_ms,
+                   "host_threads": threads,
+                   "statistics": "host" if a.offload_host_stats else "device, overlapping the copy",
+                   "adam": w.hp},
+        "breakdown_ms": {"fetch_and_stats": stats_ms, "host_adam_cast_and_push": adam_ms,
                          "push_drain": drain_ms},
         "pcie": {"d2h_gbps": 2 * valid / (d2h_ms * 1e-3) / 1e9, "h2d_gbps": 2 * valid / (h2d_ms * 1e-3) / 1e9,
                  "d2h_ms": d2h_ms, "h2d_ms": h2d_ms, "bytes_each_way": 2 * valid,

@@ -16,12 +16,15 @@
  *     ZeRO-Offload, 异步调度策略).
  *
  * The host side is this library's own runtime: a pool of worker threads runs
- * AVX-512 loops over fixed tiles of the shard; the device-to-host copy of the
- * gradient slice proceeds in blocks that the statistics pass consumes as they
- * land, and the host-to-device copy of each block of updated 16-bit weights is
- * enqueued as soon as that block is written, overlapping the update of the
- * next one.  Results do not depend on the thread count: the sum of squares is
- * formed per tile and the tile sums are added in tile order.
+ * AVX-512 loops over fixed tiles of the shard.  The device-to-host copy of the
+ * gradient slice proceeds in blocks.  With a device workspace the step's flag
+ * and sum of squares come from the GPU, where the gradient already is, and the
+ * host update starts on each block as soon as it lands, overlapping the copy;
+ * without one, a host statistics pass consumes the blocks as they land and the
+ * update follows.  The host-to-device copy of each block of updated 16-bit
+ * weights is enqueued as soon as that block is written.  Host results do not
+ * depend on the thread count: the host sum of squares is formed per tile and
+ * the tile sums are added in tile order.
  *
  * Conventions as in zero_shard.h (zero_status_t returns, zero_last_error(),
  * caller-owned memory, int64 sizes), plus:
@@ -61,6 +64,11 @@ typedef struct {
   void* param16;   /* 16-bit parameter slice written by zero_offload_adam_step and copied    */
                    /* to the device from here                                                */
   int64_t capacity;/* elements of each array (>= valid_elems of the plan)                    */
+  void* workspace; /* optional device workspace of zero_shard_plan's workspace_bytes         */
+                   /* (256-byte aligned): the flag and sum of squares are then taken on the  */
+                   /* GPU while the gradient is copied, and the host update starts on each   */
+                   /* block as it lands; NULL: the host computes them from the copied slice  */
+  int64_t workspace_capacity; /* bytes of workspace                                          */
 } zero_offload_bufs_t;
 
 /* Builds the handle: partition as zero_shard_plan (same description, same
@@ -80,16 +88,24 @@ zero_status_t zero_offload_init(const zero_shard_desc_t* desc, const zero_offloa
 /* Enqueues on `stream` the device-to-host copy of this rank's already-reduced
  * 16-bit gradient slice into bufs.grad16, block by block, and returns without
  * waiting.  flat_grad16: a device [psi] flat gradient, or NULL for the
- * gradient registered at init (grad16 / flat_grad16).  The gradient must stay
- * unchanged until zero_offload_grad_stats returns.  EINVAL for a host-only
- * handle or without a source; ESTATE after zero_offload_grad_stats of the
- * same step. */
-zero_status_t zero_offload_fetch_grads(zero_offload_t h, const void* flat_grad16, void* stream);
+ * gradient registered at init (grad16 / flat_grad16).  With a device
+ * workspace, the step's flag and sum of squares of u = g * inv_loss_scale are
+ * first computed on the device, over the gradient in device memory, by the
+ * statistics kernel of zero_reduce_grads; pass the same inv_loss_scale to
+ * zero_offload_grad_stats.  The gradient must stay unchanged until the step's
+ * zero_offload_adam_step returns.  EINVAL for a host-only handle, without a
+ * source, or for an inv_loss_scale that is not finite and positive; ESTATE
+ * after zero_offload_grad_stats of the same step. */
+zero_status_t zero_offload_fetch_grads(zero_offload_t h, const void* flat_grad16, float inv_loss_scale,
+                                       void* stream);
 
-/* Host statistics of the step's gradient in bufs.grad16 (waiting for each
- * block of a pending fetch as it lands): u = g * inv_loss_scale (fp32),
- * found_inf = any u not finite, sumsq = sum of u*u in fp64.  Both outputs are
- * nullable.  EINVAL unless inv_loss_scale is finite and positive. */
+/* The step's statistics: u = g * inv_loss_scale (fp32), found_inf = any u not
+ * finite, sumsq = sum of u*u in fp64.  After a fetch on a handle with a device
+ * workspace they are the device's (this call waits for the statistics kernel
+ * only, not for the copies); otherwise the host computes them from
+ * bufs.grad16, waiting for each block of a pending fetch as it lands.  Both
+ * outputs are nullable.  EINVAL unless inv_loss_scale is finite and positive
+ * (and, after a device fetch, equal to the fetch's). */
 zero_status_t zero_offload_grad_stats(zero_offload_t h, float inv_loss_scale, int32_t* found_inf, double* sumsq);
 
 /* The optimizer step on the host cores.  skip = this rank's flag OR
@@ -108,7 +124,9 @@ zero_status_t zero_offload_grad_stats(zero_offload_t h, float inv_loss_scale, in
  * into the device parameters as soon as the block is updated.  Returns when
  * the update is done and every copy is enqueued.  Waits first for the copies
  * of the previous push, which read bufs.param16.  EINVAL on a null hparams
- * pointer or push on a host-only handle; ESTATE before zero_offload_grad_stats. */
+ * pointer or push on a host-only handle; ESTATE before zero_offload_grad_stats.
+ * A gradient copy still in flight is consumed block by block: each block is
+ * updated as soon as it lands. */
 zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t* hp, int32_t other_ranks_found_inf,
                                      double other_ranks_sumsq, float max_norm, int32_t push, void* stream);
 

@@ -40,7 +40,8 @@ def sumsq_tol(n):
 class OffloadSim:
     """Every rank's offload handle with its own copy of the device parameters."""
 
-    def __init__(self, numel, nd, dtype, p16_full, master_full, grad_mode, per_tensor, misalign=(0,)):
+    def __init__(self, numel, nd, dtype, p16_full, master_full, grad_mode, per_tensor, misalign=(0,),
+                 device_stats=True):
         self.numel, self.nd, self.dtype, self.grad_mode = list(numel), nd, dtype, grad_mode
         self.psi = sum(numel)
         self.p16_initial = p16_full.copy()
@@ -59,7 +60,8 @@ class OffloadSim:
             self.params.append((store, views))
             grads = {"ragged": self.gviews, "registered_flat": self.gstore}.get(grad_mode)
             self.handles.append(ZeroOffload(numel, nd, r, dtype, params=views if views is not None else store,
-                                            grads=grads, master_init=mst, num_threads=(0, 3, 5)[r % 3]))
+                                            grads=grads, master_init=mst, num_threads=(0, 3, 5)[r % 3],
+                                            device_stats=device_stats))
         torch.cuda.synchronize()
 
     def step(self, g_full, inv, max_norm, hp, fused_push=True):
@@ -74,7 +76,7 @@ class OffloadSim:
             self.gstore.copy_(src)
         loc = []
         for h in self.handles:
-            h.zero_offload_fetch_grads(src if self.grad_mode == "flat" else None)
+            h.zero_offload_fetch_grads(inv, src if self.grad_mode == "flat" else None)
             loc.append(h.zero_offload_grad_stats(inv))
         for r, h in enumerate(self.handles):
             other_flag = any(loc[q][0] for q in range(self.nd) if q != r)
@@ -90,7 +92,10 @@ class OffloadSim:
             valid = self.plans[r][3]
             assert loc[r][0] == res[r]["flag"] and q["skipped"] == res[r]["skipped"], (r, loc[r], q, res[r])
             if np.isfinite(res[r]["local_sumsq"]):
-                assert abs(loc[r][1] - res[r]["local_sumsq"]) <= sumsq_tol(valid) * max(res[r]["local_sumsq"], 1e-300)
+                # host statistics: two fp64 orders of the same terms; device statistics: within the
+                # device step's bound
+                tol = sumsq_tol(valid) if h.workspace is None else 1e-9
+                assert abs(loc[r][1] - res[r]["local_sumsq"]) <= tol * max(res[r]["local_sumsq"], 1e-300)
             if not q["skipped"]:
                 assert q["clip"] == res[r]["clip"]
             assert q["t"] == self.ostates[r].counters.t
@@ -114,22 +119,26 @@ class OffloadSim:
             h.close()
 
 
-@pytest.mark.parametrize("grad_mode,per_tensor,master_given,fused_push", [
-    ("ragged", True, True, True),
-    ("ragged", True, False, False),
-    ("registered_flat", False, True, True),
-    ("flat", False, False, True),
-    ("flat", True, True, False),
+@pytest.mark.parametrize("grad_mode,per_tensor,master_given,fused_push,device_stats", [
+    ("ragged", True, True, True, True),
+    ("ragged", True, False, False, True),
+    ("registered_flat", False, True, True, True),
+    ("flat", False, False, True, True),
+    ("flat", True, True, False, True),
+    ("ragged", True, True, True, False),
+    ("flat", False, False, False, False),
 ])
-def test_offload_device_copies_match_oracle(grad_mode, per_tensor, master_given, fused_push):
+def test_offload_device_copies_match_oracle(grad_mode, per_tensor, master_given, fused_push, device_stats):
     """The ragged mini list (4 layers, d 256, MLP 688, vocab 2000) at N_d = 3, bf16, 4 steps
-    with an inf in step 2; tensors sit at odd element offsets in device memory."""
+    with an inf in step 2; tensors sit at odd element offsets in device memory.  With device
+    statistics the host update consumes the gradient blocks as they land; without, the host
+    computes the statistics first."""
     w = recipes.ragged_mini(3)
     psi = w.psi
     master = synth.normal_f32(psi, w.seed, synth.stream_id(synth.MASTER), 0, w.master_sigma)
     p16 = synth.normal_16(psi, w.dtype, w.seed, synth.stream_id(synth.MASTER), 0, w.master_sigma)
     sim = OffloadSim(w.numel, w.nd, w.dtype, p16, master if master_given else None, grad_mode, per_tensor,
-                     misalign=(0, 1, 3, 6))
+                     misalign=(0, 1, 3, 6), device_stats=device_stats)
     if not master_given:
         for h, o in zip(sim.handles, sim.ostates):
             assert (h.host("master").view(np.uint32) == o.w.view(np.uint32)).all()
@@ -144,14 +153,15 @@ def test_offload_device_copies_match_oracle(grad_mode, per_tensor, master_given,
     sim.close()
 
 
-def test_offload_fp16_loss_scale_many_blocks():
+@pytest.mark.parametrize("device_stats", [True, False])
+def test_offload_fp16_loss_scale_many_blocks(device_stats):
     """fp16 with loss scale 1024 over several copy blocks (4M elements each) and a
     ragged tail, one rank of N_d = 2; the gradient slice is fetched from a flat buffer."""
     n, nd, dtype, seed = (1 << 22) * 2 + 12345, 2, F16, 0x5EED0700
     psi = n * nd - 100
     master = synth.normal_f32(psi, seed, synth.stream_id(synth.MASTER), 0, 0.02)
     p16 = synth.normal_16(psi, dtype, seed, synth.stream_id(synth.MASTER), 0, 0.02)
-    sim = OffloadSim([psi], nd, dtype, p16, master, "flat", False)
+    sim = OffloadSim([psi], nd, dtype, p16, master, "flat", False, device_stats=device_stats)
     hp = oracle.HParams(1e-3, 0.9, 0.999, 1e-8, 0.01)
     for step in (1, 2):
         g = synth.normal_16(psi, dtype, seed, synth.stream_id(synth.GRAD, 0, step), 0, 1e-3 * 1024)
@@ -180,11 +190,11 @@ def test_offload_gpt2_shard_full_size():
         gstream = synth.stream_id(synth.GRAD, 0, step)
         synth.gpu_normal_16(grads, w.dtype, w.seed, gstream, first=0, sigma=w.grad_sigma)
         torch.cuda.synchronize()
-        h.zero_offload_fetch_grads()
+        h.zero_offload_fetch_grads(1.0)
         flag, ss = h.zero_offload_grad_stats(1.0)
         g = synth.normal_16(valid, w.dtype, w.seed, gstream, b, w.grad_sigma)
         u, oflag, oss = oracle.grad_stats(w.dtype, [g], 1.0)
-        assert flag == oflag is False and abs(ss - oss) <= sumsq_tol(valid) * oss
+        assert flag == oflag is False and abs(ss - oss) <= 1e-9 * oss    # the device's statistics
         h.zero_offload_adam_step(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, False, other, w.max_norm,
                                  push=True)
         clip, _ = oracle.clip_coef(oss + other, w.max_norm)

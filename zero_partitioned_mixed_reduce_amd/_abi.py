@@ -43,7 +43,8 @@ class zero_loss_scaler_t(ctypes.Structure):
 
 class zero_offload_bufs_t(ctypes.Structure):
     _fields_ = [("master", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("grad16", ctypes.c_void_p), ("param16", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
+                ("grad16", ctypes.c_void_p), ("param16", ctypes.c_void_p), ("capacity", ctypes.c_int64),
+                ("workspace", ctypes.c_void_p), ("workspace_capacity", ctypes.c_int64)]
 
 
 class zero_adam_hparams_t(ctypes.Structure):
@@ -82,7 +83,7 @@ _PROTOS = {
     # offloaded (host) step, include/zero_offload.h
     "zero_offload_init": [ctypes.POINTER(zero_shard_desc_t), ctypes.POINTER(zero_offload_bufs_t), ctypes.c_void_p,
                           ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)],
-    "zero_offload_fetch_grads": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
+    "zero_offload_fetch_grads": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p],
     "zero_offload_grad_stats": [ctypes.c_void_p, ctypes.c_float, ctypes.POINTER(ctypes.c_int32),
                                 ctypes.POINTER(ctypes.c_double)],
     "zero_offload_adam_step": [ctypes.c_void_p, ctypes.POINTER(zero_adam_hparams_t), ctypes.c_int32, ctypes.c_double,
@@ -253,8 +254,8 @@ def zero_offload_init(desc, bufs, master_init_ptr, num_threads, stream):
     return h
 
 
-def zero_offload_fetch_grads(h, flat_grad16_ptr, stream):
-    _call("zero_offload_fetch_grads", h, flat_grad16_ptr, stream)
+def zero_offload_fetch_grads(h, flat_grad16_ptr, inv_loss_scale, stream):
+    _call("zero_offload_fetch_grads", h, flat_grad16_ptr, inv_loss_scale, stream)
 
 
 def zero_offload_grad_stats(h, inv_loss_scale):

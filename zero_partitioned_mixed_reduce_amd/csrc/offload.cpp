@@ -8,10 +8,15 @@
 //     copy blocks of kBlockTiles tiles, the unit of device<->host transfer;
 //   - a fixed pool of worker threads takes tiles in order from an atomic
 //     counter; each tile runs one AVX-512 loop (16 elements per instruction);
-//   - the statistics pass consumes copy blocks of the gradient as their
-//     device-to-host copies complete; the Adam pass hands each finished block
-//     to the calling thread, which enqueues its host-to-device copy while the
-//     workers go on with the next blocks;
+//   - with a device workspace, the flag and sum of squares are taken on the GPU
+//     (the statistics kernel of the device step, over the gradient still in
+//     HBM) while the gradient slice is copied to the host, and the Adam pass
+//     starts on each copy block as soon as it lands; without one, a host
+//     statistics pass consumes the blocks as they land and the Adam pass
+//     follows;
+//   - the Adam pass hands each finished block to the calling thread, which
+//     enqueues its host-to-device copy while the workers go on with the next
+//     blocks;
 //   - the per-element arithmetic is the step's fp32 sequence, every operation
 //     one IEEE binary32 operation rounded to nearest even (this file is built
 //     with -ffp-contract=off; division and square root are the correctly
@@ -26,6 +31,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cstddef>
 #include <cmath>
 #include <condition_variable>
 #include <functional>
@@ -267,6 +273,16 @@ struct zero_offload {
   std::vector<hipEvent_t> fetch_ev;  // one per copy block
   hipEvent_t push_ev;
   bool fetch_pending, push_pending, pushed;
+  // device statistics (optional workspace): scalar block, chunk table, partial sums
+  bool dev_stats;
+  zs::DevScalars* sc;
+  zs::Chunk* chunks;
+  int64_t n_chunks;
+  zs::IntakeParts parts;
+  hipStream_t aux;       // non-blocking stream that reads the statistics back
+  hipEvent_t stats_ev;   // recorded after the statistics kernel
+  bool stats_pending;
+  float stats_inv;
   Phase phase;
   // step state
   float inv;
@@ -384,6 +400,13 @@ zero_status_t offload_init(const zero_shard_desc_t* desc, const zero_offload_buf
   if (((uintptr_t)bufs->grad16 | (uintptr_t)bufs->param16) & 1u)
     return fail(ZERO_EINVAL, "16-bit host arrays must be 2-byte aligned");
   if (num_threads > kMaxThreads) return fail(ZERO_EINVAL, "num_threads must be at most 256");
+  if (bufs->workspace) {
+    if (!has_device) return fail(ZERO_EINVAL, "a device workspace needs device parameters");
+    if (((uintptr_t)bufs->workspace & 255u) != 0) return fail(ZERO_EINVAL, "workspace must be 256-byte aligned");
+    if (bufs->workspace_capacity < p.info.workspace_bytes)
+      return fail(ZERO_EINVAL, "workspace_capacity " + std::to_string(bufs->workspace_capacity) +
+                                   " < workspace_bytes " + std::to_string(p.info.workspace_bytes));
+  }
   int threads = num_threads > 0 ? num_threads : (int)std::thread::hardware_concurrency();
   if (threads < 1) threads = 1;
   if (threads > kMaxThreads) threads = kMaxThreads;
@@ -429,6 +452,14 @@ zero_status_t offload_init(const zero_shard_desc_t* desc, const zero_offload_buf
   h->norm = 0.0;
   h->clip = 1.0f;
   h->device = 0;
+  h->dev_stats = bufs->workspace != nullptr;
+  h->sc = nullptr;
+  h->chunks = nullptr;
+  h->n_chunks = (int64_t)p.chunks.size();
+  h->aux = nullptr;
+  h->stats_ev = nullptr;
+  h->stats_pending = false;
+  h->stats_inv = 0.0f;
 
   auto cleanup_events = [&]() {
     for (hipEvent_t e : h->fetch_ev)
@@ -436,6 +467,10 @@ zero_status_t offload_init(const zero_shard_desc_t* desc, const zero_offload_buf
     h->fetch_ev.clear();
     if (h->push_ev) (void)hipEventDestroy(h->push_ev);
     h->push_ev = nullptr;
+    if (h->stats_ev) (void)hipEventDestroy(h->stats_ev);
+    h->stats_ev = nullptr;
+    if (h->aux) (void)hipStreamDestroy(h->aux);
+    h->aux = nullptr;
   };
   if (has_device) {
     hipError_t e = hipGetDevice(&h->device);
@@ -449,6 +484,32 @@ zero_status_t offload_init(const zero_shard_desc_t* desc, const zero_offload_buf
     if ((e = hipEventCreateWithFlags(&h->push_ev, hipEventDisableTiming)) != hipSuccess) {
       cleanup_events();
       return hip_fail("hipEventCreateWithFlags", e);
+    }
+  }
+  if (h->dev_stats) {
+    // the device step's intake layout: scalar block, chunk table, group counters at zero
+    char* ws = static_cast<char*>(bufs->workspace);
+    const zs::IntakeLayout il = zs::intake_layout(h->n_chunks);
+    h->sc = reinterpret_cast<zs::DevScalars*>(ws);
+    h->chunks = reinterpret_cast<zs::Chunk*>(ws + zs::kChunksOff);
+    h->parts.part = reinterpret_cast<uint64_t*>(ws + il.part_off);
+    h->parts.gcount = reinterpret_cast<zs::GroupCount*>(ws + il.gcount_off);
+    h->parts.gpart = reinterpret_cast<uint64_t*>(ws + il.gpart_off);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    zs::DevScalars init_sc;
+    memset(&init_sc, 0, sizeof(init_sc));
+    const int64_t n_groups = (h->n_chunks + zs::kGroup - 1) / zs::kGroup;
+    hipError_t e;
+    if ((e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&h->stats_ev, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipMemcpyAsync(h->sc, &init_sc, sizeof(init_sc), hipMemcpyHostToDevice, st)) != hipSuccess ||
+        (h->n_chunks && (e = hipMemcpyAsync(h->chunks, p.chunks.data(), p.chunks.size() * sizeof(zs::Chunk),
+                                             hipMemcpyHostToDevice, st)) != hipSuccess) ||
+        (e = zs::launch_fill_zero(reinterpret_cast<float*>(h->parts.gcount),
+                                  n_groups * (int64_t)(sizeof(zs::GroupCount) / sizeof(float)), st)) != hipSuccess ||
+        (e = hipStreamSynchronize(st)) != hipSuccess) {
+      cleanup_events();
+      return hip_fail("device statistics set-up", e);
     }
   }
   h->pool.reset(new (std::nothrow) Pool(threads));
@@ -514,14 +575,26 @@ zero_status_t zero_offload_init(const zero_shard_desc_t* desc, const zero_offloa
   }
 }
 
-zero_status_t zero_offload_fetch_grads(zero_offload_t h, const void* flat_grad16, void* stream) {
+zero_status_t zero_offload_fetch_grads(zero_offload_t h, const void* flat_grad16, float inv_loss_scale,
+                                       void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
   if (!h->has_device) return fail(ZERO_EINVAL, "host-only handle: no device gradient to fetch");
   if (!flat_grad16 && !h->has_registered_grads)
     return fail(ZERO_EINVAL, "no flat_grad16 given and no gradient registered at init");
   if (h->phase == kStats) return fail(ZERO_ESTATE, "the gradient of this step was already taken in");
+  if (!(inv_loss_scale > 0.0f) || !std::isfinite(inv_loss_scale))
+    return fail(ZERO_EINVAL, "inv_loss_scale must be finite and positive");
   hipStream_t st = static_cast<hipStream_t>(stream);
   DeviceGuard dg(h->device, h->has_device);
+  if (h->dev_stats) {
+    // flag and sum of squares on the device, from the gradient still in HBM; the copies follow
+    hipError_t he = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, static_cast<const uint16_t*>(flat_grad16),
+                                       inv_loss_scale, -1, h->sc, h->parts, st);
+    if (he == hipSuccess) he = hipEventRecord(h->stats_ev, st);
+    if (he != hipSuccess) return hip_fail("device statistics", he);
+    h->stats_pending = true;
+    h->stats_inv = inv_loss_scale;
+  }
   const int64_t begin = h->info.shard_begin;
   for (int64_t k = 0; k < h->n_blocks; ++k) {
     zero_status_t s = for_block_pieces(h, k, [&](size_t p, int64_t a, int64_t e) -> zero_status_t {
@@ -544,6 +617,30 @@ zero_status_t zero_offload_grad_stats(zero_offload_t h, float inv_loss_scale, in
   if (!h) return fail(ZERO_EINVAL, "null handle");
   if (!(inv_loss_scale > 0.0f) || !std::isfinite(inv_loss_scale))
     return fail(ZERO_EINVAL, "inv_loss_scale must be finite and positive");
+  if (h->stats_pending) {
+    // the device computed them: read the two scalars back on the non-blocking stream, without
+    // waiting for the gradient copies, which the Adam pass consumes block by block
+    if (inv_loss_scale != h->stats_inv)
+      return fail(ZERO_EINVAL, "inv_loss_scale differs from the one given to zero_offload_fetch_grads");
+    DeviceGuard dg(h->device, h->has_device);
+    struct {
+      double sumsq;
+      int32_t flag;
+    } v;
+    static_assert(offsetof(zs::DevScalars, local_flag) == sizeof(double), "scalar block layout");
+    hipError_t e = hipStreamWaitEvent(h->aux, h->stats_ev, 0);
+    if (e == hipSuccess) e = hipMemcpyAsync(&v, h->sc, sizeof(double) + sizeof(int32_t), hipMemcpyDeviceToHost, h->aux);
+    if (e == hipSuccess) e = hipStreamSynchronize(h->aux);
+    if (e != hipSuccess) return hip_fail("reading the device statistics", e);
+    h->stats_pending = false;
+    h->inv = inv_loss_scale;
+    h->local_sumsq = v.sumsq;
+    h->local_flag = v.flag;
+    h->phase = kStats;
+    if (found_inf) *found_inf = h->local_flag;
+    if (sumsq) *sumsq = v.sumsq;
+    return ZERO_OK;
+  }
   std::atomic<int64_t> next{0};
   std::atomic<int64_t> landed{h->fetch_pending ? -1 : h->n_blocks};
   const int dt = h->dtype;
@@ -612,7 +709,17 @@ zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t
   h->skipped = skip;
   h->phase = kStepped;
   h->pushed = false;
-  if (skip) return ZERO_OK;
+  if (skip) {
+    // nothing is updated; let a gradient copy still in flight land before returning
+    if (h->fetch_pending) {
+      for (int64_t k = 0; k < h->n_blocks; ++k) {
+        hipError_t e = hipEventSynchronize(h->fetch_ev[k]);
+        if (e != hipSuccess && rs == ZERO_OK) rs = hip_fail("hipEventSynchronize(gradient copy)", e);
+      }
+      h->fetch_pending = false;
+    }
+    return rs;
+  }
   h->t += 1;
   h->p1 = h->p1 * (double)hp->beta1;
   h->p2 = h->p2 * (double)hp->beta2;
@@ -630,12 +737,16 @@ zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t
   s.wd = hp->weight_decay;
 
   std::atomic<int64_t> next{0};
+  // copy blocks of the gradient that have landed (all of them unless a fetch is still in flight)
+  std::atomic<int64_t> landed{h->fetch_pending ? -1 : h->n_blocks};
   for (int64_t k = 0; k < h->n_blocks; ++k) done[k].store(0, std::memory_order_relaxed);
   const int dt = h->dtype;
   h->pool->start([&](int) {
+    int spins = 0;
     for (;;) {
       const int64_t t = next.fetch_add(1, std::memory_order_relaxed);
       if (t >= h->n_tiles) break;
+      while (landed.load(std::memory_order_acquire) < t / kBlockTiles) spin_pause(spins);
       const int64_t o = t * kTile, n = tile_len(h, t);
       if (dt == ZERO_BF16) adam_tile<ZERO_BF16>(h->g16 + o, h->master + o, h->m + o, h->v + o, h->p16 + o, n, s);
       else adam_tile<ZERO_F16>(h->g16 + o, h->master + o, h->m + o, h->v + o, h->p16 + o, n, s);
@@ -643,13 +754,35 @@ zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t
     }
   });
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // the calling thread hands each finished block to the DMA engine
-  for (int64_t k = 0; k < h->n_blocks; ++k) {
-    const int64_t want = block_tiles(h, k);
-    int spins = 0;
-    while (done[k].load(std::memory_order_acquire) < want) spin_pause(spins);
-    if (push && rs == ZERO_OK) rs = enqueue_push_block(h, k, st);
+  // The calling thread releases each gradient block to the workers as its copy lands, and
+  // hands each finished block of the 16-bit slice to the DMA engine.
+  int64_t next_push = 0;
+  auto push_finished = [&](bool wait) {
+    while (next_push < h->n_blocks) {
+      const int64_t want = block_tiles(h, next_push);
+      if (done[next_push].load(std::memory_order_acquire) < want) {
+        if (!wait) return;
+        int spins = 0;
+        while (done[next_push].load(std::memory_order_acquire) < want) spin_pause(spins);
+      }
+      if (push && rs == ZERO_OK) rs = enqueue_push_block(h, next_push, st);
+      ++next_push;
+    }
+  };
+  if (h->fetch_pending) {
+    for (int64_t k = 0; k < h->n_blocks; ++k) {
+      hipError_t e = hipEventSynchronize(h->fetch_ev[k]);
+      if (e != hipSuccess) {
+        if (rs == ZERO_OK) rs = hip_fail("hipEventSynchronize(gradient copy)", e);
+        landed.store(h->n_blocks, std::memory_order_release);  // release the workers; the result is void
+        break;
+      }
+      landed.store(k, std::memory_order_release);
+      push_finished(false);
+    }
+    h->fetch_pending = false;
   }
+  push_finished(true);
   h->pool->wait();
   if (push && rs == ZERO_OK) {
     hipError_t e = hipEventRecord(h->push_ev, st);

@@ -23,10 +23,12 @@ class ZeroOffload:
     params=None for a host-only handle (then fill grad16 / param16 yourself).
     master_init: host fp32 tensor or array of the shard's valid elements, or None (then the
     master is the upcast of the shard's 16-bit parameters: read from the device, or, for a
-    host-only handle, taken from param16_init)."""
+    host-only handle, taken from param16_init).
+    device_stats: with device parameters, give the library a device workspace so the step's
+    flag and sum of squares are taken on the GPU and the host update overlaps the copy."""
 
     def __init__(self, numel, dp_size, dp_rank, dtype, params=None, grads=None, master_init=None, num_threads=0,
-                 param16_init=None):
+                 param16_init=None, device_stats=True):
         self.dtype = dtype
         self.host_only = params is None
         if self.host_only:
@@ -48,6 +50,11 @@ class ZeroOffload:
         b.master, b.m, b.v = self.master.data_ptr(), self.m.data_ptr(), self.v.data_ptr()
         b.grad16, b.param16 = self.grad16.data_ptr(), self.param16.data_ptr()
         b.capacity = n
+        self.workspace = None
+        if device_stats and not self.host_only:
+            self.workspace = torch.empty(self.info.workspace_bytes, dtype=torch.uint8, device="cuda")
+            b.workspace = self.workspace.data_ptr()
+            b.workspace_capacity = self.info.workspace_bytes
         self.bufs = b
         if param16_init is not None:
             self.host16("param16")[:] = np.asarray(param16_init, dtype=np.uint16)
@@ -71,8 +78,9 @@ class ZeroOffload:
         return t[:self.info.valid_elems].numpy().view(np.uint16)
 
     # step calls (same names as the C ABI)
-    def zero_offload_fetch_grads(self, flat_grad=None):
-        abi.zero_offload_fetch_grads(self.h, flat_grad.data_ptr() if flat_grad is not None else None, _stream())
+    def zero_offload_fetch_grads(self, inv_loss_scale=1.0, flat_grad=None):
+        abi.zero_offload_fetch_grads(self.h, flat_grad.data_ptr() if flat_grad is not None else None,
+                                     inv_loss_scale, _stream())
 
     def zero_offload_grad_stats(self, inv_loss_scale):
         return abi.zero_offload_grad_stats(self.h, inv_loss_scale)
