@@ -59,6 +59,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1 << 26, help="elements of the oracle's timed sample")
     p.add_argument("--cpu-steps", type=int, default=7)
+    p.add_argument("--cpu-threads", type=int, default=16,
+                   help="threads of the threaded oracle baseline (at most the usable CPUs)")
+    p.add_argument("--no-copy-ceiling", action="store_true",
+                   help="skip the device-to-device copy measurement after the timed steps")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one 1 GiB read + 1 GiB write elementwise kernel first (scales the traffic counters)")
     return p.parse_args()
@@ -208,36 +212,114 @@ def bytes_per_param(w, micro_steps=1, reduce_out16=False):
     return step, 4 + 12 + 12 + 2
 
 
-def cpu_baseline(w, sample, steps):
-    """The oracle, single-threaded, on the first `sample` elements of the workload's
-    gradient and state (pre-reduced or N_d-way reduce, as configured)."""
+def cpu_baseline(w, sample, steps, threads=1, piece=1 << 20, keep=False):
+    """The oracle on the first `sample` elements of the workload's gradient and state
+    (pre-reduced or N_d-way reduce, as configured), `steps` steps of statistics, clip,
+    Adam and cast.  Returns (elements per second, seconds[, final state if keep]).
+
+    threads == 1: the oracle's whole-array calls, single-threaded.  threads > 1: the
+    oracle's own functions called from that many threads over consecutive pieces of
+    `piece` elements (ctypes releases the interpreter lock for the duration of each
+    call).  Per step: the statistics of every piece, their sums of squares added in
+    piece order, the clip, the step's bias-correction scalars and one advance of the
+    counters (an Adam call over no elements), then Adam with those scalars and the
+    cast, per piece."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
     import synth
     n = sample
-    gs = []
     if w.grad_mode == "reduce":
-        for q in range(w.nd):
-            gs.append(synth.normal_16(n, w.dtype, w.seed, synth.stream_id(synth.GRAD, q, 0), 0, w.grad_sigma,
-                                      w.seed, w.zero_mod))
+        gs = [synth.normal_16(n, w.dtype, w.seed, synth.stream_id(synth.GRAD, q, 0), 0, w.grad_sigma, w.seed,
+                              w.zero_mod) for q in range(w.nd)]
     else:
-        gs.append(synth.normal_16(n, w.dtype, w.seed, synth.stream_id(synth.GRAD, 0, 0), 0, w.grad_sigma))
+        gs = [synth.normal_16(n, w.dtype, w.seed, synth.stream_id(synth.GRAD, 0, 0), 0, w.grad_sigma)]
     st = oracle.RankState(w.dtype, synth.normal_16(n, w.dtype, w.seed, synth.stream_id(synth.MASTER), 0,
                                                    w.master_sigma),
                           synth.normal_f32(n, w.seed, synth.stream_id(synth.MASTER), 0, w.master_sigma))
     hp = oracle.HParams(w.hp["lr"], w.hp["beta1"], w.hp["beta2"], w.hp["eps"], w.hp["weight_decay"])
     inv = 1.0 / w.loss_scale
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        u, flag, ss = oracle.grad_stats(w.dtype, gs, inv)
-        clip, _ = oracle.clip_coef(ss, w.max_norm)
-        oracle.adam(flag, u, clip, hp, st.counters, st.w, st.m, st.v)
-        if not flag:
-            oracle.cast(w.dtype, st.w, st.p16)
-    dt = time.perf_counter() - t0
+    if threads <= 1:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            u, flag, ss = oracle.grad_stats(w.dtype, gs, inv)
+            clip, _ = oracle.clip_coef(ss, w.max_norm)
+            oracle.adam(flag, u, clip, hp, st.counters, st.w, st.m, st.v)
+            if not flag:
+                oracle.cast(w.dtype, st.w, st.p16)
+        dt = time.perf_counter() - t0
+    else:
+        spans = [(lo, min(lo + piece, n)) for lo in range(0, n, piece)]
+        none = np.empty(0, np.float32)
+        with ThreadPoolExecutor(threads) as ex:
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                stats = list(ex.map(lambda sp: oracle.grad_stats(w.dtype, [g[sp[0]:sp[1]] for g in gs], inv), spans))
+                flag = any(x[1] for x in stats)
+                ss = 0.0
+                for x in stats:
+                    ss = ss + x[2]
+                clip, _ = oracle.clip_coef(ss, w.max_norm)
+                if flag:
+                    continue
+                bc1, bc2 = oracle.next_scalars(hp, st.counters)
+                oracle.adam(False, none, clip, hp, st.counters, none, none, none)
+
+                def update(k, clip=clip, bc1=bc1, bc2=bc2, stats=stats):
+                    lo, hi = spans[k]
+                    oracle.adam_elems(stats[k][0], clip, hp, bc1, bc2, st.w[lo:hi], st.m[lo:hi], st.v[lo:hi])
+                    oracle.cast(w.dtype, st.w[lo:hi], st.p16[lo:hi])
+
+                list(ex.map(update, range(len(spans))))
+            dt = time.perf_counter() - t0
     assert np.isfinite(st.w).all()
-    return n * steps / dt, dt
+    return (n * steps / dt, dt, st) if keep else (n * steps / dt, dt)
+
+
+def host_info():
+    """The host the benchmark ran on: logical CPUs, those this process may use, the CPU
+    model and the memory size."""
+    model, mem_kib = None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    mem_kib = int(line.split()[1])
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)), "cpu_model": model,
+            "mem_gib": None if mem_kib is None else round(mem_kib / 2 ** 20, 1)}
+
+
+def copy_ceiling(nbytes=4 << 30, reps=5):
+    """Measured device-to-device copy rates on this GPU over nbytes: the runtime's
+    memcpy (torch copy_) and a plain elementwise kernel (torch.mul by 1), best of
+    `reps`, bytes read + written per second."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = {"memcpy": 0.0, "elementwise": 0.0}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for _ in range(reps):
+        ev[0].record()
+        dst.copy_(src)
+        ev[1].record()
+        torch.mul(src, 1.0, out=dst)
+        ev[2].record()
+        ev[2].synchronize()
+        best["memcpy"] = max(best["memcpy"], 2 * nbytes / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9)
+        best["elementwise"] = max(best["elementwise"], 2 * nbytes / (ev[1].elapsed_time(ev[2]) * 1e-3) / 1e9)
+    del src, dst
+    torch.cuda.empty_cache()
+    return best
 
 
 def traffic_from_profiles(cfg, rank, adam_launch_bytes):
@@ -432,12 +514,18 @@ def bench_offload(a, w, rank):
                      "host_probes_gbps": probes},
         "setup_s": setup_s,
     }
+    out["host"] = host_info()
     if not a.no_cpu_baseline:
         n = min(a.cpu_sample, valid)
         rate, secs = cpu_baseline(w, n, a.cpu_steps)
         out["cpu_baseline"] = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
                                "sample": f"first {n} elements of the shard's workload, {a.cpu_steps} steps "
                                          f"(statistics, clip, Adam, cast), {secs:.1f} s single-threaded"}
+        threads = max(1, min(out["host"]["usable_cpus"], a.cpu_threads))
+        rate, secs = cpu_baseline(w, n, a.cpu_steps, threads)
+        out["cpu_baseline_threaded"] = {"value": rate, "unit": "params/s", "cores": threads,
+                                        "kind": "oracle, threaded over 1M-element pieces",
+                                        "sample": f"the same {n} elements and {a.cpu_steps} steps, {secs:.1f} s"}
     print(json.dumps(out), flush=True)
 
 
@@ -539,12 +627,26 @@ def main():
         if a.segment_consumer != "none":
             out["pipeline"]["first_segment_ready_ms"] = sum(e[1].elapsed_time(e[3]) for e in evs) / a.steps
             out["pipeline"]["last_segment_done_ms"] = sum(e[1].elapsed_time(e[4]) for e in evs) / a.steps
+    if not a.no_copy_ceiling:
+        del wl
+        torch.cuda.empty_cache()
+        cc = copy_ceiling()
+        top = max(cc.values())
+        out["copy_ceiling"] = {"unit": "GB/s", "bytes": 4 << 30, "memcpy_d2d": cc["memcpy"],
+                               "elementwise_copy": cc["elementwise"],
+                               "adam_frac_of_copy": achieved / top, "step_frac_of_copy": out["hbm_gbps_step"] / top}
+    out["host"] = host_info()
     if not a.no_cpu_baseline:
         n = min(a.cpu_sample, valid)
         rate, secs = cpu_baseline(w, n, a.cpu_steps)
         out["cpu_baseline"] = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
                                "sample": f"first {n} elements of the shard's workload, {a.cpu_steps} steps "
                                          f"(statistics, clip, Adam, cast), {secs:.1f} s single-threaded"}
+        threads = max(1, min(out["host"]["usable_cpus"], a.cpu_threads))
+        rate, secs = cpu_baseline(w, n, a.cpu_steps, threads)
+        out["cpu_baseline_threaded"] = {"value": rate, "unit": "params/s", "cores": threads,
+                                        "kind": "oracle, threaded over 1M-element pieces",
+                                        "sample": f"the same {n} elements and {a.cpu_steps} steps, {secs:.1f} s"}
     print(json.dumps(out), flush=True)
 
 

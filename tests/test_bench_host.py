@@ -35,3 +35,24 @@ def test_traffic_summary_is_tied_to_the_kernel_source():
     # a committed summary is only used for the shard size it was taken on
     assert bench.traffic_from_profiles("full7p5b", 0, 1) is None
     assert bench.traffic_from_profiles("no_such_config", 0, 1) is None
+
+
+def test_threaded_oracle_baseline_runs_the_same_step():
+    """The threaded oracle baseline performs the same step as the single-threaded one:
+    after three steps of a pre-reduced and of an 8-way reduce workload (a ragged last
+    piece, no clipping at these sizes) the master, moments and 16-bit slice agree bit
+    for bit, and the counters match."""
+    import numpy as np
+    for w in (recipes.full7p5b(), recipes.reduce8()):
+        n = (1 << 18) + 1234
+        _, _, a = bench.cpu_baseline(w, n, 3, keep=True)
+        _, _, b = bench.cpu_baseline(w, n, 3, threads=4, piece=1 << 16, keep=True)
+        for name in ("w", "m", "v"):
+            assert (getattr(a, name).view(np.uint32) == getattr(b, name).view(np.uint32)).all(), name
+        assert (a.p16 == b.p16).all()
+        assert a.counters.t == b.counters.t == 3 and a.counters.p1 == b.counters.p1
+
+
+def test_host_info_fields():
+    h = bench.host_info()
+    assert h["nproc"] >= 1 and 1 <= h["usable_cpus"] <= h["nproc"]

@@ -27,6 +27,7 @@
 //   ZS_STATS_SMALL  a statistics pass over fewer chunks than this takes ZS_STATS_SMALL_CPB
 //                   consecutive chunks per block (else one); the reduce passes take one
 //   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
+//   ZS_REDUCE_NT non-temporal loads of the local reduce's and accumulation's sources
 //   ZS_STATS_PF request the next chunk's table entry before streaming the current chunk
 //               (persistent statistics and reduce passes)
 //   ZS_NT_LOAD  non-temporal loads of the fp32 state (read once per step)
@@ -53,6 +54,9 @@
 #endif
 #ifndef ZS_REDUCE_U
 #define ZS_REDUCE_U 2
+#endif
+#ifndef ZS_REDUCE_NT
+#define ZS_REDUCE_NT 1
 #endif
 #ifndef ZS_STATS_PF
 #define ZS_STATS_PF 1
@@ -120,6 +124,16 @@ __device__ __forceinline__ u32x2 enc16x4(f32x4 w) {
 __device__ __forceinline__ u32x2 ld16x4(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ u32x2 ld16x4_stats(const uint16_t* p) {
 #if ZS_STATS_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+#else
+  return *reinterpret_cast<const u32x2*>(p);
+#endif
+}
+// Vector loads of the sources of a local reduce or accumulation.  Each element is
+// read once per step (the Adam pass reads the reduce's output instead), so they
+// are marked non-temporal.
+__device__ __forceinline__ u32x2 ld16x4_src(const uint16_t* p) {
+#if ZS_REDUCE_NT
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 #else
   return *reinterpret_cast<const u32x2*>(p);
@@ -442,7 +456,7 @@ struct GradSum {
 #pragma unroll
       for (int q = 0; q < NR; ++q)
 #pragma unroll
-        for (int k = 0; k < U; ++k) raw[q][k] = ld16x4(src(q) + j + k * stride);
+        for (int k = 0; k < U; ++k) raw[q][k] = ld16x4_src(src(q) + j + k * stride);
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         s[k] = dec16x4<DT>(raw[0][k]);
@@ -451,11 +465,11 @@ struct GradSum {
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < U; ++k) s[k] = dec16x4<DT>(ld16x4(src(0) + j + k * stride));
+      for (int k = 0; k < U; ++k) s[k] = dec16x4<DT>(ld16x4_src(src(0) + j + k * stride));
       if constexpr (NR != kSrcChunk)
         for (int q = 1; q < nranks(); ++q)
 #pragma unroll
-          for (int k = 0; k < U; ++k) s[k] = s[k] + dec16x4<DT>(ld16x4(src(q) + j + k * stride));
+          for (int k = 0; k < U; ++k) s[k] = s[k] + dec16x4<DT>(ld16x4_src(src(q) + j + k * stride));
     }
   }
   // leading elements to peel, and co-alignment of every source with the fp32 buffer after them
