@@ -103,4 +103,15 @@ def ragged_mini(nd=3):
                     grad_sigma=1e-4, loss_scale=1.0, hp=dict(PAGE_ADAM, weight_decay=0.1), steps=3)
 
 
+def big_tensor():
+    """A parity case: one tensor of more than 2^31 elements between two small ones, at
+    N_d = 1, so element offsets inside a tensor pass the 32-bit range; fp16 with a loss
+    scale, the master taken from the 16-bit parameters, and a gradient norm well above
+    max_norm (clipping active)."""
+    return Workload("big_tensor_nd1", 7, [("head", 4099), ("big", (1 << 31) + 12345), ("tail", 77)], nd=1,
+                    ranks=[0], dtype=F16, grad_mode="ragged", param_mode="ragged", grad_sigma=1e-3 * 1024,
+                    loss_scale=1024.0, master_given=False, hp=dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                                                                   weight_decay=0.01))
+
+
 ALL = {"tiny": tiny, "gpt2": gpt2_shard, "zero1_7p5b": zero1_7p5b, "reduce8": reduce8, "full7p5b": full7p5b}

@@ -82,6 +82,11 @@ def sample_positions(info, pieces, rng):
     for (_, _, soff, _, ln) in pieces:
         for edge in (soff, soff + ln):
             S.append(np.arange(max(0, edge - 64), min(valid, edge + 64)))
+    # inside a tensor piece, around element offsets 2^31 and 2^32 from its start
+    for (_, _, soff, _, ln) in pieces:
+        for big in (1 << 31, 1 << 32):
+            if ln > big:
+                S.append(np.arange(soff + big - 64, soff + big + 64))
     # chunk boundaries (multiples of 4096 from a piece start, shifted by < 8 for alignment): 4000 of them
     starts = np.array([p[2] for p in pieces], np.int64)
     lens = np.array([p[4] for p in pieces], np.int64)
@@ -116,10 +121,11 @@ def gpu_params_at(wl, flat_idx):
 @pytest.mark.parametrize("cfg,rank,micro,r16", [
     ("zero1_7p5b", 0, 1, False), ("zero1_7p5b", 63, 1, False), ("gpt2", 7, 1, False), ("gpt2", 3, 1, False),
     ("reduce8", 7, 1, False), ("reduce8", 0, 1, False), ("full7p5b", 0, 1, False),
-    ("reduce8", 7, 3, False), ("zero1_7p5b", 0, 2, False), ("reduce8", 7, 1, True), ("reduce8", 0, 2, True)])
+    ("reduce8", 7, 3, False), ("zero1_7p5b", 0, 2, False), ("reduce8", 7, 1, True), ("reduce8", 0, 2, True),
+    ("big_tensor", 0, 1, False)])
 def test_full_size_sampled(cfg, rank, micro, r16):
     import bench
-    w = recipes.ALL[cfg]()
+    w = recipes.ALL[cfg]() if cfg in recipes.ALL else getattr(recipes, cfg)()
     print(f"\n[fullsize] {cfg} rank {rank} micro-steps {micro} 16-bit reduce output {r16}: setting up", flush=True)
     wl = bench.Workload(w, rank, micro, reduce_out16=r16)
     info = wl.info
@@ -152,12 +158,11 @@ def test_full_size_sampled(cfg, rank, micro, r16):
     vv = np.zeros_like(wv)
     hp = oracle.HParams(w.hp["lr"], w.hp["beta1"], w.hp["beta2"], w.hp["eps"], w.hp["weight_decay"])
     ctr = oracle.Counters.fresh()
+    none = np.empty(0, np.float32)
     for _ in range(2):
         bc1, bc2 = oracle.next_scalars(hp, ctr)
         oracle.adam_elems(u, clip, hp, bc1, bc2, wv, mv, vv)
-        ctr.t += 1
-        ctr.p1 *= float(np.float32(hp.beta1))
-        ctr.p2 *= float(np.float32(hp.beta2))
+        oracle.adam(False, none, clip, hp, ctr, none, none, none)     # advances the counters
     p16 = oracle.encode16(w.dtype, wv)
 
     sidx = torch.from_numpy(state_index(pieces, pos)).cuda()

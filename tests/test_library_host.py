@@ -73,7 +73,8 @@ def desc_for(numel, nd, r, dtype=_abi.ZERO_F16, base=1 << 20, per_tensor=False, 
     return d
 
 
-CASES = [[1 << 20], [5], [0, 3], [1000, 0, 37, 1], [123457, 99, 640001], [64 * 64 * 3 + 1]]
+CASES = [[1 << 20], [5], [0, 3], [1000, 0, 37, 1], [123457, 99, 640001], [64 * 64 * 3 + 1],
+         [4099, (1 << 31) + 12345, 77]]
 
 
 @pytest.mark.parametrize("numel", CASES)
