@@ -81,7 +81,8 @@ typedef struct {
  * device into bufs.param16 on `stream` (synchronised), or, for a host-only
  * handle, as the caller left them in bufs.param16.  num_threads <= 0 uses the
  * host's hardware concurrency; at most 256.  EINVAL on a bad description,
- * null buffers, a capacity below valid_elems, or a host without AVX-512. */
+ * null buffers, a capacity below valid_elems, or a host without AVX-512;
+ * ENOMEM when host memory or the worker threads cannot be obtained. */
 zero_status_t zero_offload_init(const zero_shard_desc_t* desc, const zero_offload_bufs_t* bufs,
                                 const float* master_init, int32_t num_threads, void* stream, zero_offload_t* out);
 

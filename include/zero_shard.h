@@ -48,6 +48,7 @@ extern "C" {
 typedef enum {
   ZERO_OK = 0,
   ZERO_EINVAL = -1, /* bad argument: null pointer, size, dtype, alignment, rank count */
+  ZERO_ENOMEM = -2, /* host memory or worker threads could not be obtained           */
   ZERO_EHIP = -3,   /* a HIP runtime call failed (message names it)                  */
   ZERO_ESTATE = -4  /* call out of the step order                                    */
 } zero_status_t;
@@ -111,7 +112,8 @@ typedef struct {
  * 基本流程 with start = partition size * rank as in "ZeRO 技术原理" 3.3.1.
  * The fp32 state is laid out in tensor pieces, each placed so that it has the
  * same 16-byte alignment as its 16-bit parameters (a few padding floats per
- * piece), hence state_elems >= valid_elems.  EINVAL on a bad description. */
+ * piece), hence state_elems >= valid_elems.  EINVAL on a bad description;
+ * ENOMEM when the host tables do not fit in host memory. */
 zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* out);
 
 /* Builds the handle: copies the work table into the workspace, zeroes the
@@ -120,7 +122,8 @@ zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* 
  * value of this shard's 16-bit parameters (the partition_fp16.copy().float()
  * of "DeepSpeed ZeRO" ZeRO Stage 1); m = v = 0 and no step applied yet.
  * Synchronises the stream before returning.  EINVAL on a bad description,
- * null or misaligned buffers, or capacities below zero_shard_plan's sizes. */
+ * null or misaligned buffers, or capacities below zero_shard_plan's sizes;
+ * ENOMEM when the handle's host tables cannot be allocated. */
 zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
                               const float* master_init, void* stream, zero_shard_t* out);
 
@@ -214,7 +217,8 @@ zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grad
  * already and are taken in unchanged.  out_16bit = 0 (the default) keeps the
  * fp32 sum.  Between steps only (ESTATE otherwise, also while micro-steps are
  * accumulated); EINVAL unless out_16bit is 0 or 1, or for 1 without bufs.red.
- * After a 16-bit intake, zero_export_state of red (3) returns ESTATE. */
+ * While bufs.red holds a 16-bit intake (until the next micro-step or intake),
+ * zero_export_state of red (3) returns ESTATE. */
 zero_status_t zero_set_reduce_output(zero_shard_t h, int32_t out_16bit);
 
 /* n_ranks value for zero_reduce_grads: no new gradient, use the accumulated one. */
@@ -299,7 +303,8 @@ zero_status_t zero_shard_query(zero_shard_t h, int64_t* t, int32_t* last_skipped
                                float* last_clip, void* stream);
 
 /* Copies state buffer `which` (0 master, 1 m, 2 v, 3 red) of this shard into
- * dst (device fp32 [valid_elems]) in logical order. */
+ * dst (device fp32 [valid_elems]) in logical order.  ESTATE for red while it
+ * holds a 16-bit intake (zero_set_reduce_output). */
 zero_status_t zero_export_state(zero_shard_t h, int32_t which, float* dst, void* stream);
 
 /* Frees the host handle (never caller memory). */

@@ -207,3 +207,26 @@ def test_offload_gpt2_shard_full_size():
         dev = host16(params)
         assert (dev[b:b + valid] == st.p16).all()
     h.close()
+
+
+def test_offload_destroy_mid_step():
+    """Handles destroyed with work still pending -- a gradient fetch in flight with its
+    device statistics unread, or statistics read but no update -- release their events
+    and streams cleanly, many times over, and a new handle then steps normally."""
+    w = recipes.ragged_mini(2)
+    psi = w.psi
+    p16 = synth.normal_16(psi, w.dtype, w.seed, synth.stream_id(synth.MASTER), 0, w.master_sigma)
+    params = dev16(p16)
+    g = dev16(synth.normal_16(psi, w.dtype, w.seed, synth.stream_id(synth.GRAD, 0, 1), 0, w.grad_sigma))
+    for k in range(40):
+        h = ZeroOffload(w.numel, 2, k % 2, w.dtype, params=params, num_threads=2)
+        h.zero_offload_fetch_grads(1.0, g)
+        if k % 3 == 1:
+            h.zero_offload_grad_stats(1.0)
+        h.close()
+    sim = OffloadSim(w.numel, 2, w.dtype, p16, None, "flat", False)
+    hp = hp_of(w.hp)
+    sim.step(synth.normal_16(psi, w.dtype, w.seed, synth.stream_id(synth.GRAD, 0, 1), 0, w.grad_sigma), 1.0,
+             w.max_norm, hp)
+    sim.compare()
+    sim.close()

@@ -657,7 +657,8 @@ def test_reduce16_api():
     psi = 4096
     w = recipes.tiny()
     _, p16 = master_of(w, psi)
-    g = [dev16(x) for x in grads_for(w, 1, psi, 2)]
+    gh = grads_for(w, 1, psi, 2)
+    g = [dev16(x) for x in gh]
     s = ZeroShard([psi], 2, 0, F16, dev16(p16))
     with pytest.raises(ZeroError) as e:
         s.zero_set_reduce_output(True)                  # no bufs.red
@@ -681,6 +682,14 @@ def test_reduce16_api():
     with pytest.raises(ZeroError) as e:
         s.export("red")                                 # red now holds the 16-bit result
     assert e.value.status == ZERO_ESTATE
+    s.zero_check_overflow(False)
+    s.zero_grad_norm(0.0, 1.0)
+    s.zero_adam_step(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    s.zero_accumulate_grads(g)                          # red holds an fp32 accumulator again
+    acc = s.export("red").cpu().numpy()
+    exp = oracle.decode16(F16, oracle.reduce_to16(F16, [x[:psi // 2] for x in gh]))
+    assert (acc.view(np.uint32) == exp.view(np.uint32)).all()
+    s.zero_reduce_grads(g, 1.0)
     s.zero_check_overflow(False)
     s.zero_grad_norm(0.0, 1.0)
     s.zero_adam_step(1e-3, 0.9, 0.999, 1e-8, 0.0)

@@ -6,7 +6,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libzero_shard.so")
 
-ZERO_OK, ZERO_EINVAL, ZERO_EHIP, ZERO_ESTATE = 0, -1, -3, -4
+ZERO_OK, ZERO_EINVAL, ZERO_ENOMEM, ZERO_EHIP, ZERO_ESTATE = 0, -1, -2, -3, -4
 ZERO_F16, ZERO_BF16 = 1, 2
 ZERO_ACCUMULATED = -1
 ZERO_DEVICE_LOSS_SCALE = 0.0

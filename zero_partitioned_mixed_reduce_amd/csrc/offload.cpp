@@ -71,18 +71,16 @@ bool host_has_avx512() {
 
 class Pool {
  public:
+  // Throws when a thread cannot be started, after stopping the ones already running.
   explicit Pool(int n) : n_(n) {
-    for (int i = 0; i < n; ++i) threads_.emplace_back([this, i] { loop(i); });
-  }
-  ~Pool() {
-    {
-      std::lock_guard<std::mutex> l(mu_);
-      stop_ = true;
-      ++gen_;
+    try {
+      for (int i = 0; i < n; ++i) threads_.emplace_back([this, i] { loop(i); });
+    } catch (...) {
+      stop_all();
+      throw;
     }
-    wake_.notify_all();
-    for (auto& t : threads_) t.join();
   }
+  ~Pool() { stop_all(); }
   int size() const { return n_; }
   // Runs fn(worker) once on every worker; wait() returns when all have returned.
   void start(std::function<void(int)> fn) {
@@ -104,6 +102,15 @@ class Pool {
   }
 
  private:
+  void stop_all() {
+    {
+      std::lock_guard<std::mutex> l(mu_);
+      stop_ = true;
+      ++gen_;
+    }
+    wake_.notify_all();
+    for (auto& t : threads_) t.join();
+  }
   void loop(int i) {
     _mm_setcsr(0x1F80);  // round to nearest even, all exceptions masked, no FTZ, no DAZ
     uint64_t seen = 0;
@@ -412,7 +419,7 @@ zero_status_t offload_init(const zero_shard_desc_t* desc, const zero_offload_buf
   if (threads > kMaxThreads) threads = kMaxThreads;
 
   std::unique_ptr<zero_offload> h(new (std::nothrow) zero_offload());
-  if (!h) return fail(ZERO_EINVAL, "out of host memory");
+  if (!h) return fail(ZERO_ENOMEM, "out of host memory");
   h->info = p.info;
   h->pieces = std::move(p.pieces);
   h->dtype = desc->dtype;
@@ -515,7 +522,7 @@ zero_status_t offload_init(const zero_shard_desc_t* desc, const zero_offload_buf
   h->pool.reset(new (std::nothrow) Pool(threads));
   if (!h->pool) {
     cleanup_events();
-    return fail(ZERO_EINVAL, "out of host memory");
+    return fail(ZERO_ENOMEM, "out of host memory");
   }
 
   // state: m = v = 0; master given, or the exact upcast of the 16-bit slice
@@ -571,7 +578,7 @@ zero_status_t zero_offload_init(const zero_shard_desc_t* desc, const zero_offloa
   try {
     return offload_init(desc, bufs, master_init, num_threads, stream, out);
   } catch (const std::exception& e) {
-    return fail(ZERO_EINVAL, std::string("host resources: ") + e.what());
+    return fail(ZERO_ENOMEM, std::string("host resources: ") + e.what());
   }
 }
 
@@ -693,7 +700,7 @@ zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t
   if (h->phase != kStats) return fail(ZERO_ESTATE, "zero_offload_adam_step needs zero_offload_grad_stats first");
   // per copy block: tiles finished (allocated before any state changes)
   std::unique_ptr<std::atomic<int64_t>[]> done(new (std::nothrow) std::atomic<int64_t>[h->n_blocks > 0 ? h->n_blocks : 1]);
-  if (!done) return fail(ZERO_EINVAL, "out of host memory");
+  if (!done) return fail(ZERO_ENOMEM, "out of host memory");
   DeviceGuard dg(h->device, h->has_device);
   zero_status_t rs = wait_push(h);
   if (rs != ZERO_OK) return rs;
@@ -834,6 +841,12 @@ zero_status_t zero_offload_destroy(zero_offload_t h) {
       (void)hipEventDestroy(h->fetch_ev[k]);
     }
     if (h->push_ev) (void)hipEventDestroy(h->push_ev);
+    if (h->stats_ev) (void)hipEventDestroy(h->stats_ev);
+    if (h->aux) {
+      hipError_t e = hipStreamSynchronize(h->aux);
+      if (e != hipSuccess && rs == ZERO_OK) rs = hip_fail("hipStreamSynchronize(statistics read-back)", e);
+      (void)hipStreamDestroy(h->aux);
+    }
   }
   delete h;
   return rs;

@@ -67,6 +67,7 @@ struct zero_shard {
   bool cast_pending;
   bool accumulating;   // micro-steps summed into red since the last intake
   bool reduce_out16;   // the local reduce delivers its sum in the 16-bit type
+  bool red_holds16;    // red holds the last intake's 16-bit reduce output (not fp32 values)
   int64_t dp_size;
   bool dynamic;        // device-resident dynamic loss scale enabled
   zero_loss_scaler_t dyn_cfg;
@@ -152,7 +153,7 @@ zero_status_t shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t*
   if (master_init && mis16(master_init)) return fail(ZERO_EINVAL, "master_init must be 16-byte aligned");
 
   zero_shard* h = new (std::nothrow) zero_shard();
-  if (!h) return fail(ZERO_EINVAL, "out of host memory");
+  if (!h) return fail(ZERO_ENOMEM, "out of host memory");
   hipStream_t st = static_cast<hipStream_t>(stream);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -192,6 +193,7 @@ zero_status_t shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t*
   h->cast_pending = false;
   h->accumulating = false;
   h->reduce_out16 = false;
+  h->red_holds16 = false;
   h->dp_size = desc->dp_size;
   h->dynamic = false;
   memset(&h->dyn_cfg, 0, sizeof(h->dyn_cfg));
@@ -258,7 +260,7 @@ zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* 
   try {
     return shard_plan(desc, out);
   } catch (const std::exception& e) {
-    return fail(ZERO_EINVAL, std::string("host resources: ") + e.what());
+    return fail(ZERO_ENOMEM, std::string("host resources: ") + e.what());
   }
 }
 
@@ -267,7 +269,7 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
   try {
     return shard_init(desc, bufs, master_init, stream, out);
   } catch (const std::exception& e) {
-    return fail(ZERO_EINVAL, std::string("host resources: ") + e.what());
+    return fail(ZERO_ENOMEM, std::string("host resources: ") + e.what());
   }
 }
 
@@ -310,6 +312,7 @@ zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grad
                                        h->reduce_out16, h->red, h->grid_main, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("accumulate kernel", e);
   h->accumulating = true;
+  h->red_holds16 = false;
   h->phase = kReady;
   h->cast_pending = false;
   return ZERO_OK;
@@ -371,6 +374,7 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     h->grad_source = h->reduce_out16 ? kGradRed16 : kGradRed;
     h->step_flat_g = nullptr;
   }
+  h->red_holds16 = h->grad_source == kGradRed16;
   h->inv = inv_loss_scale;
   h->other_flag = 0;
   h->other_sumsq = 0.0;
@@ -601,7 +605,7 @@ zero_status_t zero_export_state(zero_shard_t h, int32_t which, float* dst, void*
   if (!h) return fail(ZERO_EINVAL, "null handle");
   const float* src = which == 0 ? h->master : which == 1 ? h->m : which == 2 ? h->v : which == 3 ? h->red : nullptr;
   if (!src) return fail(ZERO_EINVAL, "which must be 0 (master), 1 (m), 2 (v) or 3 (red, when allocated)");
-  if (which == 3 && h->grad_source == kGradRed16)
+  if (which == 3 && h->red_holds16)
     return fail(ZERO_ESTATE, "bufs.red holds the last intake's 16-bit reduce output, not fp32 values");
   if (!dst && h->info.valid_elems > 0) return fail(ZERO_EINVAL, "null destination");
   DeviceGuard dg(h->device);
