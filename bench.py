@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--cpu-steps", type=int, default=7)
     p.add_argument("--cpu-threads", type=int, default=16,
                    help="threads of the threaded oracle baseline (at most the usable CPUs)")
+    p.add_argument("--no-cold-cache", action="store_true",
+                   help="skip the per-step timing after a cache-evicting write (after the timed steps)")
     p.add_argument("--no-copy-ceiling", action="store_true",
                    help="skip the device-to-device copy measurement after the timed steps")
     p.add_argument("--copy-calibration", action="store_true",
@@ -276,6 +278,28 @@ def cpu_baseline(w, sample, steps, threads=1, piece=1 << 20, keep=False):
             dt = time.perf_counter() - t0
     assert np.isfinite(st.w).all()
     return (n * steps / dt, dt, st) if keep else (n * steps / dt, dt)
+
+
+def cold_cache_steps(wl, steps, flush_bytes=1 << 30):
+    """Median duration (ms) of `steps` steps each timed on its own after a 1 GiB write that
+    evicts the 256 MB Infinity Cache and the L2s: per step, a fill of a scratch buffer, then
+    the step between two HIP events on the step's stream, then a wait for it."""
+    import statistics
+
+    import torch
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    times = []
+    for k in range(steps):
+        scratch.fill_(float(k))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        wl.step()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    torch.cuda.synchronize()
+    del scratch
+    return statistics.median(times)
 
 
 def host_info():
@@ -627,6 +651,14 @@ def main():
         if a.segment_consumer != "none":
             out["pipeline"]["first_segment_ready_ms"] = sum(e[1].elapsed_time(e[3]) for e in evs) / a.steps
             out["pipeline"]["last_segment_done_ms"] = sum(e[1].elapsed_time(e[4]) for e in evs) / a.steps
+    if not a.no_cold_cache:
+        cold_ms = cold_cache_steps(wl, a.steps)
+        out["cold_cache"] = {"ms_per_step_median": cold_ms, "value": valid / (cold_ms * 1e-3),
+                             "hbm_frac_step": step_b * valid / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                             "steps": a.steps,
+                             "protocol": "after the timed steps: per step a 1 GiB fill of a scratch buffer "
+                                         "(evicts the Infinity Cache and L2s), then the step alone between "
+                                         "two events; median"}
     if not a.no_copy_ceiling:
         del wl
         torch.cuda.empty_cache()
