@@ -200,9 +200,11 @@ def bytes_per_param(w, micro_steps=1, reduce_out16=False):
 
     One micro-step reads its sources (2 B per rank buffer, or 2 B of already-reduced
     gradient); the first accumulation writes the fp32 accumulator (4 B), later ones
-    read and write it (8 B); the step's intake on top of an accumulation reads it and
-    writes u (8 B); the Adam pass then reads u (4 B) instead of the 16-bit gradient.
-    With a 16-bit reduce output the reduce writes, and the Adam pass reads, 2 B."""
+    read and write it (8 B).  The step's intake on top of an accumulation: from rank
+    buffers it reads the accumulator and writes u (8 B) and the Adam pass reads u
+    (4 B); from one already-reduced source it only reads the accumulator (4 B) and
+    the Adam pass reads the accumulator and the source again (4 + 2 B).  With a 16-bit
+    reduce output the reduce writes, and the Adam pass reads, 2 B."""
     src = 2 * w.nd if w.grad_mode == "reduce" else 2
     if micro_steps <= 1:
         if w.grad_mode == "reduce" and reduce_out16:
@@ -210,8 +212,11 @@ def bytes_per_param(w, micro_steps=1, reduce_out16=False):
         if w.grad_mode == "reduce":
             return src + 4 + 4 + 26, 4 + 12 + 12 + 2      # write fp32 u; Adam reads u
         return src + 2 + 12 + 12 + 2, 2 + 12 + 12 + 2    # statistics pass, then Adam re-reads the gradient
-    step = (src + 4) + (micro_steps - 2) * (src + 8) + (src + 8) + (4 + 12 + 12 + 2)
-    return step, 4 + 12 + 12 + 2
+    if w.grad_mode == "reduce":
+        step = (src + 4) + (micro_steps - 2) * (src + 8) + (src + 8) + (4 + 12 + 12 + 2)
+        return step, 4 + 12 + 12 + 2
+    adam = 4 + src + 12 + 12 + 2
+    return (src + 4) + (micro_steps - 2) * (src + 8) + (src + 4) + adam, adam
 
 
 def cpu_baseline(w, sample, steps, threads=1, piece=1 << 20, keep=False):

@@ -240,7 +240,11 @@ zero_status_t zero_set_reduce_output(zero_shard_t h, int32_t out_16bit);
  *                 N_d <= 64.
  *   after zero_accumulate_grads: the sources above (or none, n_ranks =
  *                 ZERO_ACCUMULATED) are added to the accumulated gradient in
- *                 bufs.red first: acc + s.
+ *                 bufs.red first: acc + s.  With N_d >= 2 rank buffers u is
+ *                 stored in bufs.red; with one source or none bufs.red keeps
+ *                 acc, and zero_adam_step recomputes u = (acc + s) * inv with
+ *                 the same fp32 operations (so the source, registered or
+ *                 rank_grads[0], must stay unchanged until zero_adam_step).
  * u = gradient * inv_loss_scale (fp32), or gradient * (1 / device scale) with
  * ZERO_DEVICE_LOSS_SCALE; flag = any u not finite; sum of squares = sum of u*u
  * in fp64.  rank_grads is a host array of device pointers.  EINVAL on bad

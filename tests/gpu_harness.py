@@ -203,10 +203,12 @@ class Sim:
         res = oracle.step_ranks_accumulated(self.ostates, micro, self.begins, inv, max_norm, hp,
                                             reduce_out16=self.reduce_out16)
         loc = {}
+        keep = []   # the last micro-step's sources stay unchanged until the Adam pass, which re-reads them
         for k, grads in enumerate(micro):
             last = k == len(micro) - 1
             for r in self.ranks:
                 dg = self._device_grads(grads)   # registered storage is rewritten per micro-step
+                keep.append(dg)
                 s = self.shards[r]
                 if last and last_fused:
                     s.zero_reduce_grads(dg, dev_inv)

@@ -21,7 +21,10 @@ def test_bytes_per_param():
     # micro-steps: first accumulation writes the accumulator, later ones read and write it
     assert bench.bytes_per_param(recipes.reduce8(), 2) == ((16 + 4) + (16 + 8) + 30, 30)
     assert bench.bytes_per_param(recipes.reduce8(), 4) == ((16 + 4) + 2 * (16 + 8) + (16 + 8) + 30, 30)
-    assert bench.bytes_per_param(recipes.full7p5b(), 2) == ((2 + 4) + (2 + 8) + 30, 30)
+    # one already-reduced source: the last intake only reads the accumulator and the source,
+    # the Adam pass reads both again
+    assert bench.bytes_per_param(recipes.full7p5b(), 2) == ((2 + 4) + (2 + 4) + 32, 32)
+    assert bench.bytes_per_param(recipes.zero1_7p5b(), 3) == ((2 + 4) + (2 + 8) + (2 + 4) + 32, 32)
 
 
 def test_more_than_one_gpu_is_refused():

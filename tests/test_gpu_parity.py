@@ -314,7 +314,11 @@ def test_accumulation_modes(mode, nd, K):
         sim.compare()
 
 
-def test_accumulation_misaligned_tensors():
+@pytest.mark.parametrize("last_fused", [True, False])
+def test_accumulation_misaligned_tensors(last_fused):
+    """Registered per-tensor gradients at odd offsets, accumulated over three micro-steps;
+    the last one through the intake itself (the Adam pass then re-reads the registered
+    gradient next to the accumulator) or accumulated too (ZERO_ACCUMULATED)."""
     numel = [5000, 1, 8193, 64, 12345, 3]
     w = recipes.ragged_mini(3)
     psi = sum(numel)
@@ -322,8 +326,9 @@ def test_accumulation_misaligned_tensors():
     sim = Sim(numel, 3, F16, p16, master, "ragged", per_tensor_params=True, param_misalign=(1, 3),
               grad_misalign=(2,), with_red=True)
     sim.p16_initial = p16.copy()
-    sim.step_accumulated(micro_grads(w, 1, psi, 1, 3), 1.0, 1.0, hp_of(w.hp), last_fused=False)
-    sim.compare()
+    for step in (1, 2):
+        sim.step_accumulated(micro_grads(w, step, psi, 1, 3), 1.0, 1.0, hp_of(w.hp), last_fused=last_fused)
+        sim.compare()
 
 
 def test_accumulation_step_order():
@@ -400,19 +405,22 @@ def test_dynamic_loss_scale_modes(mode, nd, fuse):
         sim.compare()
 
 
-@pytest.mark.parametrize("last_fused", [True, False])
-def test_dynamic_loss_scale_with_accumulation(last_fused):
+@pytest.mark.parametrize("mode,last_fused", [("reduce", True), ("reduce", False), ("flat", True), ("flat", False)])
+def test_dynamic_loss_scale_with_accumulation(mode, last_fused):
+    """Device loss scale with two micro-steps: 3 rank buffers (u stored by the intake) or
+    one already-reduced flat source (u recomputed by the Adam pass from the accumulator);
+    an overflow in the first micro-step is seen only through the accumulator."""
     w = recipes.tiny()
     psi = 120_007
     master, p16 = master_of(w, psi)
-    sim = Sim([psi], 3, F16, p16, master, "reduce")
+    sim = Sim([psi], 3, F16, p16, master, mode, with_red=True)
     sim.p16_initial = p16.copy()
     sim.enable_dynamic(init_scale=1024.0, growth=2.0, backoff=0.5, interval=1, min_scale=1.0)
     S = sim.plans[0][1]
     for step in range(1, 5):
-        micro = micro_grads(w, step, psi, 3, 2)
+        micro = micro_grads(w, step, psi, 3 if mode == "reduce" else 1, 2)
         if step == 2:
-            _poison(micro[0][1], 2 * S + 3, F16)    # first micro-step: only the accumulation sees it
+            _poison(micro[0][min(1, len(micro[0]) - 1)], 2 * S + 3, F16)   # first micro-step only
         res = sim.step_accumulated(micro, None, w.max_norm, hp_of(w.hp), last_fused=last_fused)
         assert all(x["skipped"] == (step == 2) for x in res)
         sim.compare()

@@ -487,8 +487,9 @@ struct GradSum {
 
 // Intake with statistics: u = (ACC ? red + s : s) * inv stored in red, plus the
 // fp64 sum of squares.  With kSrcNone, u = red * inv.  R16: the new sources' sum s
-// arrives as a 16-bit reduce output (rounded once) before it is added.
-template <int DT, int NR, bool ACC, bool R16 = false>
+// arrives as a 16-bit reduce output (rounded once) before it is added.  !STORE:
+// statistics only; red keeps the accumulator and the Adam pass recomputes u.
+template <int DT, int NR, bool ACC, bool R16 = false, bool STORE = true>
 struct ReduceOp {
   GradSum<DT, NR> gs;
   float* red;
@@ -501,7 +502,7 @@ struct ReduceOp {
     else r = R16 ? round16<DT>(gs.one(j)) : gs.one(j);
     const float u = r * inv;
     ss.add(0, u);
-    red[j] = u;
+    if constexpr (STORE) red[j] = u;
   }
   template <int U>
   __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
@@ -525,14 +526,14 @@ struct ReduceOp {
       const f32x4 u = s[k] * inv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) ss.add(k, u[e]);
-      st32x4_nt(red + j + k * stride, u);
+      if constexpr (STORE) st32x4_nt(red + j + k * stride, u);
     }
   }
 };
 
-template <int DT, int NR, bool ACC, bool R16 = false>
+template <int DT, int NR, bool ACC, bool R16 = false, bool STORE = true>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
-  ReduceOp<DT, NR, ACC, R16> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc),
+  ReduceOp<DT, NR, ACC, R16, STORE> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc),
                                 SumSq{}};
   walk_chunks(a.chunks, a.n_chunks, a.cpb, [&](const ChunkRef ch) {
     op.gs.flat_off = ch.flat_off;
@@ -656,9 +657,14 @@ __device__ __forceinline__ void adam_elem(float u, float& w, float& m, float& v,
   v = vi;
 }
 
-// Gradient sources of the Adam pass: the flat or registered 16-bit gradient, the fp32
-// u of a reduce or accumulation, or the 16-bit reduce output (in red, state layout).
-enum { kGradFlat16 = 0, kGradChunk16 = 1, kGradRed = 2, kGradRed16 = 3 };
+// Gradient sources of the Adam pass (GradSource): the flat or registered 16-bit
+// gradient, the fp32 u of a reduce, the 16-bit reduce output (in red, state layout),
+// or, after an intake on top of an accumulation from one source or none, u
+// recomputed from the accumulator with the intake's own operations.
+template <int GS>
+constexpr bool grad_from_acc() { return GS == kGradAcc || GS == kGradAccFlat16 || GS == kGradAccChunk16; }
+template <int GS>
+constexpr bool grad_acc16() { return GS == kGradAccFlat16 || GS == kGradAccChunk16; }
 
 template <int DT, int GS, bool CAST, bool WT>
 struct AdamOp {
@@ -671,6 +677,8 @@ struct AdamOp {
   AdamScalars s;
   __device__ __forceinline__ float grad(int64_t j) const {
     if constexpr (GS == kGradRed) return gred[j];
+    else if constexpr (GS == kGradAcc) return gred[j] * s.inv;
+    else if constexpr (grad_acc16<GS>()) return (gred[j] + dec16<DT>(g16[j])) * s.inv;
     else return dec16<DT>(g16[j]) * s.inv;
   }
   __device__ __forceinline__ void elem(int64_t j) {
@@ -692,6 +700,10 @@ struct AdamOp {
       const int64_t o = j + k * stride;
       if constexpr (GS == kGradRed) {
         G[k] = ld32x4_nt(gred + o);
+      } else if constexpr (GS == kGradAcc) {
+        G[k] = ld32x4_nt(gred + o) * s.inv;
+      } else if constexpr (grad_acc16<GS>()) {
+        G[k] = (ld32x4_nt(gred + o) + dec16x4<DT>(ld16x4(g16 + o))) * s.inv;
       } else {
         G[k] = dec16x4<DT>(ld16x4(g16 + o)) * s.inv;
       }
@@ -893,17 +905,21 @@ __global__ void __launch_bounds__(ZS_ADAM_BLOCK) adam_kernel(AdamArgs a) {
     op.p16 = reinterpret_cast<uint16_t*>(ch.p16) + lo;
     int head;
     bool ok;
-    if constexpr (GS == kGradRed) {
+    if constexpr (GS == kGradRed || GS == kGradAcc) {
       op.gred = a.red + ch.state_off + lo;
       head = head16(op.p16);
       ok = aligned(op.w + head, 16) && aligned(op.gred + head, 16);
     } else {
-      op.g16 = (GS == kGradFlat16    ? a.flat_g + ch.flat_off
-                : GS == kGradRed16 ? reinterpret_cast<const uint16_t*>(a.red) + ch.state_off
-                                   : reinterpret_cast<const uint16_t*>(ch.g16)) +
+      op.g16 = (GS == kGradFlat16 || GS == kGradAccFlat16 ? a.flat_g + ch.flat_off
+                : GS == kGradRed16                         ? reinterpret_cast<const uint16_t*>(a.red) + ch.state_off
+                                                           : reinterpret_cast<const uint16_t*>(ch.g16)) +
                lo;
       head = head16(op.g16);
       ok = aligned(op.w + head, 16) && aligned(op.g16 + head, 8);
+      if constexpr (grad_acc16<GS>()) {
+        op.gred = a.red + ch.state_off + lo;
+        ok = ok && aligned(op.gred + head, 16);
+      }
     }
     if constexpr (CAST) ok = ok && aligned(op.p16 + head, 8);
     ok = ok && aligned(op.m + head, 16) && aligned(op.v + head, 16);
@@ -1066,6 +1082,21 @@ static void launch_reduce_acc(const ReduceArgs& a, int src, unsigned g, hipStrea
   }
 }
 
+// Statistics-only intake on top of an accumulation from one source or none: red keeps
+// the accumulator, the Adam pass recomputes u from it.
+template <int DT>
+static void launch_acc_stats(const ReduceArgs& a, int src, unsigned g, hipStream_t st) {
+  switch (src) {
+    case 1: hipLaunchKernelGGL((reduce_kernel<DT, 1, true, false, false>), dim3(g), dim3(kBlock), 0, st, a); break;
+    case kSrcChunk:
+      hipLaunchKernelGGL((reduce_kernel<DT, kSrcChunk, true, false, false>), dim3(g), dim3(kBlock), 0, st, a);
+      break;
+    default:
+      hipLaunchKernelGGL((reduce_kernel<DT, kSrcNone, true, false, false>), dim3(g), dim3(kBlock), 0, st, a);
+      break;
+  }
+}
+
 template <int DT, bool FIRST>
 static void launch_accum_first(const ReduceArgs& a, int src, unsigned g, hipStream_t st) {
   switch (src) {
@@ -1111,9 +1142,11 @@ static int src_code(int32_t n_ranks) {
 // r16: the rank buffers' sum arrives as a 16-bit reduce output.  Without
 // accumulation the 16-bit result itself is stored, in red (state layout, 2 bytes
 // per element), and u is taken from it; with accumulation the rounded sum is added.
+// keep_acc (with accumulation from one source or none, n_ranks 0, 1 or < 0):
+// statistics only, red keeps the accumulator.
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                         int32_t n_ranks, bool accumulate, bool r16, float inv, int32_t dyn_slot, float* red,
-                         DevScalars* sc, const IntakeParts& parts, hipStream_t st) {
+                         int32_t n_ranks, bool accumulate, bool r16, bool keep_acc, float inv, int32_t dyn_slot,
+                         float* red, DevScalars* sc, const IntakeParts& parts, hipStream_t st) {
   if (n_chunks == 0) {
     hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc);
     return hipGetLastError();
@@ -1121,6 +1154,12 @@ hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const
   const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, inv, dyn_slot, red, sc, parts);
   const unsigned g = intake_grid(n_chunks, a.cpb);
   const int src = src_code(n_ranks);
+  if (keep_acc) {
+    if (!accumulate || !(src == 1 || src == kSrcChunk || src == kSrcNone)) return hipErrorInvalidValue;
+    if (dtype == ZERO_BF16) launch_acc_stats<ZERO_BF16>(a, src, g, st);
+    else launch_acc_stats<ZERO_F16>(a, src, g, st);
+    return hipGetLastError();
+  }
   if (r16 && is_rank_reduce(src)) {
     if (dtype == ZERO_BF16) {
       if (accumulate) launch_reduce_acc_r16<ZERO_BF16>(a, src, g, st);
@@ -1181,10 +1220,15 @@ static void launch_adam_gs(const AdamArgs& a, bool cast, unsigned g, hipStream_t
 
 template <int DT>
 static void launch_adam_dt(const AdamArgs& a, int gs, bool cast, unsigned g, hipStream_t st) {
-  if (gs == kGradFlat16) launch_adam_gs<DT, kGradFlat16>(a, cast, g, st);
-  else if (gs == kGradChunk16) launch_adam_gs<DT, kGradChunk16>(a, cast, g, st);
-  else if (gs == kGradRed) launch_adam_gs<DT, kGradRed>(a, cast, g, st);
-  else launch_adam_gs<DT, kGradRed16>(a, cast, g, st);
+  switch (gs) {
+    case kGradFlat16: launch_adam_gs<DT, kGradFlat16>(a, cast, g, st); break;
+    case kGradChunk16: launch_adam_gs<DT, kGradChunk16>(a, cast, g, st); break;
+    case kGradRed: launch_adam_gs<DT, kGradRed>(a, cast, g, st); break;
+    case kGradRed16: launch_adam_gs<DT, kGradRed16>(a, cast, g, st); break;
+    case kGradAccFlat16: launch_adam_gs<DT, kGradAccFlat16>(a, cast, g, st); break;
+    case kGradAccChunk16: launch_adam_gs<DT, kGradAccChunk16>(a, cast, g, st); break;
+    default: launch_adam_gs<DT, kGradAcc>(a, cast, g, st); break;
+  }
 }
 
 hipError_t launch_adam(int dtype, int grad_source, bool cast, const AdamArgs& a, int64_t grid_cap, hipStream_t st) {

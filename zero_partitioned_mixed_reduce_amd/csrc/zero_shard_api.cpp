@@ -39,7 +39,13 @@ zero_status_t hip_fail(const char* what, hipError_t e) {
   } while (0)
 
 enum Phase { kReady, kReduced, kChecked, kNormed, kStepped };
-enum { kGradFlat16 = 0, kGradChunk16 = 1, kGradRed = 2, kGradRed16 = 3 };
+using zs::kGradAcc;
+using zs::kGradAccChunk16;
+using zs::kGradAccFlat16;
+using zs::kGradChunk16;
+using zs::kGradFlat16;
+using zs::kGradRed;
+using zs::kGradRed16;
 
 }  // namespace
 
@@ -336,16 +342,20 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
   DeviceGuard dg(h->device);
   hipError_t e;
   if (h->accumulating) {
-    // last micro-step (or none: ZERO_ACCUMULATED) on top of the accumulated gradient
+    // last micro-step (or none: ZERO_ACCUMULATED) on top of the accumulated gradient.  From one
+    // source or none the pass only takes the statistics: red keeps the accumulator and the Adam
+    // pass recomputes u = (acc + g) * inv from it and the (unchanged) source, which moves fewer
+    // bytes than storing u and reading it back; from rank buffers u is stored.
     if (n_ranks != ZERO_ACCUMULATED) {
       zero_status_t s = check_sources(h, rank_grads, n_ranks);
       if (s != ZERO_OK) return s;
     }
-    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, true, h->reduce_out16,
+    const bool keep_acc = n_ranks == 0 || n_ranks == 1 || n_ranks == ZERO_ACCUMULATED;
+    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, true, h->reduce_out16, keep_acc,
                           inv_loss_scale, dyn_slot, h->red, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
-    h->grad_source = kGradRed;
-    h->step_flat_g = nullptr;
+    h->grad_source = !keep_acc ? kGradRed : n_ranks == 0 ? kGradAccChunk16 : n_ranks == 1 ? kGradAccFlat16 : kGradAcc;
+    h->step_flat_g = n_ranks == 1 ? static_cast<const uint16_t*>(rank_grads[0]) : nullptr;
     h->accumulating = false;
   } else if (n_ranks == ZERO_ACCUMULATED) {
     return fail(ZERO_ESTATE, "ZERO_ACCUMULATED without zero_accumulate_grads in this step");
@@ -368,7 +378,7 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     for (int q = 0; q < n_ranks; ++q)
       if (!rank_grads[q]) return fail(ZERO_EINVAL, "rank_grads[" + std::to_string(q) + "] is null");
     if (!h->red) return fail(ZERO_EINVAL, "reducing N_d >= 2 buffers needs bufs.red");
-    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, false, h->reduce_out16,
+    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, false, h->reduce_out16, false,
                           inv_loss_scale, dyn_slot, h->red, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
     h->grad_source = h->reduce_out16 ? kGradRed16 : kGradRed;

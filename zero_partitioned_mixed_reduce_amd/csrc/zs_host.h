@@ -19,8 +19,8 @@ namespace zs {
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
                           int32_t dyn_slot, DevScalars* sc, const IntakeParts& parts, hipStream_t st);
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                         int32_t n_ranks, bool accumulate, bool r16, float inv, int32_t dyn_slot, float* red,
-                         DevScalars* sc, const IntakeParts& parts, hipStream_t st);
+                         int32_t n_ranks, bool accumulate, bool r16, bool keep_acc, float inv, int32_t dyn_slot,
+                         float* red, DevScalars* sc, const IntakeParts& parts, hipStream_t st);
 hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
                              int32_t n_ranks, bool first, bool r16, float* red, int64_t grid_cap, hipStream_t st);
 struct AdamArgs;

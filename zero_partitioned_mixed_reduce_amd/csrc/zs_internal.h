@@ -97,6 +97,17 @@ struct IntakeParts {
   uint64_t* gpart;     // one per group: the sum of its blocks' partials
 };
 
+// Gradient source of the Adam pass, fixed by the step's intake.
+enum GradSource : int {
+  kGradFlat16 = 0,      // the flat already-reduced 16-bit gradient given to the intake
+  kGradChunk16 = 1,     // the already-reduced 16-bit gradient registered at init
+  kGradRed = 2,         // fp32 u, stored in red by the intake
+  kGradRed16 = 3,       // the 16-bit reduce output, stored in red by the intake
+  kGradAccFlat16 = 4,   // u = (accumulator in red + the flat 16-bit gradient) * inv, recomputed
+  kGradAccChunk16 = 5,  // u = (accumulator in red + the registered 16-bit gradient) * inv, recomputed
+  kGradAcc = 6,         // u = accumulator in red * inv, recomputed
+};
+
 constexpr int64_t kSegOff = sizeof(DevScalars);
 constexpr int64_t kChunksOff = kSegOff + kMaxSegments * (int64_t)sizeof(SegState);
 
