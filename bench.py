@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--cpu-steps", type=int, default=7)
     p.add_argument("--cpu-threads", type=int, default=16,
                    help="threads of the threaded oracle baseline (at most the usable CPUs)")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the step captured into a HIP graph and replayed (after the timed steps)")
     p.add_argument("--no-cold-cache", action="store_true",
                    help="skip the per-step timing after a cache-evicting write (after the timed steps)")
     p.add_argument("--no-copy-ceiling", action="store_true",
@@ -305,6 +307,24 @@ def cold_cache_steps(wl, steps, flush_bytes=1 << 30):
     torch.cuda.synchronize()
     del scratch
     return statistics.median(times)
+
+
+def graph_steps(wl, steps):
+    """The step captured once into a HIP graph (torch.cuda.CUDAGraph) and replayed
+    `steps` times back to back; returns ms per replay.  Each replay is one more step
+    (the step counters live on the device)."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wl.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del graph
+    return ms
 
 
 def host_info():
@@ -656,6 +676,16 @@ def main():
         if a.segment_consumer != "none":
             out["pipeline"]["first_segment_ready_ms"] = sum(e[1].elapsed_time(e[3]) for e in evs) / a.steps
             out["pipeline"]["last_segment_done_ms"] = sum(e[1].elapsed_time(e[4]) for e in evs) / a.steps
+    if a.graph and not wl.segments:
+        t_before = wl.shard.query()["t"]
+        g_ms = graph_steps(wl, a.steps)
+        q = wl.shard.query()
+        assert not q["skipped"] and q["t"] == t_before + a.steps, q
+        out["graph_replay"] = {"ms_per_step": g_ms, "value": valid / (g_ms * 1e-3),
+                               "hbm_frac_step": step_b * valid / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                               "steps": a.steps,
+                               "protocol": "after the timed steps: the step captured once into a HIP graph, "
+                                           "then replayed back to back, bracketed by synchronisation"}
     if not a.no_cold_cache:
         cold_ms = cold_cache_steps(wl, a.steps)
         out["cold_cache"] = {"ms_per_step_median": cold_ms, "value": valid / (cold_ms * 1e-3),

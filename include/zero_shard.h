@@ -35,6 +35,15 @@
  *   - Element counts and offsets are int64 (a 7.5e9-element model is fine).
  *   - Calls on one handle must not overlap (one host thread, one stream at a
  *     time); different handles are independent.
+ *   - A step's calls (without host_* outputs or segments) only enqueue kernels,
+ *     and the step counters, the loss scale and the choice between the two
+ *     counter slots live in the workspace, so a step captured into a HIP graph
+ *     can be replayed: each replay is one more step.  Host queries after
+ *     replays read the device state.  The arguments of the captured calls
+ *     (inv_loss_scale, other_ranks_*, max_norm, hyperparameters, pointers) are
+ *     fixed in the graph; see zero_local_stats_device for taking the other
+ *     ranks' values from device memory.  Segment tracking counts steps on the
+ *     host and is not for replays.
  */
 #ifndef ZERO_SHARD_H
 #define ZERO_SHARD_H
@@ -259,6 +268,18 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
  * zero_reduce_grads, for the caller's exchange with the other ranks.
  * Synchronises the stream.  ESTATE before a zero_reduce_grads. */
 zero_status_t zero_local_stats(zero_shard_t h, int32_t* found_inf, double* sumsq, void* stream);
+
+/* Device addresses, inside the workspace and fixed for the handle's lifetime,
+ * of where zero_reduce_grads leaves this rank's fp64 sum of squares and its
+ * int32 overflow flag (0 or 1).  For a step that never waits on the host, the
+ * exchange with the other ranks can happen in place on the device: after
+ * zero_reduce_grads, all-reduce *sumsq (sum) and *found_inf (max, or sum) across
+ * the ranks on the step's stream, then pass other_ranks_found_inf = 0 and
+ * other_ranks_sumsq = 0; zero_adam_step then takes the skip, norm and clip from
+ * the global values.  (The pages exchange these scalars to decide the skip,
+ * "DeepSpeed ZeRO" 权重更新的触发条件; the library fixes no transport.)  EINVAL
+ * on null arguments. */
+zero_status_t zero_local_stats_device(zero_shard_t h, double** sumsq, int32_t** found_inf);
 
 /* Global overflow decision: this rank's flag OR other_ranks_found_inf (the
  * other ranks' flags, combined by the caller).  If host_found_inf is non-NULL

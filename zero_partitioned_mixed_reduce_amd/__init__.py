@@ -5,6 +5,7 @@ from ._abi import (ZERO_ACCUMULATED, ZERO_BF16, ZERO_DEVICE_LOSS_SCALE, ZERO_F16
                    zero_adam_hparams_t, zero_adam_step, zero_cast_params, zero_enable_dynamic_loss_scale,
                    zero_loss_scale, zero_loss_scaler_t, zero_set_reduce_output,
                    zero_check_overflow, zero_export_state, zero_grad_norm, zero_last_error, zero_local_stats,
+                   zero_local_stats_device,
                    zero_reduce_grads, zero_shard_bufs_t, zero_shard_desc_t, zero_shard_destroy, zero_shard_info,
                    zero_shard_info_t, zero_shard_init, zero_shard_pieces, zero_shard_plan, zero_shard_query,
                    zero_set_segments, zero_segment_range, zero_wait_segment, zero_segment_timeouts,
@@ -14,7 +15,7 @@ from ._abi import (ZERO_ACCUMULATED, ZERO_BF16, ZERO_DEVICE_LOSS_SCALE, ZERO_F16
 __all__ = ["ZERO_F16", "ZERO_BF16", "ZERO_ACCUMULATED", "ZERO_DEVICE_LOSS_SCALE", "ZeroError", "zero_shard_plan",
            "zero_shard_init", "zero_enable_dynamic_loss_scale", "zero_loss_scale", "zero_loss_scaler_t", "zero_set_reduce_output",
            "zero_accumulate_grads", "zero_reduce_grads",
-           "zero_local_stats", "zero_check_overflow", "zero_grad_norm", "zero_adam_step", "zero_cast_params",
+           "zero_local_stats", "zero_local_stats_device", "zero_check_overflow", "zero_grad_norm", "zero_adam_step", "zero_cast_params",
            "zero_shard_info", "zero_shard_pieces", "zero_shard_query", "zero_export_state", "zero_shard_destroy",
            "zero_last_error", "zero_shard_desc_t", "zero_shard_bufs_t", "zero_shard_info_t",
            "zero_adam_hparams_t", "zero_set_segments", "zero_segment_range", "zero_wait_segment",

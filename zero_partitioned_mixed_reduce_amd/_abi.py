@@ -62,6 +62,7 @@ _PROTOS = {
     "zero_set_reduce_output": [ctypes.c_void_p, ctypes.c_int32],
     "zero_local_stats": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
                          ctypes.c_void_p],
+    "zero_local_stats_device": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p)],
     "zero_check_overflow": [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p],
     "zero_grad_norm": [ctypes.c_void_p, ctypes.c_double, ctypes.c_float, ctypes.POINTER(ctypes.c_double),
                        ctypes.c_void_p],
@@ -167,6 +168,13 @@ def zero_local_stats(h, stream):
     f, s = ctypes.c_int32(), ctypes.c_double()
     _call("zero_local_stats", h, ctypes.byref(f), ctypes.byref(s), stream)
     return bool(f.value), s.value
+
+
+def zero_local_stats_device(h):
+    """Device addresses (ints) of this rank's fp64 sum of squares and int32 flag."""
+    s, f = ctypes.c_void_p(), ctypes.c_void_p()
+    _call("zero_local_stats_device", h, ctypes.byref(s), ctypes.byref(f))
+    return s.value, f.value
 
 
 def zero_check_overflow(h, other_ranks_found_inf, stream, sync=False):

@@ -249,7 +249,7 @@ __device__ __forceinline__ void stores_complete() {
 // adds the group sums in group order and publishes this rank's sum of squares and
 // non-finite flag (the sum is non-finite exactly when some u is, see SumSq).
 // Counters are re-armed by their last arrival.
-__device__ void finish_stats(double acc, DevScalars* sc, const IntakeParts& p) {
+__device__ void finish_stats(double acc, DevScalars* sc, const IntakeParts& p, int32_t flip) {
   __shared__ double lds[kBlock / 64];
   __shared__ int is_last;
   const double bsum = block_sum(acc, lds);
@@ -281,6 +281,7 @@ __device__ void finish_stats(double acc, DevScalars* sc, const IntakeParts& p) {
   if (threadIdx.x == 0) {
     sc->local_sumsq = total;
     sc->local_flag = !__builtin_isfinite(total);
+    if (flip) sc->cur_slot ^= 1u;  // every block of the pass has read it by now
     __hip_atomic_store(&sc->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -344,16 +345,18 @@ struct StatsArgs {
   int64_t n_chunks;
   const uint16_t* flat_g;  // flat [psi] gradient, or null to use chunk.g16
   float inv;
-  int32_t dyn_slot;        // >= 0: unscale by 1 / sc->slot[dyn_slot].scale instead of inv
+  int32_t dyn;             // 1: unscale by 1 / the device-resident loss scale instead of inv
   int32_t cpb;             // consecutive chunks per block
+  int32_t flip;            // 1: the step's first intake (its last block flips sc->cur_slot)
   DevScalars* sc;
   IntakeParts parts;
 };
 
 // The unscale factor of an intake pass: the call's inv, or 1 / the device-resident
-// dynamic loss scale (fp32, correctly rounded) of the given slot.
-__device__ __forceinline__ float intake_inv(float inv, int32_t dyn_slot, const DevScalars* sc) {
-  return dyn_slot >= 0 ? 1.0f / sc->slot[dyn_slot].scale : inv;
+// dynamic loss scale (fp32, correctly rounded) of the latest counters: slot
+// cur_slot ^ 1 before the step's first intake flips cur_slot, slot cur_slot after.
+__device__ __forceinline__ float intake_inv(float inv, int32_t dyn, int32_t flip, const DevScalars* sc) {
+  return dyn ? 1.0f / sc->slot[flip ? sc->cur_slot ^ 1u : sc->cur_slot].scale : inv;
 }
 
 // The table fields an intake pass needs, held in scalar registers.
@@ -392,7 +395,7 @@ __device__ __forceinline__ void walk_chunks(const Chunk* chunks, int64_t n_chunk
 
 template <int DT>
 __global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
-  Stats16Op<DT> op{nullptr, intake_inv(a.inv, a.dyn_slot, a.sc), SumSq{}};
+  Stats16Op<DT> op{nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc), SumSq{}};
   walk_chunks(a.chunks, a.n_chunks, a.cpb, [&](const ChunkRef ch) {
     op.g = a.flat_g ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
 #if ZS_STATS_V == 8
@@ -401,7 +404,7 @@ __global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
     run_chunk<ZS_STATS_U, 4>(op, ch.len, head16(op.g), true);
 #endif
   });
-  finish_stats(op.ss.total(), a.sc, a.parts);
+  finish_stats(op.ss.total(), a.sc, a.parts, a.flip);
 }
 
 // ---------------------------------------------------------------------------
@@ -413,9 +416,10 @@ struct ReduceArgs {
   const uint16_t* ranks[kMaxRanks];
   int32_t n_ranks;
   float inv;
-  int32_t dyn_slot;        // as in StatsArgs
+  int32_t dyn;             // as in StatsArgs
   float* red;
   int32_t cpb;             // consecutive chunks per block of the intake passes
+  int32_t flip;            // as in StatsArgs
   DevScalars* sc;
   IntakeParts parts;
 };
@@ -533,7 +537,7 @@ struct ReduceOp {
 
 template <int DT, int NR, bool ACC, bool R16 = false, bool STORE = true>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
-  ReduceOp<DT, NR, ACC, R16, STORE> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc),
+  ReduceOp<DT, NR, ACC, R16, STORE> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc),
                                 SumSq{}};
   walk_chunks(a.chunks, a.n_chunks, a.cpb, [&](const ChunkRef ch) {
     op.gs.flat_off = ch.flat_off;
@@ -542,7 +546,7 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
     const int head = op.gs.head(op.red);
     run_chunk<ZS_REDUCE_U, 4>(op, ch.len, head, op.gs.aligned_at(head, op.red));
   });
-  finish_stats(op.ss.total(), a.sc, a.parts);
+  finish_stats(op.ss.total(), a.sc, a.parts, a.flip);
 }
 
 // Intake with a 16-bit reduce output: h = RNE16(s) is stored in red16 (this rank's
@@ -576,7 +580,7 @@ struct Reduce16Op {
 
 template <int DT, int NR>
 __global__ void __launch_bounds__(kBlock) reduce16_kernel(ReduceArgs a) {
-  Reduce16Op<DT, NR> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn_slot, a.sc), SumSq{}};
+  Reduce16Op<DT, NR> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc), SumSq{}};
   walk_chunks(a.chunks, a.n_chunks, a.cpb, [&](const ChunkRef ch) {
     op.gs.flat_off = ch.flat_off;
     op.red16 = reinterpret_cast<uint16_t*>(a.red) + ch.state_off;
@@ -585,7 +589,7 @@ __global__ void __launch_bounds__(kBlock) reduce16_kernel(ReduceArgs a) {
     for (int q = 0; q < op.gs.nranks(); ++q) ok = ok && aligned(op.gs.src(q) + head, 8);
     run_chunk<ZS_REDUCE_U, 4>(op, ch.len, head, ok);
   });
-  finish_stats(op.ss.total(), a.sc, a.parts);
+  finish_stats(op.ss.total(), a.sc, a.parts, a.flip);
 }
 
 // One micro-step into the accumulator, no statistics: red = FIRST ? s : red + s.
@@ -745,7 +749,6 @@ struct AdamArgs {
   float* m;
   float* v;
   DevScalars* sc;
-  int32_t slot;            // slot to read; the other one receives this step's counters
   int32_t other_flag;
   double other_sumsq;
   float max_norm;
@@ -838,7 +841,7 @@ __device__ __forceinline__ int step_scalars(const AdamArgs& a, AdamScalars& s, S
     const double c = (double)a.max_norm / (norm + 1e-6);
     if (c < 1.0) clip = (float)c;
   }
-  const Slot cur = sc->slot[a.slot];
+  const Slot cur = sc->slot[sc->cur_slot];
   next = cur;
   if (!skip) {
     next.t = cur.t + 1;
@@ -880,7 +883,7 @@ __global__ void __launch_bounds__(ZS_ADAM_BLOCK) adam_kernel(AdamArgs a) {
   double norm;
   const int skip = step_scalars(a, s, next, norm);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    a.sc->slot[a.slot ^ 1] = next;
+    a.sc->slot[a.sc->cur_slot ^ 1u] = next;
     a.sc->norm = norm;
     a.sc->clip = s.clip;
     a.sc->skipped = skip;
@@ -996,9 +999,10 @@ __global__ void __launch_bounds__(kBlock) fill_zero_kernel(float* p, int64_t n) 
   for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < n; j += stride) p[j] = 0.0f;
 }
 
-__global__ void empty_stats_kernel(DevScalars* sc) {
+__global__ void empty_stats_kernel(DevScalars* sc, int32_t flip) {
   sc->local_sumsq = 0.0;
   sc->local_flag = 0;
+  if (flip) sc->cur_slot ^= 1u;
 }
 
 // ---------------------------------------------------------------------------
@@ -1020,13 +1024,13 @@ static unsigned intake_grid(int64_t n_chunks, int32_t cpb) {
 }
 
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
-                          int32_t dyn_slot, DevScalars* sc, const IntakeParts& parts, hipStream_t st) {
+                          bool dyn, bool flip, DevScalars* sc, const IntakeParts& parts, hipStream_t st) {
   if (n_chunks == 0) {
-    hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc);
+    hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc, (int32_t)flip);
     return hipGetLastError();
   }
   const int32_t cpb = n_chunks < ZS_STATS_SMALL ? ZS_STATS_SMALL_CPB : 1;
-  StatsArgs a{chunks, n_chunks, flat_g, inv, dyn_slot, cpb, sc, parts};
+  StatsArgs a{chunks, n_chunks, flat_g, inv, (int32_t)dyn, cpb, (int32_t)flip, sc, parts};
   const unsigned g = intake_grid(n_chunks, cpb);
   if (dtype == ZERO_BF16)
     hipLaunchKernelGGL(stats16_kernel<ZERO_BF16>, dim3(g), dim3(kBlock), 0, st, a);
@@ -1110,7 +1114,7 @@ static void launch_accum_first(const ReduceArgs& a, int src, unsigned g, hipStre
 }
 
 static ReduceArgs make_reduce_args(const Chunk* chunks, int64_t n_chunks, const void* const* ranks, int32_t n_ranks,
-                                   float inv, int32_t dyn_slot, float* red, DevScalars* sc,
+                                   float inv, bool dyn, bool flip, float* red, DevScalars* sc,
                                    const IntakeParts& parts) {
   ReduceArgs a;
   a.chunks = chunks;
@@ -1119,9 +1123,10 @@ static ReduceArgs make_reduce_args(const Chunk* chunks, int64_t n_chunks, const 
     a.ranks[q] = (ranks && q < n_ranks) ? static_cast<const uint16_t*>(ranks[q]) : nullptr;
   a.n_ranks = n_ranks > 0 ? n_ranks : 1;
   a.inv = inv;
-  a.dyn_slot = dyn_slot;
+  a.dyn = dyn;
   a.red = red;
   a.cpb = 1;
+  a.flip = flip;
   a.sc = sc;
   a.parts = parts;
   return a;
@@ -1145,13 +1150,13 @@ static int src_code(int32_t n_ranks) {
 // keep_acc (with accumulation from one source or none, n_ranks 0, 1 or < 0):
 // statistics only, red keeps the accumulator.
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                         int32_t n_ranks, bool accumulate, bool r16, bool keep_acc, float inv, int32_t dyn_slot,
+                         int32_t n_ranks, bool accumulate, bool r16, bool keep_acc, float inv, bool dyn, bool flip,
                          float* red, DevScalars* sc, const IntakeParts& parts, hipStream_t st) {
   if (n_chunks == 0) {
-    hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc);
+    hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc, (int32_t)flip);
     return hipGetLastError();
   }
-  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, inv, dyn_slot, red, sc, parts);
+  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, inv, dyn, flip, red, sc, parts);
   const unsigned g = intake_grid(n_chunks, a.cpb);
   const int src = src_code(n_ranks);
   if (keep_acc) {
@@ -1185,7 +1190,8 @@ hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const
 hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
                              int32_t n_ranks, bool first, bool r16, float* red, int64_t grid_cap, hipStream_t st) {
   if (n_chunks == 0) return hipSuccess;
-  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, 1.0f, -1, red, nullptr, IntakeParts{});
+  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, 1.0f, false, false, red, nullptr,
+                                        IntakeParts{});
   const unsigned g = clamp_grid(n_chunks * ZS_ADAM_SPLIT, grid_cap);
   const int src = src_code(n_ranks);
   if (r16 && is_rank_reduce(src)) {
@@ -1242,7 +1248,7 @@ hipError_t launch_adam(int dtype, int grad_source, bool cast, const AdamArgs& a,
 
 hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* chunks, int64_t n_chunks,
                             const uint16_t* flat_g, const float* red, float* master, float* m, float* v,
-                            DevScalars* sc, int32_t slot, int32_t other_flag, double other_sumsq, float max_norm,
+                            DevScalars* sc, int32_t other_flag, double other_sumsq, float max_norm,
                             float inv, const zero_adam_hparams_t* hp, const zero_loss_scaler_t* dyn,
                             const SegArgs* seg, int64_t grid_cap, hipStream_t st) {
   AdamArgs a;
@@ -1254,7 +1260,6 @@ hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* 
   a.m = m;
   a.v = v;
   a.sc = sc;
-  a.slot = slot;
   a.other_flag = other_flag;
   a.other_sumsq = other_sumsq;
   a.max_norm = max_norm;

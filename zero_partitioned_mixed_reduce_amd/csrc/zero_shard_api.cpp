@@ -84,7 +84,7 @@ struct zero_shard {
   int32_t other_flag;
   double other_sumsq;
   float max_norm;
-  int64_t adam_calls;  // parity selects the counter slot
+  int64_t adam_calls;  // zero_adam_step calls (the segments' epoch)
 };
 
 namespace {
@@ -110,6 +110,14 @@ int64_t blocks_per_cu() {
     if (v >= 1 && v <= 65536) return v;
   }
   return 65536;
+}
+
+// Between an intake and its zero_adam_step (the device has flipped cur_slot).
+bool in_step(const zero_shard* h) { return h->phase == kReduced || h->phase == kChecked || h->phase == kNormed; }
+
+// The slot holding the latest step counters (see DevScalars).
+const zs::Slot& latest_slot(const zero_shard* h, const zs::DevScalars& sc) {
+  return sc.slot[in_step(h) ? sc.cur_slot & 1u : (sc.cur_slot & 1u) ^ 1u];
 }
 
 zero_status_t sync_read_scalars(zero_shard* h, hipStream_t st, zs::DevScalars* out) {
@@ -329,10 +337,10 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
   if (!h) return fail(ZERO_EINVAL, "null handle");
   if (h->phase == kStepped && h->cast_pending)
     return fail(ZERO_ESTATE, "zero_cast_params of the previous step is pending");
-  int32_t dyn_slot = -1;
+  bool dyn = false;
   if (inv_loss_scale == ZERO_DEVICE_LOSS_SCALE) {
     if (!h->dynamic) return fail(ZERO_EINVAL, "ZERO_DEVICE_LOSS_SCALE needs zero_enable_dynamic_loss_scale");
-    dyn_slot = (int32_t)(h->adam_calls & 1);
+    dyn = true;
   } else if (h->dynamic) {
     return fail(ZERO_EINVAL, "with dynamic loss scaling pass inv_loss_scale = ZERO_DEVICE_LOSS_SCALE");
   } else if (!(inv_loss_scale > 0.0f) || !std::isfinite(inv_loss_scale)) {
@@ -340,6 +348,8 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   DeviceGuard dg(h->device);
+  // the step's first intake advances the device-side counter slot (a repeated one does not)
+  const bool flip = !in_step(h);
   hipError_t e;
   if (h->accumulating) {
     // last micro-step (or none: ZERO_ACCUMULATED) on top of the accumulated gradient.  From one
@@ -352,7 +362,7 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     }
     const bool keep_acc = n_ranks == 0 || n_ranks == 1 || n_ranks == ZERO_ACCUMULATED;
     e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, true, h->reduce_out16, keep_acc,
-                          inv_loss_scale, dyn_slot, h->red, h->sc, h->parts, st);
+                          inv_loss_scale, dyn, flip, h->red, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
     h->grad_source = !keep_acc ? kGradRed : n_ranks == 0 ? kGradAccChunk16 : n_ranks == 1 ? kGradAccFlat16 : kGradAcc;
     h->step_flat_g = n_ranks == 1 ? static_cast<const uint16_t*>(rank_grads[0]) : nullptr;
@@ -361,14 +371,14 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     return fail(ZERO_ESTATE, "ZERO_ACCUMULATED without zero_accumulate_grads in this step");
   } else if (n_ranks == 0) {
     if (!h->has_registered_grads) return fail(ZERO_EINVAL, "n_ranks == 0 needs gradients registered at init");
-    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, nullptr, inv_loss_scale, dyn_slot, h->sc, h->parts, st);
+    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, nullptr, inv_loss_scale, dyn, flip, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("statistics kernel", e);
     h->grad_source = kGradChunk16;
     h->step_flat_g = nullptr;
   } else if (n_ranks == 1) {
     if (!rank_grads || !rank_grads[0]) return fail(ZERO_EINVAL, "rank_grads[0] is null");
     const uint16_t* g = static_cast<const uint16_t*>(rank_grads[0]);
-    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, g, inv_loss_scale, dyn_slot, h->sc, h->parts, st);
+    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, g, inv_loss_scale, dyn, flip, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("statistics kernel", e);
     h->grad_source = kGradFlat16;
     h->step_flat_g = g;
@@ -379,7 +389,7 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
       if (!rank_grads[q]) return fail(ZERO_EINVAL, "rank_grads[" + std::to_string(q) + "] is null");
     if (!h->red) return fail(ZERO_EINVAL, "reducing N_d >= 2 buffers needs bufs.red");
     e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, false, h->reduce_out16, false,
-                          inv_loss_scale, dyn_slot, h->red, h->sc, h->parts, st);
+                          inv_loss_scale, dyn, flip, h->red, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
     h->grad_source = h->reduce_out16 ? kGradRed16 : kGradRed;
     h->step_flat_g = nullptr;
@@ -403,6 +413,13 @@ zero_status_t zero_local_stats(zero_shard_t h, int32_t* found_inf, double* sumsq
   if (s != ZERO_OK) return s;
   if (found_inf) *found_inf = sc.local_flag;
   if (sumsq) *sumsq = sc.local_sumsq;
+  return ZERO_OK;
+}
+
+zero_status_t zero_local_stats_device(zero_shard_t h, double** sumsq, int32_t** found_inf) {
+  if (!h || !sumsq || !found_inf) return fail(ZERO_EINVAL, "null handle or output");
+  *sumsq = &h->sc->local_sumsq;
+  *found_inf = &h->sc->local_flag;
   return ZERO_OK;
 }
 
@@ -456,8 +473,8 @@ zero_status_t zero_adam_step(zero_shard_t h, const zero_adam_hparams_t* hp, int3
   const bool track = h->n_seg > 0 && fuse_cast != 0;
   if (track) ZS_HIP(hipEventRecord(h->wb_event, static_cast<hipStream_t>(stream)));
   hipError_t e = zs::launch_adam_step(h->dtype, h->grad_source, fuse_cast != 0, h->chunks, h->n_chunks,
-                                      h->step_flat_g, h->red, h->master, h->m, h->v, h->sc,
-                                      (int32_t)(h->adam_calls & 1), h->other_flag, h->other_sumsq, h->max_norm,
+                                      h->step_flat_g, h->red, h->master, h->m, h->v, h->sc, h->other_flag,
+                                      h->other_sumsq, h->max_norm,
                                       h->inv, hp, h->dynamic ? &h->dyn_cfg : nullptr, h->n_seg ? &seg : nullptr,
                                       h->grid_main, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("adam kernel", e);
@@ -552,13 +569,14 @@ zero_status_t zero_enable_dynamic_loss_scale(zero_shard_t h, const zero_loss_sca
                              "growth_interval >= 1, min_scale > 0");
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int cur = (int)(h->adam_calls & 1);
   struct {
     float scale;
     int32_t good;
   } v = {cfg->init_scale, 0};
   static_assert(sizeof(v) == 8, "scale and good are adjacent in the slot");
-  ZS_HIP(hipMemcpyAsync(&h->sc->slot[cur].scale, &v, sizeof(v), hipMemcpyHostToDevice, st));
+  // both slots: whichever holds the latest counters, the next intake finds the scale there
+  for (int k = 0; k < 2; ++k)
+    ZS_HIP(hipMemcpyAsync(&h->sc->slot[k].scale, &v, sizeof(v), hipMemcpyHostToDevice, st));
   ZS_HIP(hipStreamSynchronize(st));
   h->dynamic = true;
   h->dyn_cfg = *cfg;
@@ -572,7 +590,7 @@ zero_status_t zero_loss_scale(zero_shard_t h, float* host_scale, int32_t* host_g
   zs::DevScalars sc;
   zero_status_t s = sync_read_scalars(h, static_cast<hipStream_t>(stream), &sc);
   if (s != ZERO_OK) return s;
-  const zs::Slot& cur = sc.slot[h->adam_calls & 1];
+  const zs::Slot& cur = latest_slot(h, sc);
   if (host_scale) *host_scale = cur.scale;
   if (host_good) *host_good = cur.good;
   return ZERO_OK;
@@ -604,7 +622,7 @@ zero_status_t zero_shard_query(zero_shard_t h, int64_t* t, int32_t* last_skipped
   zs::DevScalars sc;
   zero_status_t s = sync_read_scalars(h, static_cast<hipStream_t>(stream), &sc);
   if (s != ZERO_OK) return s;
-  if (t) *t = sc.slot[h->adam_calls & 1].t;
+  if (t) *t = latest_slot(h, sc).t;
   if (last_skipped) *last_skipped = h->adam_calls ? sc.skipped : 0;
   if (last_norm) *last_norm = sc.norm;
   if (last_clip) *last_clip = sc.clip;

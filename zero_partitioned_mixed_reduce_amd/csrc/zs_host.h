@@ -17,9 +17,9 @@ zero_status_t set_error(zero_status_t s, const std::string& msg);
 // Kernel launchers (kernels.hip).
 namespace zs {
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, const uint16_t* flat_g, float inv,
-                          int32_t dyn_slot, DevScalars* sc, const IntakeParts& parts, hipStream_t st);
+                          bool dyn, bool flip, DevScalars* sc, const IntakeParts& parts, hipStream_t st);
 hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
-                         int32_t n_ranks, bool accumulate, bool r16, bool keep_acc, float inv, int32_t dyn_slot,
+                         int32_t n_ranks, bool accumulate, bool r16, bool keep_acc, float inv, bool dyn, bool flip,
                          float* red, DevScalars* sc, const IntakeParts& parts, hipStream_t st);
 hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
                              int32_t n_ranks, bool first, bool r16, float* red, int64_t grid_cap, hipStream_t st);
@@ -35,7 +35,7 @@ hipError_t launch_export(const Chunk* chunks, int64_t n_chunks, const float* src
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* chunks, int64_t n_chunks,
                             const uint16_t* flat_g, const float* red, float* master, float* m, float* v,
-                            DevScalars* sc, int32_t slot, int32_t other_flag, double other_sumsq, float max_norm,
+                            DevScalars* sc, int32_t other_flag, double other_sumsq, float max_norm,
                             float inv, const zero_adam_hparams_t* hp, const zero_loss_scaler_t* dyn,
                             const SegArgs* seg, int64_t grid_cap, hipStream_t st);
 }  // namespace zs

@@ -44,16 +44,24 @@ struct Slot {
 static_assert(sizeof(Slot) == 32, "slot layout");
 
 // Device-resident scalars of the step (first 256 bytes of the workspace).
+//
+// Step counters live in two slots, selected on the device, so that a step needs no
+// host state and can be replayed from a captured graph.  Between steps the latest
+// counters are in slot[cur_slot ^ 1].  The first intake pass of a step reads its
+// loss scale there and its last block flips cur_slot; the Adam pass then reads
+// slot[cur_slot] (the latest) and writes the next counters to slot[cur_slot ^ 1].
+// A repeated intake in the same step does not flip and reads slot[cur_slot].
 struct alignas(256) DevScalars {
   double local_sumsq;  // this rank's sum of u^2 (statistics pass)
   int32_t local_flag;  // this rank's non-finite flag
   uint32_t counter;    // groups of an intake pass that have completed (reset by the last one)
-  Slot slot[2];        // step counters; zero_adam_step reads one and writes the other
+  Slot slot[2];        // step counters (see above)
   double norm;         // report of the last zero_adam_step
   float clip;
   int32_t skipped;
   int64_t report_t;
   uint32_t wait_timeouts;  // segment waits that gave up (see SegState)
+  uint32_t cur_slot;       // 0 or 1 (see above)
 };
 static_assert(sizeof(DevScalars) == 256, "scalar block");
 

@@ -104,6 +104,11 @@ class ZeroShard:
     def zero_local_stats(self):
         return abi.zero_local_stats(self.h, _stream())
 
+    def zero_local_stats_device(self):
+        """(sumsq, found_inf): device addresses of this rank's fp64 sum of squares and int32
+        flag in the workspace, for an in-place all-reduce across ranks."""
+        return abi.zero_local_stats_device(self.h)
+
     def zero_check_overflow(self, other_ranks_found_inf=False, sync=False):
         return abi.zero_check_overflow(self.h, other_ranks_found_inf, _stream(), sync)
 
