@@ -180,3 +180,54 @@ def test_full_size_sampled(cfg, rank, micro, r16):
     print(f"[fullsize] {cfg}: {pos.size} sampled elements match", flush=True)
     wl.shard.close()
     del wl
+
+
+@pytest.mark.parametrize("cfg,rank", [("zero1_7p5b", 63), ("gpt2", 3)])
+def test_full_shard_every_element(cfg, rank):
+    """Every element of a full-size shard after two steps, in the benchmark's launch
+    configuration: the ZeRO-1 7.5B shard of the last rank (fp16, loss scale 2^16, a
+    padded tail) and a middle GPT-2 shard (bf16, 386 tensor pieces).  The oracle runs
+    the whole shard (its own statistics, clip and Adam) and the master, m, v and 16-bit
+    slice are compared bit for bit."""
+    import bench
+    w = recipes.ALL[cfg]()
+    print(f"\n[fullshard] {cfg} rank {rank}: setting up", flush=True)
+    wl = bench.Workload(w, rank)
+    b, valid = wl.info.shard_begin, wl.info.valid_elems
+    for _ in range(2):
+        wl.step()
+    torch.cuda.synchronize()
+    q = wl.shard.query()
+    assert q["t"] == 2 and not q["skipped"]
+
+    print(f"[fullshard] {cfg}: oracle over {valid} elements", flush=True)
+    mstream = synth.stream_id(synth.MASTER)
+    g = host_grad(w, 0, (b, valid))
+    u, flag, local = oracle.grad_stats(w.dtype, [g], wl.inv)
+    assert not flag
+    clip, _ = oracle.clip_coef(local + wl.other_sumsq, w.max_norm)
+    assert q["clip"] == clip, (q, clip)
+    p16 = synth.normal_16(valid, w.dtype, w.seed, mstream, b, w.master_sigma)
+    mst = synth.normal_f32(valid, w.seed, mstream, b, w.master_sigma) if w.master_given else None
+    st = oracle.RankState(w.dtype, p16, mst)
+    hp = oracle.HParams(w.hp["lr"], w.hp["beta1"], w.hp["beta2"], w.hp["eps"], w.hp["weight_decay"])
+    for _ in range(2):
+        oracle.adam(False, u, clip, hp, st.counters, st.w, st.m, st.v)
+        oracle.cast(w.dtype, st.w, st.p16)
+    del u, g
+
+    s = wl.shard
+    for name, exp in (("master", st.w), ("m", st.m), ("v", st.v)):
+        got = s.export(name).cpu().numpy()
+        bad = np.flatnonzero(got.view(np.uint32) != exp.view(np.uint32))
+        assert bad.size == 0, f"{cfg} {name}: {bad.size} elements differ, first at {bad[:5]}"
+        del got
+    if isinstance(wl.params, list):
+        dev = np.concatenate([t.cpu().numpy().view(np.uint16) for t in wl.params])[b:b + valid]
+    else:
+        dev = wl.params[b:b + valid].cpu().numpy().view(np.uint16)
+    bad = np.flatnonzero(dev != st.p16)
+    assert bad.size == 0, f"{cfg} p16: {bad.size} elements differ, first at {bad[:5]}"
+    print(f"[fullshard] {cfg}: all {valid} elements match", flush=True)
+    wl.shard.close()
+    del wl
