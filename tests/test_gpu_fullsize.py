@@ -231,3 +231,76 @@ def test_full_shard_every_element(cfg, rank):
     print(f"[fullshard] {cfg}: all {valid} elements match", flush=True)
     wl.shard.close()
     del wl
+
+
+def test_full_state_every_element():
+    """Every element of the full-state 7.5B shard (N_d = 1, 292 bf16 tensors, 7.5e9
+    elements) after two steps in the benchmark's launch configuration, streamed in
+    2^25-element pieces: the oracle's statistics over the whole shard give the clip,
+    then each piece's master, m, v and 16-bit values from the oracle (two Adam steps
+    and the cast, host threads over pieces) are compared bit for bit with the device."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import bench
+    w = recipes.full7p5b()
+    print("\n[fullstate] setting up", flush=True)
+    wl = bench.Workload(w, 0)
+    b, valid = wl.info.shard_begin, wl.info.valid_elems
+    for _ in range(2):
+        wl.step()
+    torch.cuda.synchronize()
+    q = wl.shard.query()
+    assert q["t"] == 2 and not q["skipped"]
+    print(f"[fullstate] oracle sum of squares over {valid} elements", flush=True)
+    flag, local = oracle_local_sumsq(w, b, valid, wl.inv)
+    assert not flag
+    clip, _ = oracle.clip_coef(local + wl.other_sumsq, w.max_norm)
+    assert q["clip"] == clip, (q, clip)
+    hp = oracle.HParams(w.hp["lr"], w.hp["beta1"], w.hp["beta2"], w.hp["eps"], w.hp["weight_decay"])
+    mstream = synth.stream_id(synth.MASTER)
+    exports = {name: wl.shard.export(name) for name in ("master", "m", "v")}
+    starts = np.array(wl.starts, np.int64)
+
+    def device16(lo, n):
+        """The device's 16-bit parameters of logical shard elements [lo, lo + n)."""
+        parts, a, e = [], b + lo, b + lo + n
+        k = int(np.searchsorted(starts, a, side="right")) - 1
+        while a < e:
+            hi = min(e, int(starts[k + 1]))
+            parts.append(wl.params[k][a - starts[k]:hi - starts[k]])
+            a, k = hi, k + 1
+        return torch.cat(parts).cpu().numpy().view(np.uint16)
+
+    def oracle_piece(blk):
+        lo, n = blk
+        g = host_grad(w, 0, (b + lo, n))
+        u, _, _ = oracle.grad_stats(w.dtype, [g], wl.inv)
+        st = oracle.RankState(w.dtype, synth.normal_16(n, w.dtype, w.seed, mstream, b + lo, w.master_sigma),
+                              synth.normal_f32(n, w.seed, mstream, b + lo, w.master_sigma))
+        for _ in range(2):
+            oracle.adam(False, u, clip, hp, st.counters, st.w, st.m, st.v)
+            oracle.cast(w.dtype, st.w, st.p16)
+        return lo, n, st
+
+    step = 1 << 25
+    blocks = [(lo, min(step, valid - lo)) for lo in range(0, valid, step)]
+    checked = 0
+    synth.set_host_threads(1)
+    try:
+        with ThreadPoolExecutor(16) as ex:
+            for wave in range(0, len(blocks), 16):          # bounded: 16 pieces in memory at a time
+                for lo, n, st in ex.map(oracle_piece, blocks[wave:wave + 16]):
+                    for name, exp in (("master", st.w), ("m", st.m), ("v", st.v)):
+                        got = exports[name][lo:lo + n].cpu().numpy()
+                        bad = np.flatnonzero(got.view(np.uint32) != exp.view(np.uint32))
+                        assert bad.size == 0, f"{name}: {bad.size} elements differ in [{lo}, {lo + n}), first {bad[:5]}"
+                    bad = np.flatnonzero(device16(lo, n) != st.p16)
+                    assert bad.size == 0, f"p16: {bad.size} elements differ in [{lo}, {lo + n}), first {bad[:5]}"
+                    checked += n
+                print(f"[fullstate] {checked} of {valid} elements match", flush=True)
+    finally:
+        synth.set_host_threads(0)
+    assert checked == valid
+    del exports
+    wl.shard.close()
+    del wl
