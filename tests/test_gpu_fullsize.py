@@ -182,13 +182,14 @@ def test_full_size_sampled(cfg, rank, micro, r16):
     del wl
 
 
-@pytest.mark.parametrize("cfg,rank", [("zero1_7p5b", 63), ("gpt2", 3)])
+@pytest.mark.parametrize("cfg,rank", [("zero1_7p5b", 63), ("gpt2", 3), ("reduce8", 7)])
 def test_full_shard_every_element(cfg, rank):
     """Every element of a full-size shard after two steps, in the benchmark's launch
     configuration: the ZeRO-1 7.5B shard of the last rank (fp16, loss scale 2^16, a
-    padded tail) and a middle GPT-2 shard (bf16, 386 tensor pieces).  The oracle runs
-    the whole shard (its own statistics, clip and Adam) and the master, m, v and 16-bit
-    slice are compared bit for bit."""
+    padded tail), a middle GPT-2 shard (bf16, 386 tensor pieces) and the last rank of
+    the 8-way local reduce (fp16, exact zeros shared by all buffers).  The oracle runs
+    the whole shard (its own reduce, statistics, clip and Adam) and the master, m, v
+    and 16-bit slice are compared bit for bit."""
     import bench
     w = recipes.ALL[cfg]()
     print(f"\n[fullshard] {cfg} rank {rank}: setting up", flush=True)
@@ -202,8 +203,9 @@ def test_full_shard_every_element(cfg, rank):
 
     print(f"[fullshard] {cfg}: oracle over {valid} elements", flush=True)
     mstream = synth.stream_id(synth.MASTER)
-    g = host_grad(w, 0, (b, valid))
-    u, flag, local = oracle.grad_stats(w.dtype, [g], wl.inv)
+    nsrc = w.nd if w.grad_mode == "reduce" else 1
+    g = [host_grad(w, qq, (b, valid)) for qq in range(nsrc)]
+    u, flag, local = oracle.grad_stats(w.dtype, g, wl.inv)
     assert not flag
     clip, _ = oracle.clip_coef(local + wl.other_sumsq, w.max_norm)
     assert q["clip"] == clip, (q, clip)
