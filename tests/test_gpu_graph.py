@@ -212,3 +212,49 @@ def test_device_exchange_eager():
         torch.cuda.synchronize()
         assert all(x["skipped"] == (step == 2) for x in res)
         check_after(sim, res, w.max_norm)
+
+
+def test_captured_accumulation_replays():
+    """Two micro-steps per step captured into one graph (an accumulation from a flat
+    buffer, then the intake of a second flat buffer on top of it, the Adam pass
+    recomputing u from the accumulator): four replays with new contents written into the
+    two device buffers between replays, an overflow in the first micro-step of the
+    third replay."""
+    w = recipes.ragged_mini(1)
+    psi = w.psi
+    master = synth.normal_f32(psi, w.seed, synth.stream_id(synth.MASTER), 0, w.master_sigma)
+    p16 = synth.normal_16(psi, w.dtype, w.seed, synth.stream_id(synth.MASTER), 0, w.master_sigma)
+    sim = Sim([psi], 1, w.dtype, p16, master, "flat", with_red=True)
+    sim.p16_initial = p16.copy()
+    hp = hp_of(w.hp)
+
+    def micro(step):
+        gs = [synth.normal_16(psi, w.dtype, w.seed, synth.stream_id(synth.GRAD, 0, 10 * step + k), 0,
+                              w.grad_sigma * 20.0) for k in range(2)]
+        if step == 4:
+            gs[0][psi - 3] = 0xFF80                            # -inf in the first micro-step
+        return gs
+
+    res = sim.step_accumulated([[g] for g in micro(1)], 1.0, w.max_norm, hp)     # eager step 1
+    sim.compare()
+    s = sim.shards[0]
+    bufs = [torch.empty(psi, dtype=torch.int16, device="cuda") for _ in range(2)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        s.zero_accumulate_grads([bufs[0]])
+        s.zero_reduce_grads([bufs[1]], 1.0)
+        s.zero_check_overflow(False)
+        s.zero_grad_norm(0.0, w.max_norm)
+        s.zero_adam_step(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, fuse_cast=True)
+    torch.cuda.synchronize()
+    for step in range(2, 6):
+        gs = micro(step)
+        res = oracle.step_ranks_accumulated(sim.ostates, [[g] for g in gs], sim.begins, 1.0, w.max_norm, hp)
+        for buf, g in zip(bufs, gs):
+            buf.copy_(dev16(g))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert res[0]["skipped"] == (step == 4)
+        check_after(sim, res, w.max_norm)
+    assert sim.ostates[0].counters.t == 4
