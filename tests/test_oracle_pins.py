@@ -784,3 +784,32 @@ def test_accumulation_of_16bit_reduce_outputs():
     assert acc[0] == np.float32(2 + 2.0 ** -6)
     res = oracle.step_ranks_accumulated(states, micro, begins, 1.0, 0.0, hp_of(), reduce_out16=True)
     assert not res[0]["skipped"] and res[0]["local_sumsq"] == (2 + 2.0 ** -6) ** 2
+
+
+def test_adam_1000_steps_drift_against_fp64():
+    """A sanity bound on accumulated rounding: 1000 oracle steps (fp32, every operation
+    rounded) against the same recurrence carried in fp64 from the same fp32
+    hyperparameters and gradients.  The fp32 master stays within 1e-5 of the total
+    change of the weights, and m and v within 1e-5 of their largest values (measured
+    about 1e-6 and below); a wrong bias correction, decay or moment update would be
+    off by orders of magnitude more."""
+    r = np.random.default_rng(7)
+    n = 4096
+    w0 = (r.standard_normal(n) * 0.02).astype(np.float32)
+    hp = oracle.HParams(1e-3, 0.9, 0.999, 1e-8, 0.01)
+    w, m, v = w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    ctr = oracle.Counters.fresh()
+    W, M, V = w0.astype(np.float64), np.zeros(n), np.zeros(n)
+    b1, b2 = float(np.float32(0.9)), float(np.float32(0.999))
+    lr, eps, wd = float(np.float32(1e-3)), float(np.float32(1e-8)), float(np.float32(0.01))
+    for t in range(1, 1001):
+        g = (r.standard_normal(n) * 1e-3).astype(np.float32)
+        oracle.adam(False, g, np.float32(1.0), hp, ctr, w, m, v)
+        G = g.astype(np.float64)
+        M = b1 * M + (1 - b1) * G
+        V = b2 * V + (1 - b2) * G * G
+        W = W - lr * ((M / (1 - b1 ** t)) / (np.sqrt(V / (1 - b2 ** t)) + eps) + wd * W)
+    assert ctr.t == 1000
+    assert np.abs(w - W).max() <= 1e-5 * np.abs(W - w0).max()
+    assert np.abs(m - M).max() <= 1e-5 * np.abs(M).max()
+    assert np.abs(v - V).max() <= 1e-5 * np.abs(V).max()
