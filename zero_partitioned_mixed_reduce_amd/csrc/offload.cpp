@@ -595,7 +595,8 @@ zero_status_t zero_offload_fetch_grads(zero_offload_t h, const void* flat_grad16
   DeviceGuard dg(h->device, h->has_device);
   if (h->dev_stats) {
     // flag and sum of squares on the device, from the gradient still in HBM; the copies follow
-    hipError_t he = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, static_cast<const uint16_t*>(flat_grad16),
+    hipError_t he = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, h->info.valid_elems,
+                                       static_cast<const uint16_t*>(flat_grad16),
                                        inv_loss_scale, false, false, h->sc, h->parts, st);
     if (he == hipSuccess) he = hipEventRecord(h->stats_ev, st);
     if (he != hipSuccess) return hip_fail("device statistics", he);

@@ -371,14 +371,16 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     return fail(ZERO_ESTATE, "ZERO_ACCUMULATED without zero_accumulate_grads in this step");
   } else if (n_ranks == 0) {
     if (!h->has_registered_grads) return fail(ZERO_EINVAL, "n_ranks == 0 needs gradients registered at init");
-    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, nullptr, inv_loss_scale, dyn, flip, h->sc, h->parts, st);
+    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, h->info.valid_elems, nullptr, inv_loss_scale, dyn, flip,
+                           h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("statistics kernel", e);
     h->grad_source = kGradChunk16;
     h->step_flat_g = nullptr;
   } else if (n_ranks == 1) {
     if (!rank_grads || !rank_grads[0]) return fail(ZERO_EINVAL, "rank_grads[0] is null");
     const uint16_t* g = static_cast<const uint16_t*>(rank_grads[0]);
-    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, g, inv_loss_scale, dyn, flip, h->sc, h->parts, st);
+    e = zs::launch_stats16(h->dtype, h->chunks, h->n_chunks, h->info.valid_elems, g, inv_loss_scale, dyn, flip,
+                           h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("statistics kernel", e);
     h->grad_source = kGradFlat16;
     h->step_flat_g = g;
