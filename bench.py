@@ -287,17 +287,23 @@ def cpu_baseline(w, sample, steps, threads=1, piece=1 << 20, keep=False):
     return (n * steps / dt, dt, st) if keep else (n * steps / dt, dt)
 
 
-def cold_cache_steps(wl, steps, flush_bytes=1 << 30):
-    """Median duration (ms) of `steps` steps each timed on its own after a 1 GiB write that
-    evicts the 256 MB Infinity Cache and the L2s: per step, a fill of a scratch buffer, then
-    the step between two HIP events on the step's stream, then a wait for it."""
+def cold_cache_steps(wl, steps, evict="read", flush_bytes=1 << 30):
+    """Median duration (ms) of `steps` steps each timed on its own after a 1 GiB pass over
+    a scratch buffer that evicts the 256 MB Infinity Cache and the L2s: per step, the
+    eviction, then the step between two HIP events on the step's stream, then a wait for
+    it.  evict="read": a reduction over the buffer, which leaves the cache holding clean
+    lines; evict="write": a fill, which leaves up to 256 MB of dirty lines whose
+    write-back then falls inside the timed step."""
     import statistics
 
     import torch
-    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    scratch = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda")
     times = []
     for k in range(steps):
-        scratch.fill_(float(k))
+        if evict == "write":
+            scratch.fill_(float(k))
+        else:
+            torch.sum(scratch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         wl.step()
@@ -687,13 +693,17 @@ def main():
                                "protocol": "after the timed steps: the step captured once into a HIP graph, "
                                            "then replayed back to back, bracketed by synchronisation"}
     if not a.no_cold_cache:
-        cold_ms = cold_cache_steps(wl, a.steps)
+        cold_ms = cold_cache_steps(wl, a.steps, "read")
+        cold_w_ms = cold_cache_steps(wl, a.steps, "write")
         out["cold_cache"] = {"ms_per_step_median": cold_ms, "value": valid / (cold_ms * 1e-3),
                              "hbm_frac_step": step_b * valid / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                             "ms_per_step_median_after_write": cold_w_ms,
                              "steps": a.steps,
-                             "protocol": "after the timed steps: per step a 1 GiB fill of a scratch buffer "
-                                         "(evicts the Infinity Cache and L2s), then the step alone between "
-                                         "two events; median"}
+                             "protocol": "after the timed steps: per step a 1 GiB read of a scratch buffer "
+                                         "(evicts the Infinity Cache and L2s, leaving clean lines), then the "
+                                         "step alone between two events; median.  After a 1 GiB write "
+                                         "instead, the write-back of the dirty lines it leaves falls inside "
+                                         "the step"}
     if not a.no_copy_ceiling:
         del wl
         torch.cuda.empty_cache()
