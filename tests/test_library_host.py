@@ -116,3 +116,23 @@ def test_errors_are_reported():
     # null handles are rejected, not dereferenced
     assert _abi.lib().zero_cast_params(None, None) == _abi.ZERO_EINVAL
     assert "null handle" in zpm.zero_last_error()
+
+
+def test_abi_from_plain_c(tmp_path):
+    """Both headers compile as strict C99 (-Wall -Wextra -pedantic -Werror), and a C program
+    linked against the library gets the documented answers from the host-only calls."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    lib_dir = os.path.dirname(_abi.LIB_PATH)
+    exe = tmp_path / "abi_from_c"
+    src = os.path.join(ROOT, "tests", "c", "abi_from_c.c")
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                        os.path.join(ROOT, "include"), src, "-o", str(exe), "-L", lib_dir, "-lzero_shard",
+                        "-Wl,-rpath," + lib_dir], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "FAIL" not in r.stdout and r.stdout.count("ok ") == 12
