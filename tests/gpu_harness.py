@@ -104,11 +104,11 @@ class Sim:
     """N_d ranks of the HIP path plus the oracle, stepped together."""
 
     def __init__(self, numel, nd, dtype, p16_full, master_full, grad_mode, per_tensor_params=False,
-                 param_misalign=(0,), grad_misalign=(0,), ranks=None, with_red=None, segments=0):
+                 param_misalign=(0,), grad_misalign=(0,), ranks=None, with_red=None, segments=0, align=0):
         self.numel, self.nd, self.dtype, self.grad_mode = list(numel), nd, dtype, grad_mode
         self.psi = sum(numel)
         self.ranks = list(range(nd)) if ranks is None else ranks
-        self.plans = [oracle.plan(numel, nd, r) for r in range(nd)]
+        self.plans = [oracle.plan(numel, nd, r, align or 64) for r in range(nd)]
         self.begins = [p[2] for p in self.plans]
         # oracle side: every rank (the exchange needs all of them)
         self.ostates = []
@@ -137,7 +137,7 @@ class Sim:
                 grads = self.gstore
             red = (grad_mode == "reduce") if with_red is None else with_red
             self.shards[r] = ZeroShard(numel, nd, r, dtype, views if views is not None else store, grads=grads,
-                                       master_init=mi, with_red=red)
+                                       master_init=mi, with_red=red, align=align)
             if segments:
                 self.shards[r].zero_set_segments(segments)
 

@@ -186,6 +186,28 @@ def test_degenerate_hyperparameters(hp):
                     master[b:b + valid].view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("align,mode,nd", [(8, "reduce", 3), (8, "ragged", 5), (256, "reduce", 4), (1024, "ragged", 3)])
+def test_shard_alignment(align, mode, nd):
+    """Shard lengths rounded to `align` elements other than the default 64: 8 (shard
+    boundaries at 16-byte steps of the 16-bit data, so the rank slices start at every
+    phase the kernels peel), 256 and 1024 (larger padding at the last rank).  Every rank
+    against the oracle's partition with the same alignment, two steps."""
+    w = recipes.ragged_mini(nd) if mode == "ragged" else recipes.tiny()
+    numel = w.numel if mode == "ragged" else [100_003]
+    psi = sum(numel)
+    master, p16 = master_of(w, psi)
+    sim = Sim(numel, nd, w.dtype, p16, master, mode, per_tensor_params=(mode == "ragged"), align=align)
+    sim.p16_initial = p16.copy()
+    for r in range(nd):
+        _, S, b, _ = sim.plans[r]
+        assert S % align == 0 and b == r * S
+        assert sim.shards[r].info.shard_elems == S
+    inv = 1.0 / w.loss_scale
+    for step in range(1, 3):
+        sim.step(grads_for(w, step, psi, nd if mode == "reduce" else 1), inv, w.max_norm, hp_of(w.hp))
+        sim.compare()
+
+
 @pytest.mark.parametrize("pmis,gmis", [((1, 3, 5, 7), (0,)), ((2,), (1,)), ((3,), (3,)), ((1, 2), (2, 1))])
 def test_misaligned_tensors(pmis, gmis):
     """Per-tensor parameters and gradients starting at odd element offsets: the

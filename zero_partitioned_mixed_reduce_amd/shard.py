@@ -48,9 +48,9 @@ class ZeroShard:
     """One rank's shard: plan, caller-owned buffers (torch), handle."""
 
     def __init__(self, numel, dp_size, dp_rank, dtype, params, grads=None, master_init=None, with_red=False,
-                 device="cuda"):
+                 device="cuda", align=0):
         self.dtype = dtype
-        self.desc = make_desc(numel, dp_size, dp_rank, dtype, params, grads)
+        self.desc = make_desc(numel, dp_size, dp_rank, dtype, params, grads, align)
         self._params, self._grads = params, grads
         self.info = abi.zero_shard_plan(self.desc)
         n = self.info.state_elems
