@@ -1,10 +1,11 @@
 // gfx950 kernels of the partitioned mixed-precision optimizer step.
 //
 // The kernels walk the shard's chunk table (chunks of at most kChunk elements
-// inside one tensor piece).  The statistics passes use a persistent grid sized
-// by work (block b takes chunks b, b + G, ...; each block ends with one
-// completion atomic, so blocks are few); the Adam pass launches one short-lived
-// block per part of a chunk and lets the hardware dispatcher balance the load.
+// inside one tensor piece).  The intake passes launch one short-lived block per
+// chunk (or per run of a few consecutive chunks on small shards) and combine
+// their sums of squares in a fixed two-level order without float atomics (see
+// finish_stats); the Adam pass launches one short-lived block per part of a
+// chunk.  The hardware dispatcher balances the load in both.
 // Inside a run of elements a block peels at most 3 leading elements, streams
 // the body as 4-element quads -- 8-byte loads and stores of 16-bit data,
 // 16-byte loads and stores of fp32 data, each wave covering 256 consecutive
@@ -29,7 +30,7 @@
 //   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
 //   ZS_REDUCE_NT non-temporal loads of the local reduce's and accumulation's sources
 //   ZS_STATS_PF request the next chunk's table entry before streaming the current chunk
-//               (persistent statistics and reduce passes)
+//               (intake blocks that cover several chunks)
 //   ZS_NT_LOAD  non-temporal loads of the fp32 state (read once per step)
 //   ZS_NT_STORE non-temporal stores of the fp32 state and 16-bit parameters
 //   ZS_ADAM_SPLIT    parts per chunk in the Adam pass (one block per part)
