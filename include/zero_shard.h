@@ -44,6 +44,20 @@
  *     fixed in the graph; see zero_local_stats_device for taking the other
  *     ranks' values from device memory.  Segment tracking counts steps on the
  *     host and is not for replays.
+ *
+ * Typical use, one rank of N_d (error checks omitted):
+ *   zero_shard_plan(&desc, &info);                    sizes: state_elems, workspace_bytes
+ *   allocate master, m, v (and red) of info.state_elems floats, the workspace
+ *   zero_shard_init(&desc, &bufs, master_init_or_NULL, stream, &h);
+ *   per step:
+ *     zero_reduce_grads(h, rank_bufs, N_d, 1.0f / loss_scale, stream);
+ *     exchange this rank's flag and sum of squares with the other ranks, on the
+ *       host (zero_local_stats) or in place on the device (zero_local_stats_device)
+ *     zero_check_overflow(h, other_ranks_found_inf, NULL, stream);
+ *     zero_grad_norm(h, other_ranks_sumsq, max_norm, NULL, stream);
+ *     zero_adam_step(h, &hparams, 1, stream);          16-bit slice written back
+ *     all-gather the 16-bit slices
+ *   zero_shard_destroy(h);
  */
 #ifndef ZERO_SHARD_H
 #define ZERO_SHARD_H
