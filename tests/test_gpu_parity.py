@@ -186,6 +186,24 @@ def test_degenerate_hyperparameters(hp):
                     master[b:b + valid].view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("cap", ["1", "3"])
+def test_capped_grid(cap, monkeypatch):
+    """ZERO_SHARD_BLOCKS_PER_CU caps the streaming grids (init, accumulation, Adam, cast,
+    export) at that many blocks per CU, so every block walks several work items: all
+    ranks of the ragged list with two micro-steps per step, 8 tracked segments, and the
+    cast fused or not, against the oracle."""
+    monkeypatch.setenv("ZERO_SHARD_BLOCKS_PER_CU", cap)
+    w = recipes.ragged_mini(3)
+    psi = w.psi
+    master, p16 = master_of(w, psi)
+    sim = Sim(w.numel, 3, w.dtype, p16, master, "ragged", per_tensor_params=True, with_red=True, segments=8)
+    sim.p16_initial = p16.copy()
+    for step in range(1, 4):
+        sim.step_accumulated(micro_grads(w, step, psi, 1, 2), 1.0, w.max_norm, hp_of(w.hp), fuse=(step != 2),
+                             last_fused=(step != 3))
+        sim.compare()
+
+
 @pytest.mark.parametrize("align,mode,nd", [(8, "reduce", 3), (8, "ragged", 5), (256, "reduce", 4), (1024, "ragged", 3)])
 def test_shard_alignment(align, mode, nd):
     """Shard lengths rounded to `align` elements other than the default 64: 8 (shard
