@@ -136,3 +136,19 @@ def test_abi_from_plain_c(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "FAIL" not in r.stdout and r.stdout.count("ok ") == 12
+
+
+def test_gpu_c_program_compiles():
+    """The plain-C GPU driver of the ABI (tests/c/step_from_c.c) compiles cleanly as C99
+    against the headers and the HIP runtime API (it runs in the GPU tests)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    if gcc is None or not os.path.isdir(os.path.join(rocm, "include", "hip")):
+        pytest.skip("no C compiler or HIP headers")
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "c", "step_from_c.c")], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
