@@ -380,12 +380,12 @@ def copy_ceiling(nbytes=4 << 30, reps=5):
 
 
 def traffic_from_profiles(cfg, rank, adam_launch_bytes):
-    """HBM bytes per Adam launch from the committed rocprofv3 counter summary
-    (profiles/adam_<config>_traffic.txt), when it was taken on the current kernel
-    source and the same shard size; else None."""
+    """HBM bytes per launch of the Adam kernel and of the statistics kernel from the
+    committed rocprofv3 counter summary (profiles/adam_<config>_traffic.txt), when it
+    was taken on the current kernel source and the same shard size; else (None, None)."""
     path = os.path.join(ROOT, "profiles", f"adam_{cfg}_traffic.txt")
     if not os.path.exists(path):
-        return None
+        return None, None
     kv = {}
     with open(path) as f:
         for line in f:
@@ -394,10 +394,11 @@ def traffic_from_profiles(cfg, rank, adam_launch_bytes):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha") != kernel_source_sha():
-        return None
+        return None, None
     if int(kv.get("algorithmic_bytes_per_launch", -1)) != adam_launch_bytes:
-        return None
-    return int(kv["traffic_bytes_per_launch"])
+        return None, None
+    stats = kv.get("stats_traffic_bytes_per_launch")
+    return int(kv["traffic_bytes_per_launch"]), (int(stats) if stats is not None else None)
 
 
 def host_probe_gbps(threads, nbytes=1 << 31):
@@ -638,7 +639,7 @@ def main():
     adam_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps
     adam_bytes = adam_b * valid
     achieved = adam_bytes / (adam_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(a.config, rank, adam_bytes)
+    traffic, stats_traffic = traffic_from_profiles(a.config, rank, adam_bytes)
     out = {
         "metric": METRIC,
         "value": valid / (ms_step * 1e-3),
@@ -671,6 +672,17 @@ def main():
                      "avg_launch_ms": adam_ms},
         "setup_s": setup_s,
     }
+    # the same step rate with the benchmark spec's byte count (28 B/param for the step, plus 2 B per
+    # rank buffer when reducing: the second read of the gradient is not counted)
+    ns_b = 28 + (2 * w.nd if w.grad_mode == "reduce" else 0)
+    out["hbm_gbps_step_28b"] = ns_b * valid / (ms_step * 1e-3) / 1e9
+    out["bytes_per_param_28b"] = ns_b
+    if traffic is not None and stats_traffic is not None and a.micro_steps == 1 and w.grad_mode != "reduce":
+        # counter-measured bytes of the step's two kernels (profiles/), over the measured step time
+        step_traffic = traffic + stats_traffic
+        out["counter_traffic_step"] = {"bytes": step_traffic, "ratio_to_algorithmic": step_traffic / (step_b * valid),
+                                       "gbps": step_traffic / (ms_step * 1e-3) / 1e9,
+                                       "frac": step_traffic / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     if wl.segments:
         out["config"]["segments"] = len(wl.segments)
         copies = a.segment_consumer == "copy" and not isinstance(wl.params, list)

@@ -36,8 +36,8 @@ def test_more_than_one_gpu_is_refused():
 
 def test_traffic_summary_is_tied_to_the_kernel_source():
     # a committed summary is only used for the shard size it was taken on
-    assert bench.traffic_from_profiles("full7p5b", 0, 1) is None
-    assert bench.traffic_from_profiles("no_such_config", 0, 1) is None
+    assert bench.traffic_from_profiles("full7p5b", 0, 1) == (None, None)
+    assert bench.traffic_from_profiles("no_such_config", 0, 1) == (None, None)
 
 
 def test_threaded_oracle_baseline_runs_the_same_step():
@@ -59,3 +59,20 @@ def test_threaded_oracle_baseline_runs_the_same_step():
 def test_host_info_fields():
     h = bench.host_info()
     assert h["nproc"] >= 1 and 1 <= h["usable_cpus"] <= h["nproc"]
+
+
+def test_committed_traffic_summaries():
+    """Where the committed counter summaries of the target workloads match the current
+    kernel source, the benchmark reads the Adam and statistics traffic for their shards,
+    and both are within 5% of the algorithmic bytes (the bar for redundant traffic)."""
+    import pytest
+    found = 0
+    for cfg, valid in (("full7p5b", 7_500_000_000), ("zero1_7p5b", 117_187_520)):
+        adam, stats = bench.traffic_from_profiles(cfg, 0, 28 * valid)
+        if adam is None:
+            continue
+        found += 1
+        assert stats is not None, cfg
+        assert 1.0 <= adam / (28 * valid) <= 1.05 and 1.0 <= stats / (2 * valid) <= 1.05, cfg
+    if not found:
+        pytest.skip("the committed summaries were taken on another kernel source")
