@@ -104,9 +104,15 @@ static uint16_t encode_format(double r, int p, int emin, int bias) {
   return (uint16_t)(((e + bias) << p) | (uint16_t)(r / ldexp(1.0, e - p) - ldexp(1.0, p)));
 }
 
+/* NaN rule of the write-back (the pages are silent on it): every NaN becomes the
+ * format's positive canonical quiet NaN (binary16 0x7E00, bfloat16 0x7FC0),
+ * whatever its sign and payload.  IEEE 754 leaves the sign and payload of a NaN
+ * produced by arithmetic unspecified, and hosts differ (an invalid operation such
+ * as inf - inf gives a negative NaN on x86 and a positive one on the GPU), so a
+ * rule that kept them would make the written bits depend on the machine. */
 uint16_t orc_f32_to_f16(float x) {
+  if (isnan(x)) return 0x7E00;
   uint16_t sign = signbit(x) ? 0x8000 : 0;
-  if (isnan(x)) return sign | 0x7E00;
   double a = fabs((double)x);
   /* the largest finite binary16 is 65504; halfway to 65536 is 65520, which rounds to even (65536): overflow */
   if (a >= 65520.0) return sign | 0x7C00;
@@ -114,8 +120,8 @@ uint16_t orc_f32_to_f16(float x) {
 }
 
 uint16_t orc_f32_to_bf16(float x) {
+  if (isnan(x)) return 0x7FC0; /* the NaN rule above */
   uint16_t sign = signbit(x) ? 0x8000 : 0;
-  if (isnan(x)) return sign | 0x7FC0;
   double a = fabs((double)x);
   /* the largest finite bfloat16 is (2 - 2^-7) * 2^127; from (2 - 2^-8) * 2^127 on it rounds to infinity */
   if (a >= ldexp(2.0 - ldexp(1.0, -8), 127)) return sign | 0x7F80;

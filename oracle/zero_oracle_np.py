@@ -23,13 +23,18 @@ def dec(dtype, h):
 
 
 def enc(dtype, x):
+    """Round to nearest even into the 16-bit format; every NaN becomes the format's
+    positive canonical quiet NaN (0x7E00, 0x7FC0), whatever its sign and payload."""
     x = np.asarray(x, np.float32)
-    if dtype == F16:
-        return x.astype(np.float16).view(np.uint16)
-    b = x.view(np.uint32).astype(np.uint64)
     nan = np.isnan(x)
+    if dtype == F16:
+        with np.errstate(over="ignore"):
+            r = x.astype(np.float16).view(np.uint16).copy()
+        r[nan] = 0x7E00
+        return r
+    b = x.view(np.uint32).astype(np.uint64)
     r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
-    r[nan] = ((b[nan] >> 16) | 0x40).astype(np.uint16)
+    r[nan] = 0x7FC0
     return r
 
 

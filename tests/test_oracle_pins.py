@@ -135,19 +135,45 @@ def _check_encode_chunk(args):
     tdt = torch.float16 if dtype == F16 else torch.bfloat16
     ref = torch.from_numpy(x).to(tdt).view(torch.int16).numpy().view(np.uint16)
     nan = np.isnan(x)
-    inf_bits = 0x7C00 if dtype == F16 else 0x7F80
-    got_nan = (got & 0x7FFF) > inf_bits
-    ok = np.where(nan, got_nan & ((got >> 15) == (x.view(np.uint32) >> 31)), got == ref)
+    canonical = CANONICAL_NAN[dtype]
+    ok = np.where(nan, got == canonical, got == ref)
     return int((~ok).sum())
+
+
+# The write-back's NaN rule (a reading: the pages are silent): every NaN, of either sign
+# and any payload, is written as the format's positive canonical quiet NaN.
+CANONICAL_NAN = {F16: 0x7E00, BF16: 0x7FC0}
 
 
 @pytest.mark.parametrize("dtype", [F16, BF16])
 def test_encode_exhaustive_all_float32(dtype):
     """Every one of the 2^32 float32 bit patterns, against torch's CPU conversion
-    (round to nearest even, subnormals kept, overflow to infinity)."""
+    (round to nearest even, subnormals kept, overflow to infinity) for the non-NaN
+    ones, and against the NaN rule (exactly 0x7E00 / 0x7FC0) for the 2^24 - 2 NaN ones."""
     with ThreadPoolExecutor(8) as ex:
         bad = sum(ex.map(_check_encode_chunk, [(k, dtype) for k in range(256)]))
     assert bad == 0
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_nan_rule_every_nan_pattern_both_oracles(dtype):
+    """Every float32 NaN pattern (both signs, every payload, quiet and signalling) is
+    encoded to the one canonical quiet NaN by the C oracle and by the NumPy mirror;
+    +-inf stay +-inf.  A rule that kept the sign or the payload fails here."""
+    payload = np.arange(1, 1 << 23, dtype=np.uint32)
+    for sign in (0, 1):
+        bits = (np.uint32(sign << 31) | np.uint32(0x7F800000) | payload).astype(np.uint32)
+        x = bits.view(np.float32)
+        assert np.isnan(x).all()
+        assert (oracle.encode16(dtype, x) == CANONICAL_NAN[dtype]).all()
+        assert (onp.enc(dtype, x) == CANONICAL_NAN[dtype]).all()
+    inf = np.array([np.inf, -np.inf], np.float32)
+    exp = [0x7C00, 0xFC00] if dtype == F16 else [0x7F80, 0xFF80]
+    assert list(oracle.encode16(dtype, inf)) == exp and list(onp.enc(dtype, inf)) == exp
+    # the canonical value decodes to a NaN and is a quiet NaN of the format (top fraction bit set)
+    assert np.isnan(oracle.decode16(dtype, np.array([CANONICAL_NAN[dtype]], np.uint16)))[0]
+    frac_bits = 10 if dtype == F16 else 7
+    assert CANONICAL_NAN[dtype] >> (frac_bits - 1) & 1
 
 
 @pytest.mark.parametrize("dtype", [F16, BF16])
