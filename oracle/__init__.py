@@ -288,11 +288,13 @@ def step_ranks(states, rank_grads, begins, inv_loss_scale, max_norm, hp, extra_f
     states[r] holds rank r's shard (valid elements from begins[r]).  rank_grads
     is a list of full flat uint16 buffers: one already-reduced buffer, or one per
     rank to be summed.  Each rank computes its local flag and sum of squares;
-    the exchange gives rank r the OR of the other ranks' flags and the sum of
-    the other ranks' sums of squares in rank order; global = local + others.
+    the exchange gives every rank the same global flag (the OR of all ranks'
+    flags) and the same global sum of squares, the ranks' local sums added in
+    rank order (see _finish_step).
     reduce_out16: the reduce of N_d >= 2 buffers delivers its sum in 16 bits
     (reduce_to16), which the step then takes in.
-    Returns a list of per-rank dicts (flag, local_sumsq, norm, clip, skipped)."""
+    Returns a list of per-rank dicts (flag, local_sumsq, global_sumsq, norm,
+    clip, skipped)."""
     nd = len(states)
     locs = []
     for r, st in enumerate(states):
@@ -305,19 +307,26 @@ def step_ranks(states, rank_grads, begins, inv_loss_scale, max_norm, hp, extra_f
 
 
 def _finish_step(states, locs, nd, max_norm, hp, extra_found_inf):
-    """Exchange of flags and sums between the ranks, then each rank's update and cast."""
+    """Exchange of flags and sums between the ranks, then each rank's update and cast.
+
+    The global decision and norm are formed once and given to every rank: the
+    flag is the OR of all ranks' flags (and extra_found_inf, a flag from outside
+    the simulated ranks); the global sum of squares is 0 + ss_0 + ss_1 + ... +
+    ss_{N_d-1} in fp64, in rank order.  Partition invariance ("DeepSpeed ZeRO",
+    ZeRO Stage 2 数学推导: the shards together make exactly the unpartitioned
+    update) needs the same clip on every rank; a per-rank sum such as ss_r +
+    (sum of the others) can round differently on different ranks."""
+    global_flag = any(loc[1] for loc in locs) or bool(extra_found_inf)
+    global_ss = 0.0
+    for q in range(nd):
+        global_ss = global_ss + locs[q][2]
+    clip, norm = clip_coef(global_ss, max_norm)
     out = []
     for r, st in enumerate(states):
         u, flag, ss = locs[r]
-        other_flag = any(locs[q][1] for q in range(nd) if q != r) or extra_found_inf
-        other_ss = 0.0
-        for q in range(nd):
-            if q != r:
-                other_ss = other_ss + locs[q][2]
-        skip = flag or other_flag
-        clip, norm = clip_coef(ss + other_ss, max_norm)
+        skip = global_flag
         adam(skip, u, clip, hp, st.counters, st.w, st.m, st.v)
         if not skip:
             cast(st.dtype, st.w, st.p16)
-        out.append(dict(flag=flag, local_sumsq=ss, other_sumsq=other_ss, norm=norm, clip=clip, skipped=skip))
+        out.append(dict(flag=flag, local_sumsq=ss, global_sumsq=global_ss, norm=norm, clip=clip, skipped=skip))
     return out

@@ -581,6 +581,25 @@ def test_partition_invariance(nd, mode):
         assert (cat.view(np.uint8) == getattr(whole, name).view(np.uint8)).all(), name
 
 
+def test_global_sum_is_one_rank_order_sum_for_every_rank():
+    """Every rank gets the same global sum of squares, the local sums added in rank
+    order.  Local sums 1, 2^-53, 2^-53 (bf16 gradients 1.0 on rank 0, two of 2^-27 on
+    ranks 1 and 2): in rank order (1 + 2^-53) + 2^-53 rounds to 1 at each addition
+    (ties to even), so every rank must see exactly 1.0; a per-rank form ss_r + (sum
+    of the others) would give rank 0 1 + 2^-52 and the other ranks 1."""
+    nd = 3
+    states, begins, _, _ = make_states(BF16, nd, [3 * 64], 5)
+    g = np.zeros(3 * 64, np.uint16)
+    g[0] = oracle.encode16(BF16, np.array([1.0], np.float32))[0]
+    tiny = oracle.encode16(BF16, np.array([2.0 ** -27], np.float32))[0]
+    g[begins[1]] = g[begins[1] + 1] = g[begins[2]] = g[begins[2] + 1] = tiny
+    res = oracle.step_ranks(states, [g], begins, 1.0, 0.5, hp_of())
+    assert [r["local_sumsq"] for r in res] == [1.0, 2.0 ** -53, 2.0 ** -53]
+    assert all(r["global_sumsq"] == 1.0 for r in res)
+    assert 1.0 + (2.0 ** -53 + 2.0 ** -53) == 1.0 + 2.0 ** -52     # what rank 0's per-rank form would give
+    assert all(r["norm"] == 1.0 and r["clip"] == np.float32(0.5 / (1.0 + 1e-6)) for r in res)
+
+
 # --------------------------------------------------------------------------
 # the two oracles agree bit for bit
 
