@@ -287,7 +287,9 @@ void orc_adam_elems(const float* u, int64_t n, float clip, const orc_hparams* hp
  * rule taken is the standard one: after a step with an overflow the scale is
  * multiplied by `backoff` (not below min_scale) and the count of good steps is
  * reset; after `interval` consecutive good steps it is multiplied by `growth`
- * and the count is reset.  The intake then unscales by inv = 1 / scale (fp32). */
+ * when that product is finite (a scale that grew to infinity would skip every
+ * later step for good) and the count is reset.  The intake then unscales by
+ * inv = 1 / scale (fp32). */
 void orc_loss_scale_update(int skipped, float growth, float backoff, int interval, float min_scale, float* scale,
                            int* good) {
   if (skipped) {
@@ -297,7 +299,8 @@ void orc_loss_scale_update(int skipped, float growth, float backoff, int interva
   } else {
     *good += 1;
     if (*good == interval) {
-      *scale = *scale * growth;
+      float grown = *scale * growth;
+      if (isfinite(grown)) *scale = grown;
       *good = 0;
     }
   }

@@ -723,6 +723,25 @@ def test_loss_scale_against_torch_amp_update():
             assert ls.scale.value == scale.item() and ls.good.value == tracker.item()
 
 
+@pytest.mark.parametrize("interval", [1, 2])
+def test_loss_scale_growth_stops_below_infinity_against_torch(interval):
+    """From 2^126 with growth 2 the scale reaches 2^127, the largest power of two below
+    FLT_MAX, and must stay there: torch's _amp_update_scale_ keeps the old scale when
+    scale * growth is not finite.  Also a growth factor of 3 from near FLT_MAX and a
+    backoff afterwards (the scale must still come down)."""
+    for init, growth in ((2.0 ** 126, 2.0), (1.0e38, 3.0)):
+        ls = oracle.LossScaler(init_scale=init, growth=growth, backoff=0.5, interval=interval, min_scale=2.0 ** -40)
+        scale = torch.full((1,), init, dtype=torch.float32)
+        tracker = torch.zeros(1, dtype=torch.int32)
+        for k in range(12):
+            found = k == 9
+            ls.update(found)
+            torch._amp_update_scale_(scale, tracker, torch.full((1,), float(found)), growth, 0.5, interval)
+            assert ls.scale.value == scale.item() and ls.good.value == tracker.item(), (init, k)
+            assert math.isfinite(ls.scale.value)
+        assert ls.scale.value < 3.5e38
+
+
 def test_loss_scale_closed_forms():
     ls = oracle.LossScaler()                       # 2^initial_scale_power with initial_scale_power = 16
     assert ls.scale.value == 65536.0 and ls.inv == 2.0 ** -16
