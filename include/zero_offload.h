@@ -131,6 +131,15 @@ zero_status_t zero_offload_grad_stats(zero_offload_t h, float inv_loss_scale, in
 zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t* hp, int32_t other_ranks_found_inf,
                                      double other_ranks_sumsq, float max_norm, int32_t push, void* stream);
 
+/* As zero_offload_adam_step, but from the global sum of squares: norm =
+ * sqrt(global_sumsq), with global_sumsq the sum over all ranks of their local
+ * sums (zero_offload_grad_stats), formed once in rank order and given to every
+ * rank, so every rank takes the same clip (see zero_grad_norm_global).  EINVAL
+ * also if global_sumsq is negative. */
+zero_status_t zero_offload_adam_step_global(zero_offload_t h, const zero_adam_hparams_t* hp,
+                                            int32_t other_ranks_found_inf, double global_sumsq, float max_norm,
+                                            int32_t push, void* stream);
+
 /* Enqueues on `stream` the host-to-device copy of bufs.param16 (this rank's
  * valid elements) into the device parameters; nothing after a skipped step.
  * EINVAL on a host-only handle; ESTATE unless the last call was

@@ -178,8 +178,9 @@ zero_status_t zero_segment_range(zero_shard_t h, int32_t k, int64_t* shard_begin
  * watches the segment's flag.  Call it after the write-back was enqueued with
  * segments on (ESTATE otherwise), typically on a stream other than the
  * step's.  If the segment is not complete within about 2 s of polling the wait
- * gives up and the count returned by zero_segment_timeouts increases; after
- * that, waits on this handle return at once. */
+ * gives up and the count returned by zero_segment_timeouts increases (work
+ * after it then runs without that segment's guarantee).  Each wait polls on
+ * its own; an earlier timeout does not shorten later waits. */
 zero_status_t zero_wait_segment(zero_shard_t h, int32_t k, void* stream);
 
 /* Number of segment waits that gave up since init (synchronises the stream). */
@@ -224,7 +225,8 @@ zero_status_t zero_loss_scale(zero_shard_t h, float* host_scale, int32_t* host_g
  * zero_reduce_grads, which adds its own sources (the last micro-step) to acc,
  * or, with n_ranks = ZERO_ACCUMULATED, uses acc as it is, before unscaling.
  * ESTATE after the step's zero_reduce_grads or with a cast pending; EINVAL on
- * bad sources or without bufs.red. */
+ * an n_ranks other than 0, 1 or N_d (dp_size), null pointers, or without
+ * bufs.red. */
 zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks, void* stream);
 
 /* 16-bit output of the local reduce ("DeepSpeed ZeRO", ZeRO Stage 2 基本思想:
@@ -270,8 +272,9 @@ zero_status_t zero_set_reduce_output(zero_shard_t h, int32_t out_16bit);
  *                 rank_grads[0], must stay unchanged until zero_adam_step).
  * u = gradient * inv_loss_scale (fp32), or gradient * (1 / device scale) with
  * ZERO_DEVICE_LOSS_SCALE; flag = any u not finite; sum of squares = sum of u*u
- * in fp64.  rank_grads is a host array of device pointers.  EINVAL on bad
- * n_ranks, null pointers or an inv_loss_scale that is not finite and positive
+ * in fp64.  rank_grads is a host array of device pointers.  EINVAL on an
+ * n_ranks other than 0, 1, N_d (dp_size) or ZERO_ACCUMULATED, on null
+ * pointers, or on an inv_loss_scale that is not finite and positive
  * (or, with dynamic scaling, not ZERO_DEVICE_LOSS_SCALE); ESTATE if the previous
  * step's cast is still pending, or for ZERO_ACCUMULATED with nothing
  * accumulated. */
@@ -303,12 +306,35 @@ zero_status_t zero_local_stats_device(zero_shard_t h, double** sumsq, int32_t** 
 zero_status_t zero_check_overflow(zero_shard_t h, int32_t other_ranks_found_inf, int32_t* host_found_inf,
                                   void* stream);
 
-/* Global L2 norm and clip: norm = sqrt(local sum of squares +
- * other_ranks_sumsq); the clip coefficient is max_norm / (norm + 1e-6) when
- * that is below 1, else 1; max_norm <= 0 disables clipping.  If host_norm is
- * non-NULL the stream is synchronised and the norm stored there. */
+/* Global L2 norm and clip over the whole model's unscaled, reduced gradient, as
+ * if it were one flat buffer (the codezrq ZeRO optimizer page, 一. 优化前,
+ * Temporary buffers: gradient-norm computation runs over all parameters fused
+ * into one buffer; here each rank contributes its shard's sum of squares).
+ * norm = sqrt(this rank's local sum of squares + other_ranks_sumsq); the clip
+ * coefficient is max_norm / (norm + 1e-6) when that is below 1, else 1;
+ * max_norm <= 0 disables clipping (the pages give no clipping rule; this is
+ * the common one).  The device computes it in fp64 when zero_adam_step runs; a
+ * set overflow flag skips the step regardless.  If host_norm is non-NULL the
+ * stream is synchronised and the norm stored there.  Launches nothing.
+ * Since ranks add the same terms in different orders here, the rounding of the
+ * global sum can differ between ranks; zero_grad_norm_global avoids that.
+ * ESTATE unless it follows zero_check_overflow. */
 zero_status_t zero_grad_norm(zero_shard_t h, double other_ranks_sumsq, float max_norm, double* host_norm,
                              void* stream);
+
+/* As zero_grad_norm, but from the global sum of squares: norm =
+ * sqrt(global_sumsq), where global_sumsq is the sum over all N_d ranks of their
+ * local sums (zero_local_stats), formed once by the caller -- in rank order,
+ * 0 + ss_0 + ss_1 + ... -- and given to every rank, so that every rank takes
+ * the same clip coefficient by construction, as the partition-invariance of the
+ * update requires ("DeepSpeed ZeRO", ZeRO Stage 2 数学推导: the shards' updates
+ * together make the unpartitioned update).  This rank's own sum is not added
+ * again (a non-finite local sum, from a non-finite gradient, makes the global
+ * sum non-finite, and the overflow flag skips the step).  host_norm (nullable)
+ * receives the norm without a synchronisation.  EINVAL if global_sumsq is
+ * negative; ESTATE unless it follows zero_check_overflow. */
+zero_status_t zero_grad_norm_global(zero_shard_t h, double global_sumsq, float max_norm, double* host_norm,
+                                    void* stream);
 
 /* Adam on this rank's fp32 master, m and v ("DeepSpeed ZeRO" ZeRO Stage 1,
  * 以 AdaW 为例), with bias correction and decoupled weight decay.  Unless the

@@ -78,14 +78,13 @@ class OffloadSim:
         for h in self.handles:
             h.zero_offload_fetch_grads(inv, src if self.grad_mode == "flat" else None)
             loc.append(h.zero_offload_grad_stats(inv))
+        glob = 0.0
+        for x in loc:
+            glob = glob + x[1]                  # the ranks' local sums, once, in rank order
         for r, h in enumerate(self.handles):
             other_flag = any(loc[q][0] for q in range(self.nd) if q != r)
-            other_ss = 0.0
-            for q in range(self.nd):
-                if q != r:
-                    other_ss = other_ss + loc[q][1]
-            h.zero_offload_adam_step(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, other_flag, other_ss,
-                                     max_norm, push=fused_push)
+            h.zero_offload_adam_step_global(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, other_flag, glob,
+                                            max_norm, push=fused_push)
             if not fused_push:
                 h.zero_offload_push_params()
             q = h.query()

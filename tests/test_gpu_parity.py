@@ -8,6 +8,8 @@ exact, norm within 1e-6 relative (local sums of squares within 1e-9).  Past
 that bar the values are also required to be bit-exact: the kernels take the
 oracle's operation order with correctly rounded fp32 arithmetic.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -15,7 +17,7 @@ import torch
 import oracle
 import synth
 from synth import recipes
-from tests.gpu_harness import Sim, dev16, host16
+from tests.gpu_harness import Layout, Sim, dev16, host16
 
 pytestmark = pytest.mark.gpu
 F16, BF16 = oracle.F16, oracle.BF16
@@ -744,3 +746,183 @@ def test_reduce16_api():
     s.zero_set_reduce_output(False)
     torch.cuda.synchronize()
     s.close()
+
+
+# --------------------------------------------------------------------------
+# the write-back's NaN rule: every NaN is written as the canonical quiet NaN
+
+
+def _nan_payload_values(n, seed):
+    """n float32 values mixing payload NaNs of both signs (quiet and signalling), +-inf
+    and ordinary N(0, 0.02) values."""
+    r = np.random.default_rng(seed)
+    x = (r.standard_normal(n) * 0.02).astype(np.float32)
+    bits = x.view(np.uint32)
+    kind = r.integers(0, 6, size=n)
+    payload = r.integers(1, 1 << 23, size=n, dtype=np.uint32)
+    sign = r.integers(0, 2, size=n, dtype=np.uint32) << 31
+    nan_bits = sign | np.uint32(0x7F800000) | payload
+    bits[kind == 0] = nan_bits[kind == 0]
+    bits[kind == 1] = np.uint32(0x7F800000) | sign[kind == 1]            # +-inf
+    return x
+
+
+@pytest.mark.parametrize("dtype,fuse", [(F16, True), (F16, False), (BF16, True), (BF16, False)])
+def test_nan_and_inf_master_write_back(dtype, fuse):
+    """2 ranks; the given fp32 master holds payload NaNs of both signs and +-inf in both
+    ranks' slices.  After two steps every NaN and inf master value has become a NaN (the
+    decoupled decay of an infinite weight is inf - inf) and the 16-bit slice holds exactly
+    the canonical quiet NaN there; everything else bit-exact with the oracle."""
+    w = recipes.tiny()
+    psi, nd = 70_001, 2
+    master = _nan_payload_values(psi, 7 + dtype)
+    p16 = oracle.encode16(dtype, master)
+    sim = Sim([psi], nd, dtype, p16, master, "flat")
+    sim.p16_initial = p16.copy()
+    hp = hp_of(w.hp)
+    for step in (1, 2):
+        g = synth.normal_16(psi, dtype, w.seed, synth.stream_id(synth.GRAD, 0, step), 0, 1e-3)
+        res = sim.step([g], 1.0, w.max_norm, hp, fuse=fuse)
+        assert not any(x["skipped"] for x in res)
+        sim.compare()
+    canonical = 0x7E00 if dtype == F16 else 0x7FC0
+    nonfinite = ~np.isfinite(master)
+    assert nonfinite.sum() > psi // 4
+    for r in sim.ranks:
+        _, _, b, valid = sim.plans[r]
+        store, views = sim.params[r]
+        got = Layout.flat_of(views if views is not None else store)[b:b + valid]
+        assert (got[nonfinite[b:b + valid]] == canonical).all()
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_nan_payload_16bit_params_upcast(dtype):
+    """No master given: the master is the upcast of 16-bit parameters holding payload NaNs
+    and +-inf; the step writes the canonical NaN back wherever the master is NaN."""
+    w = recipes.tiny()
+    psi, nd = 40_003, 2
+    r = np.random.default_rng(11)
+    p16 = oracle.encode16(dtype, (r.standard_normal(psi) * 0.02).astype(np.float32))
+    e_bits, f_bits = (5, 10) if dtype == F16 else (8, 7)
+    exp_all = ((1 << e_bits) - 1) << f_bits
+    pick = r.integers(0, 5, size=psi)
+    pay = r.integers(1, 1 << f_bits, size=psi).astype(np.uint16)
+    sgn = (r.integers(0, 2, size=psi) << 15).astype(np.uint16)
+    p16[pick == 0] = (sgn | np.uint16(exp_all) | pay)[pick == 0]
+    p16[pick == 1] = (sgn | np.uint16(exp_all))[pick == 1]
+    sim = Sim([psi], nd, dtype, p16, None, "flat")
+    sim.p16_initial = p16.copy()
+    g = synth.normal_16(psi, dtype, w.seed, synth.stream_id(synth.GRAD, 0, 1), 0, 1e-3)
+    res = sim.step([g], 1.0, w.max_norm, hp_of(w.hp))
+    assert not any(x["skipped"] for x in res)
+    sim.compare()
+
+
+# --------------------------------------------------------------------------
+# the global sum of squares: one rank-order sum given to every rank
+
+
+def test_global_sum_gives_every_rank_the_same_clip():
+    """Local sums 1, 2^-53, 2^-53 (bf16 gradients 1.0 on rank 0, two of 2^-27 on ranks 1
+    and 2): with zero_grad_norm_global every rank takes norm 1 and the same clip, and
+    the state is bit-exact with the oracle's rank-order reading."""
+    psi, nd = 3 * 64, 3
+    master, _ = master_of(recipes.tiny(), psi)
+    p16 = oracle.encode16(BF16, master)
+    sim = Sim([psi], nd, BF16, p16, master, "flat")
+    sim.p16_initial = p16.copy()
+    g = np.zeros(psi, np.uint16)
+    g[0] = oracle.encode16(BF16, np.array([1.0], np.float32))[0]
+    tiny = oracle.encode16(BF16, np.array([2.0 ** -27], np.float32))[0]
+    S = sim.plans[0][1]
+    g[S] = g[S + 1] = g[2 * S] = g[2 * S + 1] = tiny
+    res = sim.step([g], 1.0, 0.5, hp_of(recipes.tiny().hp))
+    assert all(x["global_sumsq"] == 1.0 for x in res)
+    qs = [sim.shards[r].query() for r in range(nd)]
+    assert all(q["norm"] == 1.0 for q in qs) and len({q["clip"] for q in qs}) == 1
+    sim.compare()
+
+
+def test_others_norm_mode_on_exact_sums():
+    """The older per-rank form (zero_grad_norm with the other ranks' sum) on gradients
+    whose squares and sums are exact in fp64 in any order (multiples of 2^-8 up to 1/4,
+    unscaled by 2^-10), so it must agree with the oracle's rank-order global sum bit for
+    bit; clipping active."""
+    w = recipes.tiny()
+    psi, nd = 200_003, 4
+    master, p16 = master_of(w, psi)
+    sim = Sim([psi], nd, F16, p16, master, "reduce")
+    sim.norm_mode = "others"
+    sim.p16_initial = p16.copy()
+    r = np.random.default_rng(5)
+    for step in (1, 2):
+        g = [oracle.encode16(F16, (r.integers(-64, 65, size=psi) * 2.0 ** -8).astype(np.float32))
+             for _ in range(nd)]
+        res = sim.step(g, 1.0 / 1024, 1e-3, hp_of(w.hp))
+        assert not any(x["skipped"] for x in res) and res[0]["clip"] < 1.0
+        sim.compare()
+
+
+# --------------------------------------------------------------------------
+# argument checks that need a handle (and so a device)
+
+
+def test_reduce_rejects_a_fan_in_other_than_the_ranks():
+    from zero_partitioned_mixed_reduce_amd import ZeroError
+    from zero_partitioned_mixed_reduce_amd._abi import ZERO_EINVAL
+    from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
+    from zero_partitioned_mixed_reduce_amd import _abi
+    w = recipes.tiny()
+    psi, nd = 8192, 4
+    _, p16 = master_of(w, psi)
+    g = [dev16(x) for x in grads_for(w, 1, psi, nd)]
+    s = ZeroShard([psi], nd, 1, F16, dev16(p16), with_red=True)
+    for bad in (g[:3], g[:2], g + g[:1]):                         # N_d - 1, 2, N_d + 1 buffers
+        with pytest.raises(ZeroError) as e:
+            s.zero_reduce_grads(bad, 1.0)
+        assert e.value.status == ZERO_EINVAL and "dp_size" in str(e.value)
+        with pytest.raises(ZeroError) as e:
+            s.zero_accumulate_grads(bad)
+        assert e.value.status == ZERO_EINVAL
+    arr = (ctypes.c_void_p * nd)(*[x.data_ptr() for x in g])
+    for n in (-2, -5, 65):
+        assert _abi.lib().zero_reduce_grads(s.h, arr, n, 1.0, None) == ZERO_EINVAL
+        assert _abi.lib().zero_accumulate_grads(s.h, arr, n, None) == ZERO_EINVAL
+    with pytest.raises(ZeroError) as e:
+        s.zero_grad_norm_global(-1.0, 1.0)                        # outside a step: order first
+    s.zero_reduce_grads(g, 1.0)                                   # N_d buffers: accepted
+    s.zero_check_overflow(False)
+    for bad in (-1.0, -float("inf")):
+        with pytest.raises(ZeroError) as e:
+            s.zero_grad_norm_global(bad, 1.0)
+        assert e.value.status == ZERO_EINVAL
+    s.zero_grad_norm_global(0.0, 1.0)
+    s.zero_adam_step(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    torch.cuda.synchronize()
+    assert s.query()["t"] == 1
+    s.close()
+
+
+# --------------------------------------------------------------------------
+# the dynamic loss scale never grows to infinity
+
+
+def test_dynamic_loss_scale_growth_stops_below_infinity():
+    """From 2^126 with growth 2 every good step: 2^127, then the growth would overflow and
+    the scale stays at 2^127 (torch's rule); an overflow backs it off to 2^126; state and
+    scale checked against the oracle each step."""
+    w = recipes.tiny()
+    psi, nd = 50_001, 2
+    master, p16 = master_of(w, psi)
+    sim = Sim([psi], nd, BF16, p16, master, "flat")
+    sim.p16_initial = p16.copy()
+    sim.enable_dynamic(init_scale=2.0 ** 126, growth=2.0, backoff=0.5, interval=1, min_scale=1.0)
+    expect = {1: 2.0 ** 127, 2: 2.0 ** 127, 3: 2.0 ** 127, 4: 2.0 ** 126, 5: 2.0 ** 127}
+    for step in range(1, 6):
+        g = synth.normal_16(psi, BF16, w.seed, synth.stream_id(synth.GRAD, 0, step), 0, 1e30)
+        if step == 4:
+            _poison(g, psi // 2, BF16)
+        res = sim.step([g], None, w.max_norm, hp_of(w.hp))
+        assert all(x["skipped"] == (step == 4) for x in res)
+        assert sim.scaler.scale.value == expect[step], step
+        sim.compare()

@@ -2,8 +2,9 @@
 the CPU: host-only handles of every simulated rank stepped next to the oracle
 on the same seeded inputs, element by element.
 
-The exchange between ranks (OR of flags, the other ranks' sums of squares in
-rank order) is done here for both sides, each from its own local results.
+The exchange between ranks (OR of flags; the global sum of squares, the ranks'
+local sums added once in rank order) is done here for both sides, each from its
+own local results.
 """
 import numpy as np
 import pytest
@@ -46,6 +47,8 @@ class HostSim:
             for r, h in enumerate(self.handles):
                 h.host16("param16")[:] = self.ostates[r].p16
 
+    norm_mode = "global"   # "others": each rank passes the sum of the other ranks' sums instead
+
     def step(self, g_full, inv, max_norm, hp=HP, extra_found_inf=False):
         hpo = oracle.HParams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
         begins = [p[2] for p in self.plans]
@@ -55,15 +58,23 @@ class HostSim:
             _, _, b, valid = self.plans[r]
             h.host16("grad16")[:] = g_full[b:b + valid]
             loc.append(h.zero_offload_grad_stats(inv))
+        glob = 0.0
+        for x in loc:
+            glob = glob + x[1]                  # the ranks' local sums, once, in rank order
         for r, h in enumerate(self.handles):
             other_flag = any(loc[q][0] for q in range(self.nd) if q != r) or extra_found_inf
-            other_ss = 0.0
-            for q in range(self.nd):
-                if q != r:
-                    other_ss = other_ss + loc[q][1]
-            h.zero_offload_adam_step(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"],
-                                     other_ranks_found_inf=other_flag, other_ranks_sumsq=other_ss,
-                                     max_norm=max_norm, push=False)
+            if self.norm_mode == "global":
+                h.zero_offload_adam_step_global(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"],
+                                                other_ranks_found_inf=other_flag, global_sumsq=glob,
+                                                max_norm=max_norm, push=False)
+            else:
+                other_ss = 0.0
+                for q in range(self.nd):
+                    if q != r:
+                        other_ss = other_ss + loc[q][1]
+                h.zero_offload_adam_step(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"],
+                                         other_ranks_found_inf=other_flag, other_ranks_sumsq=other_ss,
+                                         max_norm=max_norm, push=False)
             q = h.query()
             valid = self.plans[r][3]
             assert loc[r][0] == res[r]["flag"], (r, loc[r], res[r])
@@ -267,3 +278,52 @@ def test_offload_call_order_and_errors():
     with pytest.raises(zpm.ZeroError):
         _abi.zero_offload_init(d, _abi.zero_offload_bufs_t(), None, 0, None)
     assert _abi.lib().zero_offload_destroy(None) == _abi.ZERO_EINVAL
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_offload_nan_and_inf_master_write_back(dtype):
+    """A given master holding payload NaNs of both signs and +-inf: after a step the host
+    loop writes exactly the canonical quiet NaN (0x7E00 / 0x7FC0) wherever the master
+    became NaN, as the oracle does; finite values bit-exact."""
+    n = 50_017
+    r = np.random.default_rng(3 + dtype)
+    master = (r.standard_normal(n) * 0.02).astype(np.float32)
+    bits = master.view(np.uint32)
+    kind = r.integers(0, 5, size=n)
+    sign = r.integers(0, 2, size=n, dtype=np.uint32) << 31
+    bits[kind == 0] = (sign | np.uint32(0x7F800000) | r.integers(1, 1 << 23, size=n, dtype=np.uint32))[kind == 0]
+    bits[kind == 1] = (sign | np.uint32(0x7F800000))[kind == 1]
+    st = oracle.RankState(dtype, oracle.encode16(dtype, master), master)
+    h = ZeroOffload([n], 1, 0, dtype, master_init=master)
+    g = grads(n, dtype, 0x5EED0600, 1, 1e-3)
+    h.host16("grad16")[:] = g
+    flag, ss = h.zero_offload_grad_stats(1.0)
+    u, oflag, oss = oracle.grad_stats(dtype, [g], 1.0)
+    assert flag == oflag is False
+    clip, _ = oracle.clip_coef(oss, 1.0)
+    h.zero_offload_adam_step_global(**HP, global_sumsq=ss, max_norm=1.0, push=False)
+    oracle.adam(False, u, clip, oracle.HParams(HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"]),
+                st.counters, st.w, st.m, st.v)
+    oracle.cast(dtype, st.w, st.p16)
+    assert_f32_close(h.host("master"), st.w, "master")
+    got16 = h.host16("param16")
+    assert (got16 == st.p16).all()
+    nan_w = np.isnan(st.w)
+    assert nan_w.sum() > n // 5 and (got16[nan_w] == (0x7E00 if dtype == F16 else 0x7FC0)).all()
+    h.close()
+
+
+def test_offload_others_norm_mode_on_exact_sums():
+    """The per-rank form (zero_offload_adam_step with the other ranks' sum) on gradients
+    whose squares and sums are exact in any order: bit-exact with the oracle's rank-order
+    global sum; clipping active."""
+    numel, nd, dtype, seed = [60_001], 3, F16, 0x5EED0700
+    sim = HostSim(numel, nd, dtype, seed)
+    sim.norm_mode = "others"
+    r = np.random.default_rng(8)
+    for _ in range(2):
+        g = oracle.encode16(F16, (r.integers(-64, 65, size=sim.psi) * 2.0 ** -8).astype(np.float32))
+        res = sim.step(g, 1.0 / 1024, 1e-3)
+        assert not any(x["skipped"] for x in res) and res[0]["clip"] < 1.0
+        sim.compare()
+    sim.close()

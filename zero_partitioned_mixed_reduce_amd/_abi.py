@@ -66,6 +66,8 @@ _PROTOS = {
     "zero_check_overflow": [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p],
     "zero_grad_norm": [ctypes.c_void_p, ctypes.c_double, ctypes.c_float, ctypes.POINTER(ctypes.c_double),
                        ctypes.c_void_p],
+    "zero_grad_norm_global": [ctypes.c_void_p, ctypes.c_double, ctypes.c_float, ctypes.POINTER(ctypes.c_double),
+                              ctypes.c_void_p],
     "zero_adam_step": [ctypes.c_void_p, ctypes.POINTER(zero_adam_hparams_t), ctypes.c_int32, ctypes.c_void_p],
     "zero_cast_params": [ctypes.c_void_p, ctypes.c_void_p],
     "zero_shard_info": [ctypes.c_void_p, ctypes.POINTER(zero_shard_info_t)],
@@ -89,6 +91,8 @@ _PROTOS = {
                                 ctypes.POINTER(ctypes.c_double)],
     "zero_offload_adam_step": [ctypes.c_void_p, ctypes.POINTER(zero_adam_hparams_t), ctypes.c_int32, ctypes.c_double,
                                ctypes.c_float, ctypes.c_int32, ctypes.c_void_p],
+    "zero_offload_adam_step_global": [ctypes.c_void_p, ctypes.POINTER(zero_adam_hparams_t), ctypes.c_int32,
+                                      ctypes.c_double, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p],
     "zero_offload_push_params": [ctypes.c_void_p, ctypes.c_void_p],
     "zero_offload_query": [ctypes.c_void_p, c_i64p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_float)],
@@ -189,6 +193,12 @@ def zero_grad_norm(h, other_ranks_sumsq, max_norm, stream, sync=False):
     return out.value if sync else None
 
 
+def zero_grad_norm_global(h, global_sumsq, max_norm, stream, sync=False):
+    out = ctypes.c_double(float("nan"))
+    _call("zero_grad_norm_global", h, global_sumsq, max_norm, ctypes.byref(out) if sync else None, stream)
+    return out.value if sync else None
+
+
 def zero_adam_step(h, hp, fuse_cast, stream):
     _call("zero_adam_step", h, ctypes.byref(hp), int(bool(fuse_cast)), stream)
 
@@ -274,6 +284,10 @@ def zero_offload_grad_stats(h, inv_loss_scale):
 
 def zero_offload_adam_step(h, hp, other_ranks_found_inf, other_ranks_sumsq, max_norm, push, stream):
     _call("zero_offload_adam_step", h, ctypes.byref(hp), int(bool(other_ranks_found_inf)), other_ranks_sumsq,
+          max_norm, int(bool(push)), stream)
+
+def zero_offload_adam_step_global(h, hp, other_ranks_found_inf, global_sumsq, max_norm, push, stream):
+    _call("zero_offload_adam_step_global", h, ctypes.byref(hp), int(bool(other_ranks_found_inf)), global_sumsq,
           max_norm, int(bool(push)), stream)
 
 

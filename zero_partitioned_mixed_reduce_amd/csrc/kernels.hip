@@ -90,14 +90,19 @@ __device__ __forceinline__ float dec16(uint32_t h) {
   }
 }
 
+// Round to nearest even into the 16-bit format.  Every NaN, whatever its sign and
+// payload, becomes the format's positive canonical quiet NaN (0x7FC0, 0x7E00): the
+// sign and payload of an arithmetic NaN are not fixed by IEEE 754 and differ
+// between machines, so keeping them would make the written bits machine-dependent.
 template <int DT>
 __device__ __forceinline__ uint32_t enc16(float x) {
   if constexpr (DT == ZERO_BF16) {
     uint32_t u = __float_as_uint(x);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // quiet NaN
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;           // canonical quiet NaN
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;                   // round to nearest even
   } else {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);      // v_cvt_f16_f32, RNE
+    const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);  // v_cvt_f16_f32, RNE
+    return __builtin_isnan(x) ? 0x7E00u : h;                         // canonical quiet NaN
   }
 }
 
@@ -720,7 +725,8 @@ struct AdamArgs {
   float* v;
   DevScalars* sc;
   int32_t other_flag;
-  double other_sumsq;
+  double other_sumsq;      // the other ranks' sum of squares, or (sumsq_global) the global sum
+  int32_t sumsq_global;
   float max_norm;
   float inv;
   float lr, beta1, beta2, eps, wd;
@@ -780,11 +786,11 @@ __device__ __forceinline__ void seg_publish_all(const SegArgs& g) {
 
 // One lane polls segment k until step `epoch` has published it, sleeping
 // between polls; after max_polls it gives up and counts a timeout, so the
-// wait always ends.  Once a wait has timed out, later ones return at once.
+// wait always ends.  Every wait polls on its own: an earlier timeout does not
+// shorten a later wait.
 __global__ void seg_wait_kernel(const SegState* seg, int32_t k, uint64_t epoch, int64_t max_polls,
                                 DevScalars* sc) {
   if (threadIdx.x != 0) return;
-  if (__hip_atomic_load(&sc->wait_timeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
   for (int64_t n = 0;; ++n) {
     // relaxed polls (device scope, no cache invalidation each time); one acquire at the end
     const uint64_t e = __hip_atomic_load(&seg[k].epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -805,7 +811,7 @@ __global__ void seg_wait_kernel(const SegState* seg, int32_t k, uint64_t epoch, 
 __device__ __forceinline__ int step_scalars(const AdamArgs& a, AdamScalars& s, Slot& next, double& norm) {
   const DevScalars* sc = a.sc;
   const int skip = (sc->local_flag | a.other_flag) != 0;
-  norm = sqrt(sc->local_sumsq + a.other_sumsq);
+  norm = sqrt(a.sumsq_global ? a.other_sumsq : sc->local_sumsq + a.other_sumsq);
   float clip = 1.0f;
   if (a.max_norm > 0.0f) {
     const double c = (double)a.max_norm / (norm + 1e-6);
@@ -827,7 +833,8 @@ __device__ __forceinline__ int step_scalars(const AdamArgs& a, AdamScalars& s, S
     } else {
       next.good = cur.good + 1;
       if (next.good == a.interval) {
-        next.scale = cur.scale * a.growth;
+        const float grown = cur.scale * a.growth;
+        if (__builtin_isfinite(grown)) next.scale = grown;  // never grow to infinity
         next.good = 0;
       }
     }
@@ -1223,7 +1230,7 @@ hipError_t launch_adam(int dtype, int grad_source, bool cast, const AdamArgs& a,
 
 hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* chunks, int64_t n_chunks,
                             const uint16_t* flat_g, const float* red, float* master, float* m, float* v,
-                            DevScalars* sc, int32_t other_flag, double other_sumsq, float max_norm,
+                            DevScalars* sc, int32_t other_flag, double other_sumsq, bool sumsq_global, float max_norm,
                             float inv, const zero_adam_hparams_t* hp, const zero_loss_scaler_t* dyn,
                             const SegArgs* seg, int64_t grid_cap, hipStream_t st) {
   AdamArgs a;
@@ -1237,6 +1244,7 @@ hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* 
   a.sc = sc;
   a.other_flag = other_flag;
   a.other_sumsq = other_sumsq;
+  a.sumsq_global = sumsq_global ? 1 : 0;
   a.max_norm = max_norm;
   a.inv = inv;
   a.lr = hp->lr;

@@ -157,22 +157,21 @@ ZO_AVX512 inline __m512 dec16(__m256i h) {
   else return _mm512_cvtph_ps(h);
 }
 
-// Round to nearest even into the 16-bit format; NaN becomes the format's
-// canonical quiet NaN with the input's sign.
+// Round to nearest even into the 16-bit format; every NaN becomes the format's
+// positive canonical quiet NaN (0x7FC0, 0x7E00), whatever its sign and payload, as
+// on the device.
 template <int DT>
 ZO_AVX512 inline __m256i enc16(__m512 w) {
   const __m512i u = _mm512_castps_si512(w);
   const __mmask16 nan = _mm512_cmp_ps_mask(w, w, _CMP_UNORD_Q);
-  const __m512i sign = _mm512_and_si512(_mm512_srli_epi32(u, 16), _mm512_set1_epi32(0x8000));
   if constexpr (DT == ZERO_BF16) {
     const __m512i lsb = _mm512_and_si512(_mm512_srli_epi32(u, 16), _mm512_set1_epi32(1));
     __m512i r = _mm512_srli_epi32(_mm512_add_epi32(_mm512_add_epi32(u, _mm512_set1_epi32(0x7FFF)), lsb), 16);
-    r = _mm512_mask_mov_epi32(r, nan, _mm512_or_si512(sign, _mm512_set1_epi32(0x7FC0)));
+    r = _mm512_mask_mov_epi32(r, nan, _mm512_set1_epi32(0x7FC0));
     return _mm512_cvtepi32_epi16(r);
   } else {
     const __m256i h = _mm512_cvtps_ph(w, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
-    const __m256i qnan = _mm512_cvtepi32_epi16(_mm512_or_si512(sign, _mm512_set1_epi32(0x7E00)));
-    return _mm256_mask_mov_epi16(h, nan, qnan);
+    return _mm256_mask_mov_epi16(h, nan, _mm256_set1_epi16(0x7E00));
   }
 }
 
@@ -693,9 +692,13 @@ zero_status_t zero_offload_grad_stats(zero_offload_t h, float inv_loss_scale, in
   return ZERO_OK;
 }
 
-zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t* hp, int32_t other_ranks_found_inf,
-                                     double other_ranks_sumsq, float max_norm, int32_t push, void* stream) {
+namespace {
+// The step of zero_offload_adam_step / zero_offload_adam_step_global: sumsq is the other
+// ranks' sum of squares (global false) or the global sum.
+zero_status_t offload_adam_step(zero_offload_t h, const zero_adam_hparams_t* hp, int32_t other_ranks_found_inf,
+                                double sumsq, bool global, float max_norm, int32_t push, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  if (global && sumsq < 0.0) return fail(ZERO_EINVAL, "global_sumsq must not be negative");
   if (!hp) return fail(ZERO_EINVAL, "null hparams");
   if (push && !h->has_device) return fail(ZERO_EINVAL, "push needs device parameters (host-only handle)");
   if (h->phase != kStats) return fail(ZERO_ESTATE, "zero_offload_adam_step needs zero_offload_grad_stats first");
@@ -706,7 +709,7 @@ zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t
   zero_status_t rs = wait_push(h);
   if (rs != ZERO_OK) return rs;
   const int skip = (h->local_flag | (other_ranks_found_inf != 0)) != 0;
-  const double norm = sqrt(h->local_sumsq + other_ranks_sumsq);
+  const double norm = sqrt(global ? sumsq : h->local_sumsq + sumsq);
   float clip = 1.0f;
   if (max_norm > 0.0f) {
     const double c = (double)max_norm / (norm + 1e-6);
@@ -799,6 +802,18 @@ zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t
   }
   h->pushed = push && rs == ZERO_OK;
   return rs;
+}
+}  // namespace
+
+zero_status_t zero_offload_adam_step(zero_offload_t h, const zero_adam_hparams_t* hp, int32_t other_ranks_found_inf,
+                                     double other_ranks_sumsq, float max_norm, int32_t push, void* stream) {
+  return offload_adam_step(h, hp, other_ranks_found_inf, other_ranks_sumsq, false, max_norm, push, stream);
+}
+
+zero_status_t zero_offload_adam_step_global(zero_offload_t h, const zero_adam_hparams_t* hp,
+                                            int32_t other_ranks_found_inf, double global_sumsq, float max_norm,
+                                            int32_t push, void* stream) {
+  return offload_adam_step(h, hp, other_ranks_found_inf, global_sumsq, true, max_norm, push, stream);
 }
 
 zero_status_t zero_offload_push_params(zero_offload_t h, void* stream) {

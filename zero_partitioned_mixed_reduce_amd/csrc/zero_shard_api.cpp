@@ -82,7 +82,8 @@ struct zero_shard {
   const uint16_t* step_flat_g;
   float inv;
   int32_t other_flag;
-  double other_sumsq;
+  double other_sumsq;  // the other ranks' sum of squares, or (sumsq_global) the global sum
+  bool sumsq_global;   // zero_grad_norm_global: other_sumsq is the global sum, the local one is not added
   float max_norm;
   int64_t adam_calls;  // zero_adam_step calls (the segments' epoch)
 };
@@ -288,13 +289,17 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
 }
 
 namespace {
-// Checks a gradient source list: 0 (registered), 1 (flat, already reduced) or 2..64 rank buffers.
+// Checks a gradient source list: 0 (registered), 1 (flat, already reduced) or the N_d rank
+// buffers (2 <= N_d <= 64): summing fewer or more buffers than there are ranks is an error.
 zero_status_t check_sources(zero_shard* h, const void* const* rank_grads, int32_t n_ranks) {
   if (n_ranks == 0) {
     if (!h->has_registered_grads) return fail(ZERO_EINVAL, "n_ranks == 0 needs gradients registered at init");
     return ZERO_OK;
   }
   if (n_ranks < 0 || n_ranks > zs::kMaxRanks) return fail(ZERO_EINVAL, "n_ranks must be 0..64");
+  if (n_ranks >= 2 && n_ranks != h->dp_size)
+    return fail(ZERO_EINVAL, "the local reduce takes one buffer per rank: n_ranks " + std::to_string(n_ranks) +
+                                 " != dp_size " + std::to_string(h->dp_size));
   if (!rank_grads) return fail(ZERO_EINVAL, "rank_grads is null");
   for (int q = 0; q < n_ranks; ++q)
     if (!rank_grads[q]) return fail(ZERO_EINVAL, "rank_grads[" + std::to_string(q) + "] is null");
@@ -385,10 +390,8 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     h->grad_source = kGradFlat16;
     h->step_flat_g = g;
   } else {
-    if (n_ranks > zs::kMaxRanks) return fail(ZERO_EINVAL, "n_ranks above 64");
-    if (!rank_grads) return fail(ZERO_EINVAL, "rank_grads is null");
-    for (int q = 0; q < n_ranks; ++q)
-      if (!rank_grads[q]) return fail(ZERO_EINVAL, "rank_grads[" + std::to_string(q) + "] is null");
+    zero_status_t sc = check_sources(h, rank_grads, n_ranks);  // n_ranks < -1 or >= 2 here
+    if (sc != ZERO_OK) return sc;
     if (!h->red) return fail(ZERO_EINVAL, "reducing N_d >= 2 buffers needs bufs.red");
     e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, false, h->reduce_out16, false,
                           inv_loss_scale, dyn, flip, h->red, h->sc, h->parts, st);
@@ -400,6 +403,7 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
   h->inv = inv_loss_scale;
   h->other_flag = 0;
   h->other_sumsq = 0.0;
+  h->sumsq_global = false;
   h->max_norm = 0.0f;
   h->phase = kReduced;
   h->cast_pending = false;
@@ -442,22 +446,40 @@ zero_status_t zero_check_overflow(zero_shard_t h, int32_t other_ranks_found_inf,
   return ZERO_OK;
 }
 
-zero_status_t zero_grad_norm(zero_shard_t h, double other_ranks_sumsq, float max_norm, double* host_norm,
-                             void* stream) {
+namespace {
+// The norm call of a step: sumsq is the other ranks' sum (global false) or the global sum.
+zero_status_t grad_norm(zero_shard_t h, double sumsq, bool global, float max_norm, double* host_norm, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
   if (h->phase != kChecked && h->phase != kNormed)
-    return fail(ZERO_ESTATE, "zero_grad_norm must follow zero_check_overflow");
-  h->other_sumsq = other_ranks_sumsq;
+    return fail(ZERO_ESTATE, "the norm call must follow zero_check_overflow");
+  if (global && sumsq < 0.0) return fail(ZERO_EINVAL, "global_sumsq must not be negative");
+  h->other_sumsq = sumsq;
+  h->sumsq_global = global;
   h->max_norm = max_norm;
   h->phase = kNormed;
   if (host_norm) {
+    if (global) {
+      *host_norm = sqrt(sumsq);
+      return ZERO_OK;
+    }
     DeviceGuard dg(h->device);
     zs::DevScalars sc;
     zero_status_t s = sync_read_scalars(h, static_cast<hipStream_t>(stream), &sc);
     if (s != ZERO_OK) return s;
-    *host_norm = sqrt(sc.local_sumsq + other_ranks_sumsq);
+    *host_norm = sqrt(sc.local_sumsq + sumsq);
   }
   return ZERO_OK;
+}
+}  // namespace
+
+zero_status_t zero_grad_norm(zero_shard_t h, double other_ranks_sumsq, float max_norm, double* host_norm,
+                             void* stream) {
+  return grad_norm(h, other_ranks_sumsq, false, max_norm, host_norm, stream);
+}
+
+zero_status_t zero_grad_norm_global(zero_shard_t h, double global_sumsq, float max_norm, double* host_norm,
+                                    void* stream) {
+  return grad_norm(h, global_sumsq, true, max_norm, host_norm, stream);
 }
 
 namespace {
@@ -476,7 +498,7 @@ zero_status_t zero_adam_step(zero_shard_t h, const zero_adam_hparams_t* hp, int3
   if (track) ZS_HIP(hipEventRecord(h->wb_event, static_cast<hipStream_t>(stream)));
   hipError_t e = zs::launch_adam_step(h->dtype, h->grad_source, fuse_cast != 0, h->chunks, h->n_chunks,
                                       h->step_flat_g, h->red, h->master, h->m, h->v, h->sc, h->other_flag,
-                                      h->other_sumsq, h->max_norm,
+                                      h->other_sumsq, h->sumsq_global, h->max_norm,
                                       h->inv, hp, h->dynamic ? &h->dyn_cfg : nullptr, h->n_seg ? &seg : nullptr,
                                       h->grid_main, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("adam kernel", e);

@@ -91,6 +91,12 @@ class ZeroOffload:
         abi.zero_offload_adam_step(self.h, hp, other_ranks_found_inf, other_ranks_sumsq, max_norm,
                                    push and not self.host_only, _stream())
 
+    def zero_offload_adam_step_global(self, lr, beta1, beta2, eps, weight_decay, other_ranks_found_inf=False,
+                                      global_sumsq=0.0, max_norm=1.0, push=True):
+        hp = abi.zero_adam_hparams_t(lr, beta1, beta2, eps, weight_decay)
+        abi.zero_offload_adam_step_global(self.h, hp, other_ranks_found_inf, global_sumsq, max_norm,
+                                          push and not self.host_only, _stream())
+
     def zero_offload_push_params(self):
         abi.zero_offload_push_params(self.h, _stream())
 

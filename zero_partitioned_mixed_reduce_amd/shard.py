@@ -115,6 +115,11 @@ class ZeroShard:
     def zero_grad_norm(self, other_ranks_sumsq=0.0, max_norm=1.0, sync=False):
         return abi.zero_grad_norm(self.h, other_ranks_sumsq, max_norm, _stream(), sync)
 
+    def zero_grad_norm_global(self, global_sumsq, max_norm=1.0, sync=False):
+        """The norm from the global sum of squares (all ranks' local sums, added once in
+        rank order and given to every rank)."""
+        return abi.zero_grad_norm_global(self.h, global_sumsq, max_norm, _stream(), sync)
+
     def zero_adam_step(self, lr, beta1, beta2, eps, weight_decay, fuse_cast=True):
         hp = abi.zero_adam_hparams_t(lr, beta1, beta2, eps, weight_decay)
         abi.zero_adam_step(self.h, hp, fuse_cast, _stream())
