@@ -150,6 +150,36 @@ zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* 
 zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
                               const float* master_init, void* stream, zero_shard_t* out);
 
+/* Size in bytes of the library's static device workspace (one per device): the
+ * largest workspace_bytes a handle made by zero_shard_init_static may need.
+ * 8 MiB holds the workspace of shards of up to about 140,000 work items (one
+ * flat tensor of about 1.1e9 elements; fewer elements when a ragged tensor
+ * list cuts the shard into more pieces). */
+#define ZERO_STATIC_WORKSPACE_BYTES (8 * 1024 * 1024)
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: as
+ * zero_shard_init, but the handle's workspace is the library's own static
+ * device array of ZERO_STATIC_WORKSPACE_BYTES on the current device, held
+ * from the first such call on the device until the process ends.
+ * bufs->workspace must be NULL (bufs->workspace_capacity is ignored); the
+ * caller still passes the state buffers (master, m, v, red) and the 16-bit
+ * inputs and outputs.  Makes no device allocation: no hipMalloc, hipFree or
+ * allocating library routine (the handle itself is host memory).
+ *   - EINVAL if zero_shard_plan's workspace_bytes for the description exceeds
+ *     ZERO_STATIC_WORKSPACE_BYTES (use zero_shard_init with a workspace then),
+ *     or if bufs->workspace is not NULL; otherwise the errors of
+ *     zero_shard_init.
+ *   - One array per device: every zero_shard_init_static on a device takes it
+ *     over (re-initialising all of it, so nothing of an earlier handle
+ *     carries over), after which calls on earlier such handles of that device
+ *     return ZERO_ESTATE (zero_shard_destroy still frees them).  Work that an
+ *     earlier handle already enqueued must have completed before the new call,
+ *     and calls on such handles must not overlap on one device: they would
+ *     race on the array. */
+zero_status_t zero_shard_init_static(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
+                                     const float* master_init, void* stream, zero_shard_t* out);
+
 /* Chunk-pipelined step ("DeepSpeed ZeRO", ZeRO Stage 1, 通信与计算重叠: the
  * all-gather of updated parameters can start on each part as soon as it is
  * updated, alongside the update of the rest).  The shard's chunks are split

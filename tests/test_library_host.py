@@ -152,3 +152,28 @@ def test_gpu_c_program_compiles():
                         os.path.join(ROOT, "tests", "c", "step_from_c.c")], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 0, r.stderr
+
+
+def test_static_init_refuses_before_device_work():
+    """zero_shard_init_static checks the plan's workspace against the static array
+    (ZERO_STATIC_WORKSPACE_BYTES) and the absent caller workspace before any device call,
+    so both refusals are visible without a GPU."""
+    big = desc_for([2_000_000_000], 1, 0, dtype=_abi.ZERO_BF16)
+    info = zpm.zero_shard_plan(big)
+    assert info.workspace_bytes > _abi.ZERO_STATIC_WORKSPACE_BYTES
+    bufs = _abi.zero_shard_bufs_t()
+    bufs.master = bufs.m = bufs.v = 1 << 20                  # never dereferenced: refused first
+    bufs.state_capacity = info.state_elems
+    h = ctypes.c_void_p()
+    assert _abi.lib().zero_shard_init_static(ctypes.byref(big), ctypes.byref(bufs), None, None,
+                                             ctypes.byref(h)) == _abi.ZERO_EINVAL
+    assert "ZERO_STATIC_WORKSPACE_BYTES" in zpm.zero_last_error() and not h.value
+    bufs.workspace = 1 << 21
+    small = desc_for([4096], 1, 0, dtype=_abi.ZERO_BF16)
+    assert _abi.lib().zero_shard_init_static(ctypes.byref(small), ctypes.byref(bufs), None, None,
+                                             ctypes.byref(h)) == _abi.ZERO_EINVAL
+    assert "NULL" in zpm.zero_last_error()
+    # the header's limit and the binding's agree
+    hdr = open(os.path.join(ROOT, "include", "zero_shard.h")).read()
+    assert re.search(r"#define ZERO_STATIC_WORKSPACE_BYTES \(8 \* 1024 \* 1024\)", hdr)
+    assert _abi.ZERO_STATIC_WORKSPACE_BYTES == 8 * 1024 * 1024

@@ -10,6 +10,7 @@ ZERO_OK, ZERO_EINVAL, ZERO_ENOMEM, ZERO_EHIP, ZERO_ESTATE = 0, -1, -2, -3, -4
 ZERO_F16, ZERO_BF16 = 1, 2
 ZERO_ACCUMULATED = -1
 ZERO_DEVICE_LOSS_SCALE = 0.0
+ZERO_STATIC_WORKSPACE_BYTES = 8 * 1024 * 1024
 
 c_i64p = ctypes.POINTER(ctypes.c_int64)
 
@@ -56,6 +57,8 @@ _PROTOS = {
     "zero_shard_plan": [ctypes.POINTER(zero_shard_desc_t), ctypes.POINTER(zero_shard_info_t)],
     "zero_shard_init": [ctypes.POINTER(zero_shard_desc_t), ctypes.POINTER(zero_shard_bufs_t), ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)],
+    "zero_shard_init_static": [ctypes.POINTER(zero_shard_desc_t), ctypes.POINTER(zero_shard_bufs_t), ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)],
     "zero_reduce_grads": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_float,
                           ctypes.c_void_p],
     "zero_accumulate_grads": [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_void_p],
@@ -145,6 +148,12 @@ def zero_shard_plan(desc):
 def zero_shard_init(desc, bufs, master_init_ptr, stream):
     h = ctypes.c_void_p()
     _call("zero_shard_init", ctypes.byref(desc), ctypes.byref(bufs), master_init_ptr, stream, ctypes.byref(h))
+    return h
+
+
+def zero_shard_init_static(desc, bufs, master_init_ptr, stream):
+    h = ctypes.c_void_p()
+    _call("zero_shard_init_static", ctypes.byref(desc), ctypes.byref(bufs), master_init_ptr, stream, ctypes.byref(h))
     return h
 
 

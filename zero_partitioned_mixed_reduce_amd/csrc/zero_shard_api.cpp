@@ -9,6 +9,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -86,6 +87,7 @@ struct zero_shard {
   bool sumsq_global;   // zero_grad_norm_global: other_sumsq is the global sum, the local one is not added
   float max_norm;
   int64_t adam_calls;  // zero_adam_step calls (the segments' epoch)
+  uint64_t static_gen; // 0: caller workspace; else which zero_shard_init_static on this device made it
 };
 
 namespace {
@@ -127,6 +129,53 @@ zero_status_t sync_read_scalars(zero_shard* h, hipStream_t st, zs::DevScalars* o
   return ZERO_OK;
 }
 
+// The library's own workspace for handles made by zero_shard_init_static (for callers that
+// cannot allocate device memory).  Each device holds its own copy of the array, at its own
+// address, until the process ends.  In host code the array's name is only a host-side
+// stand-in: the device address comes from hipGetSymbolAddress (static_workspace below), and
+// only that address is ever handed to kernels or copies.
+static_assert(ZERO_STATIC_WORKSPACE_BYTES % 256 == 0, "static workspace size");
+__device__ __align__(256) static unsigned char scratch[ZERO_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices];     // device address of `scratch` on each device (null until looked up)
+uint64_t g_static_gen[kMaxDevices];  // zero_shard_init_static calls on each device
+
+// Takes the static workspace of device `dev` (the current device) for a new handle: looks up
+// its device address on the first call on that device, and advances the device's generation,
+// which retires every earlier handle on it.
+zero_status_t static_workspace(int dev, char** ws, uint64_t* gen) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(ZERO_EINVAL, "device index beyond the static workspaces");
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(static workspace)", e);
+    if (!ptr || ((uintptr_t)ptr & 255u) != 0) return fail(ZERO_EHIP, "static workspace address is not 256-byte aligned");
+    g_static_ptr[dev] = ptr;
+  }
+  *ws = static_cast<char*>(g_static_ptr[dev]);
+  *gen = ++g_static_gen[dev];
+  return ZERO_OK;
+}
+
+// A handle on the static workspace is usable until the next zero_shard_init_static on its device.
+zero_status_t check_workspace(const zero_shard* h) {
+  if (h->static_gen == 0) return ZERO_OK;
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (g_static_gen[h->device] != h->static_gen)
+    return fail(ZERO_ESTATE, "this handle's static workspace was taken over by a later zero_shard_init_static "
+                             "on the same device");
+  return ZERO_OK;
+}
+
+#define ZS_OWNER(h)                             \
+  do {                                          \
+    zero_status_t o_ = check_workspace(h);      \
+    if (o_ != ZERO_OK) return o_;               \
+  } while (0)
+
 }  // namespace
 
 extern "C" {
@@ -146,38 +195,54 @@ zero_status_t shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* out) 
   return ZERO_OK;
 }
 
+// zero_shard_init (use_static false: the caller's workspace) and zero_shard_init_static (the
+// library's static workspace of the current device).
 zero_status_t shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs, const float* master_init,
-                         void* stream, zero_shard_t* out) {
+                         void* stream, zero_shard_t* out, bool use_static) {
   if (!bufs || !out) return fail(ZERO_EINVAL, "null buffers or output handle");
   *out = nullptr;
   zs::Plan p;
   zero_status_t s = zs::build_plan(desc, &p, &g_err);
   if (s != ZERO_OK) return s;
-  if (!bufs->master || !bufs->m || !bufs->v || !bufs->workspace)
-    return fail(ZERO_EINVAL, "master, m, v and workspace must be non-null");
+  if (!bufs->master || !bufs->m || !bufs->v) return fail(ZERO_EINVAL, "master, m and v must be non-null");
   auto mis16 = [](const void* q) { return ((uintptr_t)q & 15u) != 0; };
   if (mis16(bufs->master) || mis16(bufs->m) || mis16(bufs->v) || (bufs->red && mis16(bufs->red)))
     return fail(ZERO_EINVAL, "state buffers must be 16-byte aligned");
-  if (((uintptr_t)bufs->workspace & 255u) != 0) return fail(ZERO_EINVAL, "workspace must be 256-byte aligned");
   if (bufs->state_capacity < p.info.state_elems)
     return fail(ZERO_EINVAL, "state_capacity " + std::to_string(bufs->state_capacity) + " < state_elems " +
                                  std::to_string(p.info.state_elems));
-  if (bufs->workspace_capacity < p.info.workspace_bytes)
-    return fail(ZERO_EINVAL, "workspace_capacity " + std::to_string(bufs->workspace_capacity) +
-                                 " < workspace_bytes " + std::to_string(p.info.workspace_bytes));
+  if (use_static) {
+    if (bufs->workspace) return fail(ZERO_EINVAL, "zero_shard_init_static takes no workspace: bufs->workspace "
+                                                  "must be NULL");
+    if (p.info.workspace_bytes > (int64_t)ZERO_STATIC_WORKSPACE_BYTES)
+      return fail(ZERO_EINVAL, "the shard needs a workspace of " + std::to_string(p.info.workspace_bytes) +
+                                   " bytes, beyond the static workspace of " +
+                                   std::to_string((int64_t)ZERO_STATIC_WORKSPACE_BYTES) +
+                                   " bytes (ZERO_STATIC_WORKSPACE_BYTES); use zero_shard_init with a workspace");
+  } else {
+    if (!bufs->workspace) return fail(ZERO_EINVAL, "workspace must be non-null");
+    if (((uintptr_t)bufs->workspace & 255u) != 0) return fail(ZERO_EINVAL, "workspace must be 256-byte aligned");
+    if (bufs->workspace_capacity < p.info.workspace_bytes)
+      return fail(ZERO_EINVAL, "workspace_capacity " + std::to_string(bufs->workspace_capacity) +
+                                   " < workspace_bytes " + std::to_string(p.info.workspace_bytes));
+  }
   if (master_init && mis16(master_init)) return fail(ZERO_EINVAL, "master_init must be 16-byte aligned");
 
-  zero_shard* h = new (std::nothrow) zero_shard();
-  if (!h) return fail(ZERO_ENOMEM, "out of host memory");
   hipStream_t st = static_cast<hipStream_t>(stream);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   int cus = 0;
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) {
-    delete h;
-    return hip_fail("hipGetDevice/hipDeviceGetAttribute", e);
+  if (e != hipSuccess) return hip_fail("hipGetDevice/hipDeviceGetAttribute", e);
+  char* ws = static_cast<char*>(bufs->workspace);
+  uint64_t gen = 0;
+  if (use_static) {
+    s = static_workspace(dev, &ws, &gen);
+    if (s != ZERO_OK) return s;
   }
+  zero_shard* h = new (std::nothrow) zero_shard();
+  if (!h) return fail(ZERO_ENOMEM, "out of host memory");
+  h->static_gen = gen;
   h->info = p.info;
   h->pieces = std::move(p.pieces);
   h->dtype = desc->dtype;
@@ -187,7 +252,6 @@ zero_status_t shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t*
   h->m = bufs->m;
   h->v = bufs->v;
   h->red = bufs->red;
-  char* ws = static_cast<char*>(bufs->workspace);
   h->sc = reinterpret_cast<zs::DevScalars*>(ws);
   const zs::IntakeLayout il = zs::intake_layout((int64_t)p.chunks.size());
   h->parts.part = reinterpret_cast<uint64_t*>(ws + il.part_off);
@@ -223,10 +287,6 @@ zero_status_t shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t*
   do {
     if ((e = hipMemcpyAsync(h->sc, &init_sc, sizeof(init_sc), hipMemcpyHostToDevice, st)) != hipSuccess) {
       rs = hip_fail("hipMemcpyAsync(scalars)", e);
-      break;
-    }
-    if ((e = hipEventCreateWithFlags(&h->wb_event, hipEventDisableTiming)) != hipSuccess) {
-      rs = hip_fail("hipEventCreateWithFlags", e);
       break;
     }
     static const zs::SegState zero_segs[zs::kMaxSegments] = {};
@@ -282,7 +342,16 @@ zero_status_t zero_shard_plan(const zero_shard_desc_t* desc, zero_shard_info_t* 
 zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
                               const float* master_init, void* stream, zero_shard_t* out) {
   try {
-    return shard_init(desc, bufs, master_init, stream, out);
+    return shard_init(desc, bufs, master_init, stream, out, false);
+  } catch (const std::exception& e) {
+    return fail(ZERO_ENOMEM, std::string("host resources: ") + e.what());
+  }
+}
+
+zero_status_t zero_shard_init_static(const zero_shard_desc_t* desc, const zero_shard_bufs_t* bufs,
+                                     const float* master_init, void* stream, zero_shard_t* out) {
+  try {
+    return shard_init(desc, bufs, master_init, stream, out, true);
   } catch (const std::exception& e) {
     return fail(ZERO_ENOMEM, std::string("host resources: ") + e.what());
   }
@@ -309,6 +378,7 @@ zero_status_t check_sources(zero_shard* h, const void* const* rank_grads, int32_
 
 zero_status_t zero_set_reduce_output(zero_shard_t h, int32_t out_16bit) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   if (out_16bit != 0 && out_16bit != 1) return fail(ZERO_EINVAL, "out_16bit must be 0 or 1");
   if (!(h->phase == kReady || h->phase == kStepped) || h->cast_pending || h->accumulating)
     return fail(ZERO_ESTATE, "the reduce output is set between steps");
@@ -319,6 +389,7 @@ zero_status_t zero_set_reduce_output(zero_shard_t h, int32_t out_16bit) {
 
 zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   if (h->phase == kReduced || h->phase == kChecked || h->phase == kNormed)
     return fail(ZERO_ESTATE, "micro-steps are accumulated before the step's zero_reduce_grads");
   if (h->phase == kStepped && h->cast_pending)
@@ -340,6 +411,7 @@ zero_status_t zero_accumulate_grads(zero_shard_t h, const void* const* rank_grad
 zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, int32_t n_ranks, float inv_loss_scale,
                                 void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   if (h->phase == kStepped && h->cast_pending)
     return fail(ZERO_ESTATE, "zero_cast_params of the previous step is pending");
   bool dyn = false;
@@ -412,6 +484,7 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
 
 zero_status_t zero_local_stats(zero_shard_t h, int32_t* found_inf, double* sumsq, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   if (h->phase == kReady || h->phase == kStepped) return fail(ZERO_ESTATE, "no gradient intake in this step yet");
   DeviceGuard dg(h->device);
   zs::DevScalars sc;
@@ -424,6 +497,7 @@ zero_status_t zero_local_stats(zero_shard_t h, int32_t* found_inf, double* sumsq
 
 zero_status_t zero_local_stats_device(zero_shard_t h, double** sumsq, int32_t** found_inf) {
   if (!h || !sumsq || !found_inf) return fail(ZERO_EINVAL, "null handle or output");
+  ZS_OWNER(h);
   *sumsq = &h->sc->local_sumsq;
   *found_inf = &h->sc->local_flag;
   return ZERO_OK;
@@ -432,6 +506,7 @@ zero_status_t zero_local_stats_device(zero_shard_t h, double** sumsq, int32_t** 
 zero_status_t zero_check_overflow(zero_shard_t h, int32_t other_ranks_found_inf, int32_t* host_found_inf,
                                   void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   if (h->phase != kReduced && h->phase != kChecked)
     return fail(ZERO_ESTATE, "zero_check_overflow must follow zero_reduce_grads");
   h->other_flag = other_ranks_found_inf ? 1 : 0;
@@ -450,6 +525,7 @@ namespace {
 // The norm call of a step: sumsq is the other ranks' sum (global false) or the global sum.
 zero_status_t grad_norm(zero_shard_t h, double sumsq, bool global, float max_norm, double* host_norm, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   if (h->phase != kChecked && h->phase != kNormed)
     return fail(ZERO_ESTATE, "the norm call must follow zero_check_overflow");
   if (global && sumsq < 0.0) return fail(ZERO_EINVAL, "global_sumsq must not be negative");
@@ -490,6 +566,7 @@ zs::SegArgs seg_args(const zero_shard* h, int64_t epoch) {
 
 zero_status_t zero_adam_step(zero_shard_t h, const zero_adam_hparams_t* hp, int32_t fuse_cast, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   if (!hp) return fail(ZERO_EINVAL, "null hyperparameters");
   if (h->phase != kNormed) return fail(ZERO_ESTATE, "zero_adam_step must follow zero_grad_norm");
   DeviceGuard dg(h->device);
@@ -511,6 +588,7 @@ zero_status_t zero_adam_step(zero_shard_t h, const zero_adam_hparams_t* hp, int3
 
 zero_status_t zero_cast_params(zero_shard_t h, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   if (h->phase != kStepped) return fail(ZERO_ESTATE, "zero_cast_params must follow zero_adam_step");
   if (!h->cast_pending) return ZERO_OK;
   DeviceGuard dg(h->device);
@@ -526,9 +604,14 @@ zero_status_t zero_cast_params(zero_shard_t h, void* stream) {
 
 zero_status_t zero_set_segments(zero_shard_t h, int32_t n_segments, int32_t* out_segments) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   if (n_segments < 0 || n_segments > zs::kMaxSegments) return fail(ZERO_EINVAL, "n_segments must be 0..256");
   if (h->phase != kReady && h->phase != kStepped) return fail(ZERO_ESTATE, "set segments between steps");
   if (h->phase == kStepped && h->cast_pending) return fail(ZERO_ESTATE, "zero_cast_params is pending");
+  if (n_segments > 0 && h->n_chunks > 0 && !h->wb_event) {
+    DeviceGuard dg(h->device);
+    ZS_HIP(hipEventCreateWithFlags(&h->wb_event, hipEventDisableTiming));
+  }
   // every counter is re-armed once a write-back completes, so the layout may change between steps
   if (n_segments == 0 || h->n_chunks == 0) {
     h->n_seg = 0;
@@ -554,6 +637,7 @@ zero_status_t zero_segment_range(zero_shard_t h, int32_t k, int64_t* shard_begin
 
 zero_status_t zero_wait_segment(zero_shard_t h, int32_t k, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   if (k < 0 || k >= h->n_seg) return fail(ZERO_EINVAL, "no segment " + std::to_string(k));
   if (h->adam_calls == 0 || h->phase != kStepped || h->cast_pending)
     return fail(ZERO_ESTATE, "the write-back of this step has not been enqueued");
@@ -573,6 +657,7 @@ zero_status_t zero_wait_segment(zero_shard_t h, int32_t k, void* stream) {
 
 zero_status_t zero_segment_timeouts(zero_shard_t h, int64_t* timeouts, void* stream) {
   if (!h || !timeouts) return fail(ZERO_EINVAL, "null handle or output");
+  ZS_OWNER(h);
   DeviceGuard dg(h->device);
   zs::DevScalars sc;
   zero_status_t s = sync_read_scalars(h, static_cast<hipStream_t>(stream), &sc);
@@ -583,6 +668,7 @@ zero_status_t zero_segment_timeouts(zero_shard_t h, int64_t* timeouts, void* str
 
 zero_status_t zero_enable_dynamic_loss_scale(zero_shard_t h, const zero_loss_scaler_t* cfg, void* stream) {
   if (!h || !cfg) return fail(ZERO_EINVAL, "null handle or configuration");
+  ZS_OWNER(h);
   if (h->phase != kReady && h->phase != kStepped) return fail(ZERO_ESTATE, "enable loss scaling between steps");
   if (h->phase == kStepped && h->cast_pending) return fail(ZERO_ESTATE, "zero_cast_params is pending");
   if (h->accumulating) return fail(ZERO_ESTATE, "enable loss scaling before accumulating micro-steps");
@@ -609,6 +695,7 @@ zero_status_t zero_enable_dynamic_loss_scale(zero_shard_t h, const zero_loss_sca
 
 zero_status_t zero_loss_scale(zero_shard_t h, float* host_scale, int32_t* host_good, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   if (!h->dynamic) return fail(ZERO_ESTATE, "dynamic loss scaling is not enabled");
   DeviceGuard dg(h->device);
   zs::DevScalars sc;
@@ -642,6 +729,7 @@ zero_status_t zero_shard_pieces(zero_shard_t h, int64_t* out, int64_t cap) {
 zero_status_t zero_shard_query(zero_shard_t h, int64_t* t, int32_t* last_skipped, double* last_norm,
                                float* last_clip, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   DeviceGuard dg(h->device);
   zs::DevScalars sc;
   zero_status_t s = sync_read_scalars(h, static_cast<hipStream_t>(stream), &sc);
@@ -655,6 +743,7 @@ zero_status_t zero_shard_query(zero_shard_t h, int64_t* t, int32_t* last_skipped
 
 zero_status_t zero_export_state(zero_shard_t h, int32_t which, float* dst, void* stream) {
   if (!h) return fail(ZERO_EINVAL, "null handle");
+  ZS_OWNER(h);
   const float* src = which == 0 ? h->master : which == 1 ? h->m : which == 2 ? h->v : which == 3 ? h->red : nullptr;
   if (!src) return fail(ZERO_EINVAL, "which must be 0 (master), 1 (m), 2 (v) or 3 (red, when allocated)");
   if (which == 3 && h->red_holds16)

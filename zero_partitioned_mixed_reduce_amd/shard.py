@@ -48,26 +48,31 @@ class ZeroShard:
     """One rank's shard: plan, caller-owned buffers (torch), handle."""
 
     def __init__(self, numel, dp_size, dp_rank, dtype, params, grads=None, master_init=None, with_red=False,
-                 device="cuda", align=0):
+                 device="cuda", align=0, static_workspace=False):
+        """static_workspace: no workspace is allocated; the handle uses the library's static
+        device workspace (zero_shard_init_static)."""
         self.dtype = dtype
         self.desc = make_desc(numel, dp_size, dp_rank, dtype, params, grads, align)
         self._params, self._grads = params, grads
         self.info = abi.zero_shard_plan(self.desc)
         n = self.info.state_elems
         self.master, self.m, self.v, self.red = self._alloc_state(n, with_red, device)
-        self.workspace = torch.empty(self.info.workspace_bytes, dtype=torch.uint8, device=device)
+        self.workspace = None
+        if not static_workspace:
+            self.workspace = torch.empty(self.info.workspace_bytes, dtype=torch.uint8, device=device)
         b = abi.zero_shard_bufs_t()
         b.master, b.m, b.v = self.master.data_ptr(), self.m.data_ptr(), self.v.data_ptr()
         b.red = self.red.data_ptr() if self.red is not None else None
-        b.workspace = self.workspace.data_ptr()
+        b.workspace = self.workspace.data_ptr() if self.workspace is not None else None
         b.state_capacity = n
-        b.workspace_capacity = self.info.workspace_bytes
+        b.workspace_capacity = self.info.workspace_bytes if self.workspace is not None else 0
         self.bufs = b
         mi = None
         if master_init is not None:
             assert master_init.dtype == torch.float32 and master_init.numel() == self.info.valid_elems
             mi = master_init.data_ptr()
-        self.h = abi.zero_shard_init(self.desc, b, mi, _stream())
+        init = abi.zero_shard_init_static if static_workspace else abi.zero_shard_init
+        self.h = init(self.desc, b, mi, _stream())
 
     # Offset, in floats, between consecutive state arrays carved from one allocation.
     # None: one allocation per array.
