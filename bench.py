@@ -71,6 +71,13 @@ def parse():
                    help="skip the device-to-device copy measurement after the timed steps")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one 1 GiB read + 1 GiB write elementwise kernel first (scales the traffic counters)")
+    p.add_argument("--no-probes", action="store_true",
+                   help="skip the bandwidth probes (the step's access patterns without its arithmetic) after the "
+                        "timed steps")
+    p.add_argument("--secondary", default="auto",
+                   choices=["auto", "none", "tiny", "gpt2", "zero1_7p5b", "reduce8", "full7p5b"],
+                   help="a second configuration measured the same way after the first, reported as `secondary` "
+                        "(auto: the ZeRO-1 7.5B/64 shard after the full-state one, else none)")
     return p.parse_args()
 
 
@@ -587,29 +594,115 @@ def bench_offload(a, w, rank):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(json.dumps({"error": f"this benchmark runs one data-parallel rank on one GPU; --gpus {a.gpus} "
-                                   "is not supported (the path has no collectives: see the design notes "
-                                   "for how it shards)"}), flush=True)
-        sys.exit(2)
+INFINITY_CACHE_BYTES = 256 << 20
+
+
+def hbm_side(w, valid, micro_steps, reduce_out16, step_b, adam_b):
+    """HBM-side bytes per parameter where they differ from the fabric-side (L2-requested)
+    count: a gradient slice that fits in the 256 MB Infinity Cache is read by the statistics
+    pass with plain loads and re-read by the Adam pass from the cache, so the second read
+    does not reach HBM.  Returns (step, adam, note)."""
+    slice_bytes = 2 * valid
+    if w.grad_mode != "reduce" and micro_steps == 1 and slice_bytes <= INFINITY_CACHE_BYTES:
+        return step_b - 2, adam_b - 2, (f"the {slice_bytes / 1e6:.0f} MB gradient slice fits in the 256 MB Infinity "
+                                        "Cache: the Adam pass re-reads it from there, so HBM moves 2 B/param less "
+                                        "than the fabric count (no hardware counter separates the two on gfx950)")
+    return step_b, adam_b, "no re-read fits in the 256 MB Infinity Cache: HBM-side bytes equal the fabric count"
+
+
+def probe_ceiling(wl, a, adam_gbps, adam_b, stats_gbps):
+    """The step's access patterns without its arithmetic, on the workload's own buffers
+    (probes/): the Adam pass's stream mix in the kernel's own grid, block and
+    non-temporal policy, and two nearby shapes; the statistics pass's (or the local
+    reduce's) read pattern; pure fp32 read, write and copy streams over the state arrays.
+    Runs after every step measurement (it overwrites the state).  GB/s, medians of 3."""
+    import torch
+    import probes
+    st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    w, sh = wl.w, wl.shard
+    valid, b = wl.info.valid_elems, wl.info.shard_begin
+    n = valid // 4 * 4
+    if n < 4096:
+        return None
+    scratch = []
+
+    def flat16(t):
+        if t is not None and not isinstance(t, list):
+            return t.data_ptr() + 2 * b                 # this rank's slice of a flat buffer
+        x = torch.empty(n, dtype=torch.int16, device="cuda")  # ragged tensors: one flat stand-in of the slice's size
+        x.fill_(0x3C00)
+        scratch.append(x)
+        return x.data_ptr()
+
+    def timed(fn, reps=3):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            fn()
+            e[1].record()
+            e[1].synchronize()
+            ts.append(e[0].elapsed_time(e[1]))
+        return sorted(ts)[len(ts) // 2]
+
+    gbps = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    wp, mp, vp = sh.master.data_ptr(), sh.m.data_ptr(), sh.v.data_ptr()
+    p16 = flat16(wl.params)
+    out = {"unit": "GB/s", "elements": n,
+           "buffers": "the benchmark's own fp32 state arrays and the shard's 16-bit slices (ragged tensor lists: a "
+                      "flat 16-bit stand-in of the slice's size), after the timed steps"}
+    reduce_mode = w.grad_mode == "reduce"
+    if reduce_mode:
+        g, g32, mix_b = sh.red.data_ptr(), True, 30             # the Adam pass reads fp32 u after a local reduce
+    else:
+        g, g32, mix_b = flat16(wl.grads_reg), False, 28
+    shapes = {"kernel_shape": (2048, 2, 256), "u4_bs512": (2048, 4, 512), "epb1024_u4": (1024, 4, 256)}
+    mix = {}
+    for name, (epb, u, bs) in shapes.items():
+        mix[name] = gbps(mix_b * n, timed(lambda: probes.adam_mix(g, wp, mp, vp, p16, n, st(), epb, u, bs, 1, 1,
+                                                                   g32)))
+    out["adam_mix_bytes_per_param"] = mix_b
+    out["adam_mix"] = mix
+    best = max(mix.values())
+    out["adam_mix_best"] = best
+    out["adam_frac_of_ceiling"] = adam_gbps / best
+    out["adam_frac_of_same_pattern_probe"] = adam_gbps / mix["kernel_shape"]
+    sink = torch.empty(n // 1024 + 1, device="cuda")
+    if reduce_mode:
+        srcs = [x.data_ptr() + 2 * b for x in wl.rank_grads]
+        out["reduce_mix"] = {f: gbps((2 * len(srcs) + 4) * n, timed(lambda: probes.reduce_mix(
+            srcs, sh.red.data_ptr(), n, st(), epb, u, bs, 1))) for f, (epb, u, bs) in
+            {"kernel_shape": (8192, 2, 256), "epb4096_bs512": (4096, 2, 512), "epb1024": (1024, 2, 256)}.items()}
+        out["reduce_frac_of_ceiling"] = stats_gbps / max(out["reduce_mix"].values())
+    else:
+        nt = int(2 * valid > INFINITY_CACHE_BYTES)               # the statistics pass's load policy
+        out["read16_grad"] = {f: gbps(2 * n, timed(lambda: probes.read16(g, n, sink.data_ptr(), st(), epb, u, bs, nt)))
+                              for f, (epb, u, bs) in {"kernel_shape": (8192, 4, 256),
+                                                      "epb32768_bs512": (32768, 2, 512)}.items()}
+        out["stats_frac_of_ceiling"] = stats_gbps / max(out["read16_grad"].values())
+    out["read32"] = gbps(4 * n, timed(lambda: probes.read32(wp, n, sink.data_ptr(), st(), 2048, 1, 256, 1)))
+    out["write32"] = gbps(4 * n, timed(lambda: probes.write32(mp, n, st(), 2048, 2, 512, 1)))
+    out["copy32"] = gbps(8 * n, timed(lambda: probes.copy32(wp, mp, n, st(), 2048, 2, 512, 1)))
+    del scratch, sink
+    return out
+
+
+def measure(a, config, rank, primary=True):
+    """Builds the workload, runs the warm-up and the timed steps, and returns the bench
+    fields for one configuration (the workload is freed before returning)."""
     import torch
     from synth import recipes
 
-    w = recipes.ALL[a.config]()
-    rank = a.rank if a.rank is not None else w.ranks[0]
-    if a.offload:
-        bench_offload(a, w, rank)
-        return
-    torch.cuda.set_device(0)
+    w = recipes.ALL[config]()
+    rank = rank if rank is not None else w.ranks[0]
     t_setup = time.perf_counter()
     wl = Workload(w, rank, a.micro_steps, a.dynamic_loss_scale, a.segments, a.segment_consumer, a.reduce_output16)
     setup_s = time.perf_counter() - t_setup
     valid = wl.info.valid_elems
     step_b, adam_b = bytes_per_param(w, a.micro_steps, a.reduce_output16)
 
-    if a.copy_calibration:
+    if a.copy_calibration and primary:
         # a plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB), used to scale
         # the FETCH_SIZE / WRITE_SIZE counters of the same run
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -639,7 +732,7 @@ def main():
     adam_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps
     adam_bytes = adam_b * valid
     achieved = adam_bytes / (adam_ms * 1e-3) / 1e9
-    traffic, stats_traffic = traffic_from_profiles(a.config, rank, adam_bytes)
+    traffic, stats_traffic = traffic_from_profiles(config, rank, adam_bytes)
     out = {
         "metric": METRIC,
         "value": valid / (ms_step * 1e-3),
@@ -663,11 +756,14 @@ def main():
         "hbm_gbps_step": step_b * valid / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": step_b * valid / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "bytes_per_param_step": step_b,
+        "bytes_counted": "fabric side: the dependency-minimal bytes the L2s request (the gradient read twice)",
         "breakdown_ms": {"accumulate": ms_step - stats_ms - adam_ms if a.micro_steps > 1 else 0.0,
                          "intake_stats": stats_ms, "norm_adam_cast": adam_ms},
         "roofline": {"kernel": "adam_kernel (Adam + fused 16-bit write-back)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "traffic_counts": "FETCH_SIZE + WRITE_SIZE per launch (scaled by a known copy): requests "
+                                       "below the L2s, Infinity Cache hits included",
                      "algorithmic_bytes_per_launch": adam_bytes, "bytes_per_param": adam_b,
                      "avg_launch_ms": adam_ms},
         "setup_s": setup_s,
@@ -677,6 +773,7 @@ def main():
     ns_b = 28 + (2 * w.nd if w.grad_mode == "reduce" else 0)
     out["hbm_gbps_step_28b"] = ns_b * valid / (ms_step * 1e-3) / 1e9
     out["bytes_per_param_28b"] = ns_b
+    hs_step, hs_adam, hs_note = hbm_side(w, valid, a.micro_steps, a.reduce_output16, step_b, adam_b)
     if traffic is not None and stats_traffic is not None and a.micro_steps == 1 and w.grad_mode != "reduce":
         # counter-measured bytes of the step's two kernels (profiles/), over the measured step time
         step_traffic = traffic + stats_traffic
@@ -706,6 +803,7 @@ def main():
                                "steps": a.steps,
                                "protocol": "after the timed steps: the step captured once into a HIP graph, "
                                            "then replayed back to back, bracketed by synchronisation"}
+    cold_ms = None
     if not a.no_cold_cache:
         cold_ms = cold_cache_steps(wl, a.steps, "read")
         cold_w_ms = cold_cache_steps(wl, a.steps, "write")
@@ -718,9 +816,49 @@ def main():
                                          "step alone between two events; median.  After a 1 GiB write "
                                          "instead, the write-back of the dirty lines it leaves falls inside "
                                          "the step"}
+    hs = {"bytes_per_param_step": hs_step, "bytes_per_param_adam": hs_adam, "note": hs_note,
+          "gbps_step": hs_step * valid / (ms_step * 1e-3) / 1e9,
+          "frac_step": hs_step * valid / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+          "gbps_adam": hs_adam * valid / (adam_ms * 1e-3) / 1e9,
+          "frac_adam": hs_adam * valid / (adam_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    if cold_ms is not None:
+        hs["frac_step_cold_cache"] = hs_step * valid / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS
+    out["hbm_side"] = hs
+    if not a.no_probes:
+        stats_gbps = ((2 * w.nd + 4) if w.grad_mode == "reduce" else 2) * valid / (stats_ms * 1e-3) / 1e9
+        ceil = probe_ceiling(wl, a, achieved, adam_b, stats_gbps)
+        if ceil is not None:
+            out["roofline"]["ceiling"] = ceil
+    del wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out, w, rank, achieved
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": f"this benchmark runs one data-parallel rank on one GPU; --gpus {a.gpus} "
+                                   "is not supported (the path has no collectives: see the design notes "
+                                   "for how it shards)"}), flush=True)
+        sys.exit(2)
+    import torch
+    from synth import recipes
+
+    if a.offload:
+        w = recipes.ALL[a.config]()
+        bench_offload(a, w, a.rank if a.rank is not None else w.ranks[0])
+        return
+    torch.cuda.set_device(0)
+    out, w, rank, achieved = measure(a, a.config, a.rank)
+    secondary = a.secondary if a.secondary != "auto" else ("zero1_7p5b" if a.config == "full7p5b" else "none")
+    if secondary != "none" and secondary != a.config:
+        sec, _, _, _ = measure(a, secondary, None, primary=False)
+        keep = ("value", "unit", "ms_per_step", "steps", "warmup", "config", "hbm_gbps_step", "hbm_frac_step",
+                "bytes_per_param_step", "bytes_counted", "hbm_gbps_step_28b", "bytes_per_param_28b",
+                "breakdown_ms", "roofline", "counter_traffic_step", "cold_cache", "hbm_side")
+        out["secondary"] = {k: sec[k] for k in keep if k in sec}
     if not a.no_copy_ceiling:
-        del wl
-        torch.cuda.empty_cache()
         cc = copy_ceiling()
         top = max(cc.values())
         out["copy_ceiling"] = {"unit": "GB/s", "bytes": 4 << 30, "memcpy_d2d": cc["memcpy"],
@@ -728,6 +866,7 @@ def main():
                                "adam_frac_of_copy": achieved / top, "step_frac_of_copy": out["hbm_gbps_step"] / top}
     out["host"] = host_info()
     if not a.no_cpu_baseline:
+        valid = out["config"]["shard_params"]
         n = min(a.cpu_sample, valid)
         rate, secs = cpu_baseline(w, n, a.cpu_steps)
         out["cpu_baseline"] = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",

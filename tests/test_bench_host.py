@@ -76,3 +76,32 @@ def test_committed_traffic_summaries():
         assert 1.0 <= adam / (28 * valid) <= 1.05 and 1.0 <= stats / (2 * valid) <= 1.05, cfg
     if not found:
         pytest.skip("the committed summaries were taken on another kernel source")
+
+
+def test_hbm_side_bytes():
+    """Where the gradient slice fits in the 256 MB Infinity Cache (the ZeRO-1 7.5B/64 shard,
+    234 MB), the Adam pass's re-read is not counted as HBM traffic: 28 B/param for the step and
+    26 for the Adam pass, against the fabric counts 30 and 28.  Slices that do not fit (the
+    GPT-2 shard's 389 MB, the full state) and the local reduce keep the fabric count."""
+    assert bench.hbm_side(recipes.zero1_7p5b(), 117_187_520, 1, False, 30, 28)[:2] == (28, 26)
+    assert bench.hbm_side(recipes.full7p5b(), 7_500_000_000, 1, False, 30, 28)[:2] == (30, 28)
+    assert bench.hbm_side(recipes.gpt2_shard(), 194_409_856, 1, False, 30, 28)[:2] == (30, 28)
+    assert bench.hbm_side(recipes.reduce8(), 187_500_032, 1, False, 50, 30)[:2] == (50, 30)
+    # with micro-steps the accumulator is re-read instead: no adjustment
+    assert bench.hbm_side(recipes.zero1_7p5b(), 117_187_520, 2, False, 44, 32)[:2] == (44, 32)
+
+
+def test_probe_library_checks_its_grid_on_the_host():
+    """The bandwidth probes load and refuse shapes they cannot cover before any device work:
+    an element count that is not a multiple of 4, a block span that is not a multiple of
+    4 x the block size, an unsupported block size or quad count (hipErrorInvalidValue = 1)."""
+    import ctypes
+    import probes
+    L = probes.lib()
+    P = ctypes.c_void_p(1 << 20)
+    assert L.zprobe_adam_mix(P, 0, P, P, P, P, 6, 2048, 2, 256, 1, 1, None) == 1
+    assert L.zprobe_adam_mix(P, 0, P, P, P, P, 4096, 1000, 2, 256, 1, 1, None) == 1
+    assert L.zprobe_adam_mix(P, 0, P, P, P, P, 4096, 2048, 3, 256, 1, 1, None) == 1
+    assert L.zprobe_copy32(P, P, 4096, 2048, 2, 128, 1, None) == 1
+    assert L.zprobe_reduce_mix((ctypes.c_void_p * 3)(P, P, P), 3, P, 4096, 2048, 2, 256, 1, None) == 1
+    assert L.zprobe_adam_mix(P, 0, P, P, P, P, 0, 2048, 2, 256, 1, 1, None) == 0      # nothing to do
