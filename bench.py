@@ -74,6 +74,10 @@ def parse():
     p.add_argument("--no-probes", action="store_true",
                    help="skip the bandwidth probes (the step's access patterns without its arithmetic) after the "
                         "timed steps")
+    p.add_argument("--state-pitch-gib", type=float, default=0.0,
+                   help="place the shard's fp32 state arrays this many GiB apart inside one allocation (the gaps "
+                        "are allocated too); 0: one allocation per array (default).  An experiment on the DRAM "
+                        "address mapping, not the benchmark's layout")
     p.add_argument("--secondary", default="auto",
                    choices=["auto", "none", "tiny", "gpt2", "zero1_7p5b", "reduce8", "full7p5b"],
                    help="a second configuration measured the same way after the first, reported as `secondary` "
@@ -696,6 +700,9 @@ def measure(a, config, rank, primary=True):
 
     w = recipes.ALL[config]()
     rank = rank if rank is not None else w.ranks[0]
+    from zero_partitioned_mixed_reduce_amd.shard import ZeroShard
+    pitch = int(getattr(a, "state_pitch_gib", 0.0) * (1 << 30)) // 256 * 256
+    ZeroShard.state_pitch = pitch if pitch > 0 else None
     t_setup = time.perf_counter()
     wl = Workload(w, rank, a.micro_steps, a.dynamic_loss_scale, a.segments, a.segment_consumer, a.reduce_output16)
     setup_s = time.perf_counter() - t_setup
@@ -752,6 +759,8 @@ def measure(a, config, rank, primary=True):
                    "loss_scale_mode": "dynamic, device-resident" if a.dynamic_loss_scale else "static",
                    "micro_steps": a.micro_steps,
                    "reduce_output": "16-bit" if a.reduce_output16 and w.grad_mode == "reduce" else "fp32",
+                   "state_placement": (f"one allocation, arrays {pitch / (1 << 30):g} GiB apart" if pitch > 0
+                                       else "one allocation per array"),
                    "adam": w.hp},
         "hbm_gbps_step": step_b * valid / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": step_b * valid / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

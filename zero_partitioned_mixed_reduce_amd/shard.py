@@ -74,13 +74,21 @@ class ZeroShard:
         init = abi.zero_shard_init_static if static_workspace else abi.zero_shard_init
         self.h = init(self.desc, b, mi, _stream())
 
-    # Offset, in floats, between consecutive state arrays carved from one allocation.
-    # None: one allocation per array.
+    # Placement of the state arrays (master, m, v, red).  None: one allocation per array.
+    # state_stagger (floats): carved from one allocation, each n + state_stagger floats after
+    # the previous one.  state_pitch (bytes, a multiple of 256): carved from one allocation,
+    # each starting state_pitch bytes after the previous one; the gaps are allocated too.
     state_stagger = None
+    state_pitch = None
 
     def _alloc_state(self, n, with_red, device):
         k = 4 if with_red else 3
-        if self.state_stagger is None:
+        if self.state_pitch is not None:
+            pitch = self.state_pitch // 4
+            assert self.state_pitch % 256 == 0 and pitch >= n, "state_pitch must hold one array"
+            self._state_store = torch.empty((k - 1) * pitch + n, dtype=torch.float32, device=device)
+            arrs = [self._state_store[i * pitch:i * pitch + n] for i in range(k)]
+        elif self.state_stagger is None:
             arrs = [torch.empty(n, dtype=torch.float32, device=device) for _ in range(k)]
         else:
             pitch = n + self.state_stagger
