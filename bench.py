@@ -614,7 +614,7 @@ def hbm_side(w, valid, micro_steps, reduce_out16, step_b, adam_b):
     return step_b, adam_b, "no re-read fits in the 256 MB Infinity Cache: HBM-side bytes equal the fabric count"
 
 
-def probe_ceiling(wl, a, adam_gbps, adam_b, stats_gbps):
+def probe_ceiling(wl, adam_gbps, stats_gbps):
     """The step's access patterns without its arithmetic, on the workload's own buffers
     (probes/): the Adam pass's stream mix in the kernel's own grid, block and
     non-temporal policy, and two nearby shapes; the statistics pass's (or the local
@@ -835,7 +835,7 @@ def measure(a, config, rank, primary=True):
     out["hbm_side"] = hs
     if not a.no_probes:
         stats_gbps = ((2 * w.nd + 4) if w.grad_mode == "reduce" else 2) * valid / (stats_ms * 1e-3) / 1e9
-        ceil = probe_ceiling(wl, a, achieved, adam_b, stats_gbps)
+        ceil = probe_ceiling(wl, achieved, stats_gbps)
         if ceil is not None:
             out["roofline"]["ceiling"] = ceil
     del wl
