@@ -169,7 +169,10 @@ int step_from_c(void) {
     int32_t gflag = -1;
     ZCHECK(zero_check_overflow(h, flag[0], &gflag, NULL));
     double dnorm = 0.0;
-    ZCHECK(zero_grad_norm(h, local[0], max_norm, &dnorm, NULL));
+    if (step != 3) /* the global sum of squares, added once in rank order and given to every rank */
+      ZCHECK(zero_grad_norm_global(h, local[0] + local[1], max_norm, &dnorm, NULL));
+    else /* the other rank's sum; this rank's own is added on the device */
+      ZCHECK(zero_grad_norm(h, local[0], max_norm, &dnorm, NULL));
     ZCHECK(zero_adam_step(h, &hp, 1, NULL));
     int64_t t;
     int32_t skipped;
