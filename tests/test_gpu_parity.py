@@ -926,3 +926,57 @@ def test_dynamic_loss_scale_growth_stops_below_infinity():
         assert all(x["skipped"] == (step == 4) for x in res)
         assert sim.scaler.scale.value == expect[step], step
         sim.compare()
+
+
+# --------------------------------------------------------------------------
+# seeded random small configurations, every rank against the oracle
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_small_configurations(seed):
+    """A seeded random configuration per case: a tensor list of 1-11 tensors (sizes 0-40000,
+    some empty), N_d 1-7, shard alignment 8, 64 or 256, fp16 or bf16, the gradient as N_d rank
+    buffers, one flat buffer, per-tensor registered or flat registered, parameters flat or
+    per tensor at element misalignments, a given or upcast master; three steps with a
+    non-finite value injected at a random step and place (or none), clipping off, loose or
+    active, the cast fused or standalone.  Every rank's state and 16-bit slice must match the
+    oracle bit for bit, and nothing outside each rank's slice may change."""
+    r = np.random.default_rng(0x5EED1000 + seed)
+    T = int(r.integers(1, 12))
+    numel = [int(x) if r.random() > 0.1 else 0 for x in r.integers(1, 40001, size=T)]
+    if sum(numel) == 0:
+        numel[0] = 12345
+    psi = sum(numel)
+    nd = int(r.integers(1, 8))
+    align = int(r.choice([8, 64, 256]))
+    dtype = int(r.choice([F16, BF16]))
+    mode = str(r.choice(["reduce", "flat", "ragged", "registered_flat"]))
+    per_tensor = bool(r.random() < 0.5)
+    pmis = tuple(int(x) for x in r.integers(0, 8, size=3))
+    gmis = tuple(int(x) for x in r.integers(0, 8, size=2))
+    master_given = bool(r.random() < 0.7)
+    fuse = bool(r.random() < 0.5)
+    max_norm = float(r.choice([0.0, 1.0, 1e-3]))
+    hp = oracle.HParams(float(r.choice([1e-4, 1e-3, 1e-2])), 0.9, 0.999, 1e-8, float(r.choice([0.0, 0.01, 0.1])))
+    seed_w = 0x5EED2000 + seed
+    print(f"[random {seed}] T {T} psi {psi} N_d {nd} align {align} dtype {dtype} mode {mode} "
+          f"per_tensor {per_tensor} master {master_given} fuse {fuse} max_norm {max_norm}", flush=True)
+    master = synth.normal_f32(psi, seed_w, synth.stream_id(synth.MASTER), 0, 0.02)
+    p16 = oracle.encode16(dtype, master) if master_given else \
+        synth.normal_16(psi, dtype, seed_w, synth.stream_id(synth.MASTER), 0, 0.02)
+    sim = Sim(numel, nd, dtype, p16, master if master_given else None, mode, per_tensor_params=per_tensor,
+              param_misalign=pmis, grad_misalign=gmis, align=align)
+    sim.p16_initial = p16.copy()
+    scale = 1024.0 if dtype == F16 else 1.0
+    bad_step = int(r.integers(1, 5))              # 4: no injection
+    bad_val = float(r.choice([np.inf, -np.inf, np.nan]))
+    nbuf = nd if mode == "reduce" else 1
+    for step in range(1, 4):
+        g = [synth.normal_16(psi, dtype, seed_w, synth.stream_id(synth.GRAD, q, step), 0, 1e-3 * scale * 30)
+             for q in range(nbuf)]
+        if step == bad_step:
+            g[int(r.integers(0, nbuf))][int(r.integers(0, psi))] = oracle.encode16(
+                dtype, np.array([bad_val], np.float32))[0]
+        res = sim.step(g, 1.0 / scale, max_norm, hp, fuse=fuse)
+        assert all(x["skipped"] == (step == bad_step) for x in res)
+        sim.compare()

@@ -24,7 +24,8 @@ def st():
 @pytest.mark.parametrize("epb,u,bs", [(2048, 2, 256), (2048, 4, 512), (1024, 4, 256), (8192, 1, 256)])
 def test_probes_touch_every_element(epb, u, bs):
     n = 3 * epb + 4 * 37                                   # a partial last block
-    g = torch.randint(-2000, 2000, (n,), dtype=torch.int16, device="cuda")
+    # finite, normal bf16 bit patterns (0x0080..0x3F7F: 2^-126 <= x < 1), so every sum is a number
+    g = torch.randint(0x0080, 0x3F80, (n,), dtype=torch.int16, device="cuda")
     w0, m0, v0 = (torch.randn(n, device="cuda") for _ in range(3))
     w, m, v = w0.clone(), m0.clone(), v0.clone()
     p = torch.zeros(n, dtype=torch.int16, device="cuda")
@@ -57,9 +58,9 @@ def test_probes_touch_every_element(epb, u, bs):
         q = (min(epb, n - b * epb)) // 4
         exp_sink.append(4.0 * sum(max(0, -(-(q - t) // bs)) for t in range(64)))
     assert sink[:nb].cpu().tolist() == exp_sink
-    srcs = [torch.randint(-500, 500, (n,), dtype=torch.int16, device="cuda") for _ in range(4)]
+    srcs = [torch.randint(0x0080, 0x3F80, (n,), dtype=torch.int16, device="cuda") for _ in range(4)]
     out = torch.zeros(n, device="cuda")
     probes.reduce_mix([x.data_ptr() for x in srcs], out.data_ptr(), n, st(), epb, u, bs, 1)
     torch.cuda.synchronize()
-    exp = sum((x.to(torch.int32) << 16).view(torch.float32) for x in srcs)
-    assert torch.allclose(out, exp, rtol=1e-6, atol=0)
+    exp = sum((x.to(torch.int32) << 16).view(torch.float32) for x in srcs)    # the probe's order: ((0 + s0) + s1) + ...
+    assert torch.equal(out, exp)
