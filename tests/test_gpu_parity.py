@@ -980,3 +980,59 @@ def test_random_small_configurations(seed):
         res = sim.step(g, 1.0 / scale, max_norm, hp, fuse=fuse)
         assert all(x["skipped"] == (step == bad_step) for x in res)
         sim.compare()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configurations_with_the_next_rows(seed):
+    """Seeded random configurations that combine the step's extensions: 1-3 micro-steps
+    (the last one fused into the intake or accumulated and taken with ZERO_ACCUMULATED), the
+    device-resident dynamic loss scale, the 16-bit output of the local reduce and a tracked
+    segmented write-back, over random tensor lists, N_d, dtypes, gradient modes and layouts;
+    three steps with a non-finite value injected into a random micro-step of a random step (or
+    none).  Every rank's state, 16-bit slice and loss scale must match the oracle bit for bit."""
+    r = np.random.default_rng(0x5EED3000 + seed)
+    T = int(r.integers(1, 9))
+    numel = [int(x) for x in r.integers(1, 30001, size=T)]
+    psi = sum(numel)
+    nd = int(r.integers(1, 6))
+    dtype = int(r.choice([F16, BF16]))
+    mode = str(r.choice(["reduce", "flat", "ragged", "registered_flat"]))
+    K = int(r.integers(1, 4))
+    last_fused = bool(r.random() < 0.5)
+    out16 = mode == "reduce" and nd >= 2 and bool(r.random() < 0.5)
+    dynamic = bool(r.random() < 0.6)
+    segments = int(r.choice([0, 3, 17]))
+    fuse = bool(r.random() < 0.6)
+    per_tensor = bool(r.random() < 0.5)
+    max_norm = float(r.choice([0.0, 1.0, 1e-3]))
+    hp = oracle.HParams(1e-3, 0.9, 0.999, 1e-8, float(r.choice([0.0, 0.01])))
+    seed_w = 0x5EED4000 + seed
+    print(f"[random-next {seed}] T {T} psi {psi} N_d {nd} dtype {dtype} mode {mode} K {K} last_fused {last_fused} "
+          f"out16 {out16} dynamic {dynamic} segments {segments} fuse {fuse} per_tensor {per_tensor}", flush=True)
+    master = synth.normal_f32(psi, seed_w, synth.stream_id(synth.MASTER), 0, 0.02)
+    p16 = oracle.encode16(dtype, master)
+    sim = Sim(numel, nd, dtype, p16, master, mode, per_tensor_params=per_tensor, param_misalign=(0, 3),
+              grad_misalign=(1,), with_red=True, segments=segments)
+    sim.p16_initial = p16.copy()
+    if out16:
+        sim.set_reduce_out16(True)
+    scale = 1024.0 if dtype == F16 else 1.0
+    if dynamic:
+        sim.enable_dynamic(init_scale=float(2.0 ** int(r.integers(4, 12))), growth=2.0, backoff=0.5,
+                           interval=int(r.integers(1, 3)), min_scale=1.0)
+    bad_step = int(r.integers(1, 5))
+    bad_micro = int(r.integers(0, K))
+    nbuf = nd if mode == "reduce" else 1
+    for step in range(1, 4):
+        micro = [[synth.normal_16(psi, dtype, seed_w, synth.stream_id(synth.GRAD, q, 100 * step + k), 0, 30e-3 * scale)
+                  for q in range(nbuf)] for k in range(K)]
+        if step == bad_step:
+            micro[bad_micro][int(r.integers(0, nbuf))][int(r.integers(0, psi))] = oracle.encode16(
+                dtype, np.array([np.inf], np.float32))[0]
+        inv = None if dynamic else 1.0 / scale
+        if K == 1:
+            res = sim.step(micro[0], inv, max_norm, hp, fuse=fuse)
+        else:
+            res = sim.step_accumulated(micro, inv, max_norm, hp, fuse=fuse, last_fused=last_fused)
+        assert all(x["skipped"] == (step == bad_step) for x in res)
+        sim.compare()
