@@ -777,8 +777,8 @@ def measure(a, config, rank, primary=True):
                      "avg_launch_ms": adam_ms},
         "setup_s": setup_s,
     }
-    # the same step rate with the benchmark spec's byte count (28 B/param for the step, plus 2 B per
-    # rank buffer when reducing: the second read of the gradient is not counted)
+    # the same step rate at 28 B/param (the read of g, w, m, v and the writes of w, m, v, p16, plus
+    # 2 B per rank buffer when reducing): the second read of the gradient is not counted
     ns_b = 28 + (2 * w.nd if w.grad_mode == "reduce" else 0)
     out["hbm_gbps_step_28b"] = ns_b * valid / (ms_step * 1e-3) / 1e9
     out["bytes_per_param_28b"] = ns_b
@@ -848,8 +848,9 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(json.dumps({"error": f"this benchmark runs one data-parallel rank on one GPU; --gpus {a.gpus} "
-                                   "is not supported (the path has no collectives: see the design notes "
-                                   "for how it shards)"}), flush=True)
+                                   "is not supported (the path has no collectives: each rank would run this "
+                                   "step on its own shard, with the reduce-scatter before it, a two-scalar "
+                                   "all-reduce between its passes and the all-gather after it)"}), flush=True)
         sys.exit(2)
     import torch
     from synth import recipes

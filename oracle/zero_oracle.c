@@ -21,9 +21,9 @@
  *    not copy fp32 into fp16: "DeepSpeed ZeRO" 权重更新的触发条件.
  *  - the Adam formulas m, v, W: "DeepSpeed ZeRO" ZeRO Stage 1, "以 AdaW 为例".
  *  - the in-place 16-bit copy of the updated fp32 slice: same page, step 4 text.
- * Readings where the pages are silent (bias correction, decoupled weight decay,
- * clipping, the reduce order, the partition rule) are listed in the design notes
- * and restated at each function below.
+ * Where the pages are silent (bias correction, decoupled weight decay, clipping,
+ * the reduce order, the partition rule, the NaN encoding), the reading taken is
+ * stated at each function below.
  */
 #include <math.h>
 #include <stdint.h>

@@ -20,7 +20,7 @@
 
 #include "zs_internal.h"
 
-// Tuning knobs (measured on MI355X; see the design notes):
+// Tuning knobs (each set to the value measured fastest on MI355X):
 //   ZS_ADAM_U   quads per lane in flight in the Adam pass
 //   ZS_STATS_U  quads per lane in flight in the statistics pass
 //   ZS_STATS_NT_BYTES  a statistics pass over a gradient slice of more bytes than this (the
