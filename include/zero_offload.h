@@ -117,7 +117,8 @@ zero_status_t zero_offload_grad_stats(zero_offload_t h, float inv_loss_scale, in
  * operation rounded to nearest even and no fused multiply-add,
  *   g = u * clip; m = b1 m + (1-b1) g; v = b2 v + (1-b2) g g;
  *   w = w - lr * ((m / bc1) / (sqrt(v / bc2) + eps) + wd * w);
- *   param16 = round-to-nearest-even 16-bit value of w
+ *   param16 = round-to-nearest-even 16-bit value of w (a NaN w: the positive
+ *             canonical quiet NaN, as zero_cast_params writes it)
  * ("DeepSpeed ZeRO", ZeRO Stage 1, 以 AdaW 为例, with the readings of
  * zero_adam_step).  A skipped step changes nothing and copies nothing
  * ("DeepSpeed ZeRO", 权重更新的触发条件).  push != 0 (needs a device handle)

@@ -381,7 +381,13 @@ zero_status_t zero_adam_step(zero_shard_t h, const zero_adam_hparams_t* hp, int3
 /* In-place write-back p16 = round-to-nearest-even(master) of this rank's
  * valid elements ("DeepSpeed ZeRO" 权重更新的触发条件, step 4: fp32 copied
  * into fp16 in place); nothing outside the shard is touched, nothing at all
- * after a skipped step.  No-op when the step fused the cast. */
+ * after a skipped step.  fp16: IEEE binary16 with subnormals, overflow to
+ * +-inf; bf16: the top half of the binary32, rounded.  Every NaN master value,
+ * whatever its sign and payload, is written as the format's positive
+ * canonical quiet NaN (0x7E00, 0x7FC0): IEEE 754 leaves an arithmetic NaN's
+ * sign and payload open and machines differ, so keeping them would make the
+ * written bits machine-dependent.  The same encoding serves the fused cast of
+ * zero_adam_step.  No-op when the step fused the cast. */
 zero_status_t zero_cast_params(zero_shard_t h, void* stream);
 
 /* Plan sizes of an initialised handle. */
