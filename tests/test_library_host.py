@@ -177,3 +177,34 @@ def test_static_init_refuses_before_device_work():
     hdr = open(os.path.join(ROOT, "include", "zero_shard.h")).read()
     assert re.search(r"#define ZERO_STATIC_WORKSPACE_BYTES \(8 \* 1024 \* 1024\)", hdr)
     assert _abi.ZERO_STATIC_WORKSPACE_BYTES == 8 * 1024 * 1024
+
+
+def test_plan_matches_oracle_on_random_lists():
+    """Property check over random descriptions (hypothesis): tensor lists of 1-40 tensors
+    (empty ones included, totals up to about 2^35 elements), N_d 1-128, every alignment that is a
+    multiple of 8 up to 4096, flat or per-tensor parameters.  For every rank the library's plan
+    equals the oracle's partition (psi, S, shard start, valid length), the state covers the
+    valid elements with at most 7 padding floats per piece plus the 64-float rounding, the
+    ranks' valid lengths sum to psi, and the model-state bytes follow 4 psi + 12 state_elems."""
+    from hypothesis import given, settings, strategies as st
+
+    @settings(max_examples=150, deadline=None, derandomize=True)
+    @given(numel=st.lists(st.one_of(st.just(0), st.integers(1, 70000), st.integers(1, 1 << 30)), min_size=1,
+                          max_size=40),
+           nd=st.integers(1, 128), align8=st.integers(1, 512), per_tensor=st.booleans(), data=st.data())
+    def check(numel, nd, align8, per_tensor, data):
+        align = 8 * align8
+        ranks = sorted({0, nd - 1, data.draw(st.integers(0, nd - 1))})
+        total_valid = 0
+        for r in ranks:
+            info = zpm.zero_shard_plan(desc_for(numel, nd, r, per_tensor=per_tensor, align=align))
+            psi, S, b, valid = oracle.plan(numel, nd, r, align)
+            assert (info.psi, info.shard_elems, info.shard_begin, info.valid_elems) == (psi, S, b, valid)
+            pieces = oracle.shard_pieces(numel, b, valid)
+            assert valid <= info.state_elems <= valid + 8 * len(pieces) + 64
+            assert info.model_state_bytes == 4 * psi + 12 * info.state_elems
+        for r in range(nd):
+            total_valid += oracle.plan(numel, nd, r, align)[3]
+        assert total_valid == sum(numel)
+
+    check()
