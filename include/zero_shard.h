@@ -152,8 +152,8 @@ zero_status_t zero_shard_init(const zero_shard_desc_t* desc, const zero_shard_bu
 
 /* Size in bytes of the library's static device workspace (one per device): the
  * largest workspace_bytes a handle made by zero_shard_init_static may need.
- * 8 MiB holds the workspace of shards of up to about 140,000 work items (one
- * flat tensor of about 1.1e9 elements; fewer elements when a ragged tensor
+ * 8 MiB holds the workspace of shards of up to about 100,000 work items (one
+ * flat tensor of about 8.2e8 elements; fewer elements when a ragged tensor
  * list cuts the shard into more pieces). */
 #define ZERO_STATIC_WORKSPACE_BYTES (8 * 1024 * 1024)
 

@@ -378,6 +378,27 @@ __device__ __forceinline__ void walk_chunks(const Chunk* chunks, int64_t n_chunk
   for (int64_t c = c0; c < c1; ++c) body(chunk_ref(chunks + c));
 }
 
+// Walks block b's part (b % ppc) of chunk b / ppc: a run of consecutive elements whose
+// length is a multiple of 8 (the last part takes the rest), so the parts of a chunk keep
+// its alignment.  ppc == 1 walks one whole chunk per block.
+template <class Body>
+__device__ __forceinline__ void walk_parts(const Chunk* chunks, int64_t n_chunks, int32_t ppc, Body body) {
+  const int64_t c = (int64_t)blockIdx.x / ppc;
+  if (c >= n_chunks) return;
+  ChunkRef ch = chunk_ref(chunks + c);
+  if (ppc > 1) {
+    const int64_t part = (int64_t)blockIdx.x % ppc;
+    const int64_t sub = ((ch.len + ppc - 1) / ppc + 7) & ~(int64_t)7;
+    const int64_t lo = part * sub;
+    if (lo >= ch.len) return;
+    ch.len = (lo + sub < ch.len ? lo + sub : ch.len) - lo;
+    ch.state_off += lo;
+    ch.flat_off += lo;
+    if (ch.g16) ch.g16 += 2 * (uint64_t)lo;
+  }
+  body(ch);
+}
+
 template <int DT, bool NT>
 __global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
   Stats16Op<DT, NT> op{nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc), SumSq{}};
@@ -400,6 +421,7 @@ struct ReduceArgs {
   int32_t dyn;             // as in StatsArgs
   float* red;
   int32_t cpb;             // consecutive chunks per block of the intake passes
+  int32_t ppc;             // parts per chunk of the local-reduce intake passes (cpb is then 1)
   int32_t flip;            // as in StatsArgs
   DevScalars* sc;
   IntakeParts parts;
@@ -520,7 +542,7 @@ template <int DT, int NR, bool ACC, bool R16 = false, bool STORE = true>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
   ReduceOp<DT, NR, ACC, R16, STORE> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc),
                                 SumSq{}};
-  walk_chunks(a.chunks, a.n_chunks, a.cpb, [&](const ChunkRef ch) {
+  walk_parts(a.chunks, a.n_chunks, a.ppc, [&](const ChunkRef ch) {
     op.gs.flat_off = ch.flat_off;
     op.gs.src0 = reinterpret_cast<const uint16_t*>(ch.g16);
     op.red = a.red + ch.state_off;
@@ -562,7 +584,7 @@ struct Reduce16Op {
 template <int DT, int NR>
 __global__ void __launch_bounds__(kBlock) reduce16_kernel(ReduceArgs a) {
   Reduce16Op<DT, NR> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc), SumSq{}};
-  walk_chunks(a.chunks, a.n_chunks, a.cpb, [&](const ChunkRef ch) {
+  walk_parts(a.chunks, a.n_chunks, a.ppc, [&](const ChunkRef ch) {
     op.gs.flat_off = ch.flat_off;
     op.red16 = reinterpret_cast<uint16_t*>(a.red) + ch.state_off;
     const int head = head16(op.gs.src(0));
@@ -1118,6 +1140,7 @@ static ReduceArgs make_reduce_args(const Chunk* chunks, int64_t n_chunks, const 
   a.dyn = dyn;
   a.red = red;
   a.cpb = 1;
+  a.ppc = kIntakeParts;
   a.flip = flip;
   a.sc = sc;
   a.parts = parts;
@@ -1149,7 +1172,7 @@ hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const
     return hipGetLastError();
   }
   const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, inv, dyn, flip, red, sc, parts);
-  const unsigned g = intake_grid(n_chunks, a.cpb);
+  const unsigned g = clamp_grid(n_chunks * a.ppc, n_chunks * a.ppc);
   const int src = src_code(n_ranks);
   if (keep_acc) {
     if (!accumulate || !(src == 1 || src == kSrcChunk || src == kSrcNone)) return hipErrorInvalidValue;

@@ -504,7 +504,7 @@ zero_status_t offload_init(const zero_shard_desc_t* desc, const zero_offload_buf
     hipStream_t st = static_cast<hipStream_t>(stream);
     zs::DevScalars init_sc;
     memset(&init_sc, 0, sizeof(init_sc));
-    const int64_t n_groups = (h->n_chunks + zs::kGroup - 1) / zs::kGroup;
+    const int64_t n_groups = zs::intake_groups(h->n_chunks);
     hipError_t e;
     if ((e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&h->stats_ev, hipEventDisableTiming)) != hipSuccess ||

@@ -301,7 +301,7 @@ zero_status_t shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t*
       break;
     }
     // the intake passes' group counters start at zero (and are re-armed by every pass)
-    const int64_t n_groups = (h->n_chunks + zs::kGroup - 1) / zs::kGroup;
+    const int64_t n_groups = zs::intake_groups(h->n_chunks);
     if ((e = zs::launch_fill_zero(reinterpret_cast<float*>(h->parts.gcount),
                                   n_groups * (int64_t)(sizeof(zs::GroupCount) / sizeof(float)), st)) != hipSuccess) {
       rs = hip_fail("group counters", e);

@@ -17,6 +17,13 @@ namespace zs {
 constexpr int64_t kChunk = ZS_CHUNK;
 // Local-reduce fan-in limit (rank pointers travel as kernel arguments).
 constexpr int kMaxRanks = 64;
+// Parts per chunk of the local-reduce intake passes (one block per part, one partial
+// sum per part): 2048-element parts measured 5-6% faster than whole chunks for the
+// local reduce of 8 ranks, 1024-element parts slower.
+#ifndef ZS_REDUCE_PARTS
+#define ZS_REDUCE_PARTS 4
+#endif
+constexpr int kIntakeParts = ZS_REDUCE_PARTS;
 constexpr int kBlock = 256;
 // Blocks of an intake pass whose partial sums one group combines (a group's last
 // block adds them; the last group adds the group sums).
@@ -120,16 +127,17 @@ constexpr int64_t kSegOff = sizeof(DevScalars);
 constexpr int64_t kChunksOff = kSegOff + kMaxSegments * (int64_t)sizeof(SegState);
 
 // Workspace after the chunk table: per-block partials, group counters and group
-// sums, sized for the largest intake grid (one block per chunk).
+// sums, sized for the largest intake grid (one block per part of a chunk).
 struct IntakeLayout {
   int64_t part_off, gcount_off, gpart_off, end;
 };
+inline int64_t intake_groups(int64_t n_chunks) { return (n_chunks * kIntakeParts + kGroup - 1) / kGroup; }
 inline IntakeLayout intake_layout(int64_t n_chunks) {
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  const int64_t n_groups = (n_chunks + kGroup - 1) / kGroup;
+  const int64_t n_groups = intake_groups(n_chunks);
   IntakeLayout l;
   l.part_off = up(kChunksOff + n_chunks * (int64_t)sizeof(Chunk));
-  l.gcount_off = up(l.part_off + 8 * n_chunks);
+  l.gcount_off = up(l.part_off + 8 * n_chunks * kIntakeParts);
   l.gpart_off = up(l.gcount_off + n_groups * (int64_t)sizeof(GroupCount));
   l.end = up(l.gpart_off + 8 * n_groups);
   return l;
