@@ -1,11 +1,12 @@
 // gfx950 kernels of the partitioned mixed-precision optimizer step.
 //
 // The kernels walk the shard's chunk table (chunks of at most kChunk elements
-// inside one tensor piece).  The intake passes launch one short-lived block per
-// chunk (or per run of a few consecutive chunks on small shards) and combine
-// their sums of squares in a fixed two-level order without float atomics (see
-// finish_stats); the Adam pass launches one short-lived block per part of a
-// chunk.  The hardware dispatcher balances the load in both.
+// inside one tensor piece).  The statistics pass launches one short-lived block
+// per chunk (or per run of a few consecutive chunks on small shards), the local
+// reduce one per part of a chunk; both combine their sums of squares in a fixed
+// two-level order without float atomics (see finish_stats).  The Adam pass
+// launches one short-lived block per part of a chunk.  The hardware dispatcher
+// balances the load in all of them.
 // Inside a run of elements a block peels at most 3 leading elements, streams
 // the body as 4-element quads -- 8-byte loads and stores of 16-bit data,
 // 16-byte loads and stores of fp32 data, each wave covering 256 consecutive
