@@ -1141,7 +1141,7 @@ static ReduceArgs make_reduce_args(const Chunk* chunks, int64_t n_chunks, const 
   a.dyn = dyn;
   a.red = red;
   a.cpb = 1;
-  a.ppc = kIntakeParts;
+  a.ppc = 1;
   a.flip = flip;
   a.sc = sc;
   a.parts = parts;
@@ -1172,9 +1172,12 @@ hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const
     hipLaunchKernelGGL(empty_stats_kernel, dim3(1), dim3(1), 0, st, sc, (int32_t)flip);
     return hipGetLastError();
   }
-  const ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, inv, dyn, flip, red, sc, parts);
-  const unsigned g = clamp_grid(n_chunks * a.ppc, n_chunks * a.ppc);
   const int src = src_code(n_ranks);
+  ReduceArgs a = make_reduce_args(chunks, n_chunks, ranks, n_ranks, inv, dyn, flip, red, sc, parts);
+  // Parts of a chunk pay off where a block reads several rank slices; over one
+  // 16-bit source (and the accumulator) whole chunks per block measured faster.
+  a.ppc = is_rank_reduce(src) ? kIntakeParts : 1;
+  const unsigned g = clamp_grid(n_chunks * a.ppc, n_chunks * a.ppc);
   if (keep_acc) {
     if (!accumulate || !(src == 1 || src == kSrcChunk || src == kSrcNone)) return hipErrorInvalidValue;
     if (dtype == ZERO_BF16) launch_acc_stats<ZERO_BF16>(a, src, g, st);

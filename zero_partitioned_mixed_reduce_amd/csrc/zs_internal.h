@@ -17,9 +17,9 @@ namespace zs {
 constexpr int64_t kChunk = ZS_CHUNK;
 // Local-reduce fan-in limit (rank pointers travel as kernel arguments).
 constexpr int kMaxRanks = 64;
-// Parts per chunk of the local-reduce intake passes (one block per part, one partial
-// sum per part): 2048-element parts measured 5-6% faster than whole chunks for the
-// local reduce of 8 ranks, 1024-element parts slower.
+// Parts per chunk of the local-reduce intake passes over several rank slices (one
+// block per part, one partial sum per part): 2048-element parts measured 5-6% faster
+// than whole chunks for the local reduce of 8 ranks, 1024-element parts slower.
 #ifndef ZS_REDUCE_PARTS
 #define ZS_REDUCE_PARTS 4
 #endif
