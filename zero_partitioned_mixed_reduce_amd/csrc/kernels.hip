@@ -379,23 +379,31 @@ __device__ __forceinline__ void walk_chunks(const Chunk* chunks, int64_t n_chunk
   for (int64_t c = c0; c < c1; ++c) body(chunk_ref(chunks + c));
 }
 
-// Walks block b's part (b % ppc) of chunk b / ppc: a run of consecutive elements whose
-// length is a multiple of 8 (the last part takes the rest), so the parts of a chunk keep
-// its alignment.  ppc == 1 walks one whole chunk per block.
+// Part `part` of `n_parts` of a chunk of `chunk_len` elements: [lo, lo + len), every
+// part but the last of a length that is a multiple of 8, so the parts keep the chunk's
+// alignment.  Trailing parts of a short chunk are empty (len <= 0).
+struct Part {
+  int64_t lo, len;
+};
+__device__ __forceinline__ Part chunk_part(int64_t chunk_len, int64_t part, int64_t n_parts) {
+  const int64_t sub = ((chunk_len + n_parts - 1) / n_parts + 7) & ~(int64_t)7;
+  const int64_t lo = part * sub;
+  return Part{lo, (lo + sub < chunk_len ? lo + sub : chunk_len) - lo};
+}
+
+// Walks block b's part (b % ppc) of chunk b / ppc.  ppc == 1 walks one whole chunk per block.
 template <class Body>
 __device__ __forceinline__ void walk_parts(const Chunk* chunks, int64_t n_chunks, int32_t ppc, Body body) {
   const int64_t c = (int64_t)blockIdx.x / ppc;
   if (c >= n_chunks) return;
   ChunkRef ch = chunk_ref(chunks + c);
   if (ppc > 1) {
-    const int64_t part = (int64_t)blockIdx.x % ppc;
-    const int64_t sub = ((ch.len + ppc - 1) / ppc + 7) & ~(int64_t)7;
-    const int64_t lo = part * sub;
-    if (lo >= ch.len) return;
-    ch.len = (lo + sub < ch.len ? lo + sub : ch.len) - lo;
-    ch.state_off += lo;
-    ch.flat_off += lo;
-    if (ch.g16) ch.g16 += 2 * (uint64_t)lo;
+    const Part p = chunk_part(ch.len, (int64_t)blockIdx.x % ppc, ppc);
+    if (p.len <= 0) return;
+    ch.len = p.len;
+    ch.state_off += p.lo;
+    ch.flat_off += p.lo;
+    if (ch.g16) ch.g16 += 2 * (uint64_t)p.lo;
   }
   body(ch);
 }
@@ -421,8 +429,7 @@ struct ReduceArgs {
   float inv;
   int32_t dyn;             // as in StatsArgs
   float* red;
-  int32_t cpb;             // consecutive chunks per block of the intake passes
-  int32_t ppc;             // parts per chunk of the local-reduce intake passes (cpb is then 1)
+  int32_t ppc;             // parts per chunk of the local-reduce intake passes
   int32_t flip;            // as in StatsArgs
   DevScalars* sc;
   IntakeParts parts;
@@ -632,16 +639,13 @@ __global__ void __launch_bounds__(kBlock) accum_kernel(ReduceArgs a) {
   const int64_t n_items = a.n_chunks * ZS_ADAM_SPLIT;
   for (int64_t i = blockIdx.x; i < n_items; i += gridDim.x) {
     const Chunk ch = a.chunks[i / ZS_ADAM_SPLIT];
-    const int64_t part = i % ZS_ADAM_SPLIT;
-    const int64_t sub = ((ch.len + ZS_ADAM_SPLIT - 1) / ZS_ADAM_SPLIT + 7) & ~(int64_t)7;
-    const int64_t lo = part * sub;
-    if (lo >= ch.len) continue;
-    const int64_t len = (lo + sub < ch.len ? lo + sub : ch.len) - lo;
-    op.gs.flat_off = ch.flat_off + lo;
-    op.gs.src0 = reinterpret_cast<const uint16_t*>(ch.g16) + lo;
-    op.red = a.red + ch.state_off + lo;
+    const Part p = chunk_part(ch.len, i % ZS_ADAM_SPLIT, ZS_ADAM_SPLIT);
+    if (p.len <= 0) continue;
+    op.gs.flat_off = ch.flat_off + p.lo;
+    op.gs.src0 = reinterpret_cast<const uint16_t*>(ch.g16) + p.lo;
+    op.red = a.red + ch.state_off + p.lo;
     const int head = op.gs.head(op.red);
-    run_chunk<ZS_REDUCE_U, 4>(op, len, head, op.gs.aligned_at(head, op.red));
+    run_chunk<ZS_REDUCE_U, 4>(op, p.len, head, op.gs.aligned_at(head, op.red));
   }
 }
 
@@ -907,36 +911,34 @@ __global__ void __launch_bounds__(ZS_ADAM_BLOCK) adam_kernel(AdamArgs a) {
   const int64_t n_items = a.n_chunks * kSplit;
   for (int64_t i = blockIdx.x; i < n_items; i += gridDim.x) {
     const Chunk ch = a.chunks[i / kSplit];
-    const int64_t part = i % kSplit;
-    const int64_t sub = ((ch.len + kSplit - 1) / kSplit + 7) & ~(int64_t)7;
-    const int64_t lo = part * sub;
-    if (lo < ch.len) {
-    const int64_t len = (lo + sub < ch.len ? lo + sub : ch.len) - lo;
-    op.w = a.master + ch.state_off + lo;
-    op.m = a.m + ch.state_off + lo;
-    op.v = a.v + ch.state_off + lo;
-    op.p16 = reinterpret_cast<uint16_t*>(ch.p16) + lo;
-    int head;
-    bool ok;
-    if constexpr (GS == kGradRed || GS == kGradAcc) {
-      op.gred = a.red + ch.state_off + lo;
-      head = head16(op.p16);
-      ok = aligned(op.w + head, 16) && aligned(op.gred + head, 16);
-    } else {
-      op.g16 = (GS == kGradFlat16 || GS == kGradAccFlat16 ? a.flat_g + ch.flat_off
-                : GS == kGradRed16                         ? reinterpret_cast<const uint16_t*>(a.red) + ch.state_off
-                                                           : reinterpret_cast<const uint16_t*>(ch.g16)) +
-               lo;
-      head = head16(op.g16);
-      ok = aligned(op.w + head, 16) && aligned(op.g16 + head, 8);
-      if constexpr (grad_acc16<GS>()) {
+    const Part p = chunk_part(ch.len, i % kSplit, kSplit);
+    if (p.len > 0) {
+      const int64_t lo = p.lo;
+      op.w = a.master + ch.state_off + lo;
+      op.m = a.m + ch.state_off + lo;
+      op.v = a.v + ch.state_off + lo;
+      op.p16 = reinterpret_cast<uint16_t*>(ch.p16) + lo;
+      int head;
+      bool ok;
+      if constexpr (GS == kGradRed || GS == kGradAcc) {
         op.gred = a.red + ch.state_off + lo;
-        ok = ok && aligned(op.gred + head, 16);
+        head = head16(op.p16);
+        ok = aligned(op.w + head, 16) && aligned(op.gred + head, 16);
+      } else {
+        op.g16 = (GS == kGradFlat16 || GS == kGradAccFlat16 ? a.flat_g + ch.flat_off
+                  : GS == kGradRed16 ? reinterpret_cast<const uint16_t*>(a.red) + ch.state_off
+                                     : reinterpret_cast<const uint16_t*>(ch.g16)) +
+                 lo;
+        head = head16(op.g16);
+        ok = aligned(op.w + head, 16) && aligned(op.g16 + head, 8);
+        if constexpr (grad_acc16<GS>()) {
+          op.gred = a.red + ch.state_off + lo;
+          ok = ok && aligned(op.gred + head, 16);
+        }
       }
-    }
-    if constexpr (CAST) ok = ok && aligned(op.p16 + head, 8);
-    ok = ok && aligned(op.m + head, 16) && aligned(op.v + head, 16);
-    run_chunk<ZS_ADAM_U, 4, AdamOp<DT, GS, CAST, SEG>, ZS_ADAM_BLOCK>(op, len, head, ok);
+      if constexpr (CAST) ok = ok && aligned(op.p16 + head, 8);
+      ok = ok && aligned(op.m + head, 16) && aligned(op.v + head, 16);
+      run_chunk<ZS_ADAM_U, 4, AdamOp<DT, GS, CAST, SEG>, ZS_ADAM_BLOCK>(op, p.len, head, ok);
     }
     if constexpr (SEG) seg_arrive(a.seg, i, i / kSplit, (int)kSplit);
   }
@@ -1140,7 +1142,6 @@ static ReduceArgs make_reduce_args(const Chunk* chunks, int64_t n_chunks, const 
   a.inv = inv;
   a.dyn = dyn;
   a.red = red;
-  a.cpb = 1;
   a.ppc = 1;
   a.flip = flip;
   a.sc = sc;
