@@ -399,7 +399,7 @@ __device__ __forceinline__ void walk_parts(const Chunk* chunks, int64_t n_chunks
   ChunkRef ch = chunk_ref(chunks + c);
   if (ppc > 1) {
     const Part p = chunk_part(ch.len, (int64_t)blockIdx.x % ppc, ppc);
-    if (p.len <= 0) return;
+    if (p.lo >= ch.len) return;
     ch.len = p.len;
     ch.state_off += p.lo;
     ch.flat_off += p.lo;
@@ -640,7 +640,7 @@ __global__ void __launch_bounds__(kBlock) accum_kernel(ReduceArgs a) {
   for (int64_t i = blockIdx.x; i < n_items; i += gridDim.x) {
     const Chunk ch = a.chunks[i / ZS_ADAM_SPLIT];
     const Part p = chunk_part(ch.len, i % ZS_ADAM_SPLIT, ZS_ADAM_SPLIT);
-    if (p.len <= 0) continue;
+    if (p.lo >= ch.len) continue;
     op.gs.flat_off = ch.flat_off + p.lo;
     op.gs.src0 = reinterpret_cast<const uint16_t*>(ch.g16) + p.lo;
     op.red = a.red + ch.state_off + p.lo;
@@ -912,7 +912,7 @@ __global__ void __launch_bounds__(ZS_ADAM_BLOCK) adam_kernel(AdamArgs a) {
   for (int64_t i = blockIdx.x; i < n_items; i += gridDim.x) {
     const Chunk ch = a.chunks[i / kSplit];
     const Part p = chunk_part(ch.len, i % kSplit, kSplit);
-    if (p.len > 0) {
+    if (p.lo < ch.len) {
       const int64_t lo = p.lo;
       op.w = a.master + ch.state_off + lo;
       op.m = a.m + ch.state_off + lo;
