@@ -468,6 +468,8 @@ zero_status_t offload_init(const zero_shard_desc_t* desc, const zero_offload_buf
   h->stats_inv = 0.0f;
 
   auto cleanup_events = [&]() {
+    // copies already enqueued on the caller's stream may still read the set-up's host tables
+    if (has_device) (void)hipStreamSynchronize(static_cast<hipStream_t>(stream));
     for (hipEvent_t e : h->fetch_ev)
       if (e) (void)hipEventDestroy(e);
     h->fetch_ev.clear();

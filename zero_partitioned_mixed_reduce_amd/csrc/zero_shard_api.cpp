@@ -318,6 +318,8 @@ zero_status_t shard_init(const zero_shard_desc_t* desc, const zero_shard_bufs_t*
     }
   } while (0);
   if (rs != ZERO_OK) {
+    // copies already enqueued may still read init_sc and the plan's chunk table
+    (void)hipStreamSynchronize(st);
     if (h->wb_event) (void)hipEventDestroy(h->wb_event);
     delete h;
     return rs;
