@@ -87,8 +87,8 @@ typedef struct {
   int32_t dtype;              /* zero_dtype_t of the 16-bit parameters and gradients         */
   int32_t align;              /* shard length is a multiple of this many elements; 0 -> 64;  */
                               /* must be a multiple of 8                                      */
-  int64_t num_tensors;        /* T >= 1 tensors, flattened in this order                     */
-  const int64_t* numel;       /* host [T], each >= 0; psi = sum                               */
+  int64_t num_tensors;        /* 1 <= T <= 2^31 - 1 tensors, flattened in this order         */
+  const int64_t* numel;       /* host [T], each >= 0; psi = sum <= 2^60                       */
   void* const* param16;       /* host [T] of device pointers, one per tensor, or NULL         */
   void* flat_param16;         /* device [psi] flat 16-bit parameters, or NULL                 */
                               /* (exactly one of param16 / flat_param16)                      */

@@ -113,6 +113,17 @@ def test_errors_are_reported():
     d = desc_for([100, -1], 2, 0)
     with pytest.raises(zpm.ZeroError):
         zpm.zero_shard_plan(d)
+    # sizes whose byte counts would leave int64: more than 2^60 elements, more than 2^31 - 1 tensors
+    assert zpm.zero_shard_plan(desc_for([1 << 59, 1 << 59], 1 << 30, 0)).psi == 1 << 60   # 2^30-element shard
+    for numel in ([1 << 59, 1 << 59, 1], [(1 << 63) - 1, (1 << 63) - 1]):
+        with pytest.raises(zpm.ZeroError) as e:
+            zpm.zero_shard_plan(desc_for(numel, 1, 0))
+        assert e.value.status == _abi.ZERO_EINVAL and "2^60" in str(e.value)
+    d = desc_for([100], 1, 0)
+    d.num_tensors = 1 << 31                      # numel is never read past the count check
+    with pytest.raises(zpm.ZeroError) as e:
+        zpm.zero_shard_plan(d)
+    assert "num_tensors" in str(e.value)
     # null handles are rejected, not dereferenced
     assert _abi.lib().zero_cast_params(None, None) == _abi.ZERO_EINVAL
     assert "null handle" in zpm.zero_last_error()

@@ -13,6 +13,7 @@
 // the kernels can use vector loads on both after peeling at most 3 elements.
 // Pieces are cut into chunks of at most kChunk elements whose starts (after
 // the first) are 8-element aligned in the 16-bit data.
+#include <stdint.h>
 #include <string.h>
 
 #include "zs_internal.h"
@@ -20,6 +21,10 @@
 namespace zs {
 
 static int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Largest model: every byte count and flat byte offset derived from psi stays far
+// inside int64 (the model-state count is about 16 psi).
+static constexpr int64_t kMaxPsi = int64_t{1} << 60;
 
 zero_status_t build_plan(const zero_shard_desc_t* d, Plan* out, std::string* err) {
   if (!d || !out) {
@@ -39,8 +44,8 @@ zero_status_t build_plan(const zero_shard_desc_t* d, Plan* out, std::string* err
     *err = "align must be a positive multiple of 8";
     return ZERO_EINVAL;
   }
-  if (d->num_tensors < 1 || !d->numel) {
-    *err = "need num_tensors >= 1 and a numel array";
+  if (d->num_tensors < 1 || d->num_tensors > INT32_MAX || !d->numel) {
+    *err = "need 1 <= num_tensors <= 2^31 - 1 and a numel array";
     return ZERO_EINVAL;
   }
   if ((d->param16 == nullptr) == (d->flat_param16 == nullptr)) {
@@ -56,6 +61,10 @@ zero_status_t build_plan(const zero_shard_desc_t* d, Plan* out, std::string* err
   for (int64_t k = 0; k < T; ++k) {
     if (d->numel[k] < 0) {
       *err = "numel must be >= 0";
+      return ZERO_EINVAL;
+    }
+    if (d->numel[k] > kMaxPsi - psi) {
+      *err = "the model exceeds 2^60 elements";
       return ZERO_EINVAL;
     }
     if (d->numel[k] > 0 && d->param16 && !d->param16[k]) {
