@@ -601,17 +601,31 @@ def bench_offload(a, w, rank):
 INFINITY_CACHE_BYTES = 256 << 20
 
 
-def hbm_side(w, valid, micro_steps, reduce_out16, step_b, adam_b):
+STATS_TAIL_BYTES = 256 << 20   # a larger slice's tail that the statistics pass leaves in the cache
+
+
+def hbm_side(w, valid, micro_steps, reduce_out16, step_b, adam_b, segments=0):
     """HBM-side bytes per parameter where they differ from the fabric-side (L2-requested)
-    count: a gradient slice that fits in the 256 MB Infinity Cache is read by the statistics
-    pass with plain loads and re-read by the Adam pass from the cache, so the second read
-    does not reach HBM.  Returns (step, adam, note)."""
+    count.  A 16-bit gradient slice that fits in the 256 MiB Infinity Cache is read by the
+    statistics pass with plain loads and re-read by the Adam pass from the cache, so the
+    second read does not reach HBM.  Of a larger slice the statistics pass reads the last
+    256 MiB with plain loads and the Adam pass (walking from the end, unless the write-back
+    tracks segments) re-reads those from the cache.  Returns (step, adam, note)."""
     slice_bytes = 2 * valid
-    if w.grad_mode != "reduce" and micro_steps == 1 and slice_bytes <= INFINITY_CACHE_BYTES:
-        return step_b - 2, adam_b - 2, (f"the {slice_bytes / 1e6:.0f} MB gradient slice fits in the 256 MB Infinity "
+    fabric = "HBM-side bytes equal the fabric count"
+    if w.grad_mode == "reduce" or micro_steps > 1 or valid == 0:
+        return step_b, adam_b, "no re-read of a 16-bit gradient slice in this step: " + fabric
+    unseen = "(no hardware counter separates the two on gfx950)"
+    if slice_bytes <= INFINITY_CACHE_BYTES:
+        return step_b - 2, adam_b - 2, (f"the {slice_bytes / 1e6:.0f} MB gradient slice fits in the 256 MiB Infinity "
                                         "Cache: the Adam pass re-reads it from there, so HBM moves 2 B/param less "
-                                        "than the fabric count (no hardware counter separates the two on gfx950)")
-    return step_b, adam_b, "no re-read fits in the 256 MB Infinity Cache: HBM-side bytes equal the fabric count"
+                                        "than the fabric count " + unseen)
+    if segments:
+        return step_b, adam_b, "with tracked segments the Adam pass walks forward and re-reads no cached tail: " + fabric
+    d = STATS_TAIL_BYTES / valid
+    return step_b - d, adam_b - d, (f"the last 256 MiB of the {slice_bytes / 1e6:.0f} MB gradient slice stay in the "
+                                    "Infinity Cache for the Adam pass, which starts there: HBM moves "
+                                    f"{d:.4f} B/param less than the fabric count " + unseen)
 
 
 def probe_ceiling(wl, adam_gbps, stats_gbps):
@@ -782,7 +796,7 @@ def measure(a, config, rank, primary=True):
     ns_b = 28 + (2 * w.nd if w.grad_mode == "reduce" else 0)
     out["hbm_gbps_step_28b"] = ns_b * valid / (ms_step * 1e-3) / 1e9
     out["bytes_per_param_28b"] = ns_b
-    hs_step, hs_adam, hs_note = hbm_side(w, valid, a.micro_steps, a.reduce_output16, step_b, adam_b)
+    hs_step, hs_adam, hs_note = hbm_side(w, valid, a.micro_steps, a.reduce_output16, step_b, adam_b, a.segments)
     if traffic is not None and stats_traffic is not None and a.micro_steps == 1 and w.grad_mode != "reduce":
         # counter-measured bytes of the step's two kernels (profiles/), over the measured step time
         step_traffic = traffic + stats_traffic

@@ -26,6 +26,10 @@
 //   ZS_STATS_U  quads per lane in flight in the statistics pass
 //   ZS_STATS_NT_BYTES  a statistics pass over a gradient slice of more bytes than this (the
 //                      Infinity Cache, 256 MiB) reads it with non-temporal loads
+//   ZS_STATS_TAIL_BYTES  ... except for its last ZS_STATS_TAIL_BYTES, read with plain loads so
+//                      they stay in the Infinity Cache; the Adam pass then walks the shard from
+//                      its end and re-reads them from there (256 MiB measured 3.8% faster on
+//                      the 389 MB GPT-2 slice than none, 240 and 320 MiB in between)
 //   ZS_STATS_SMALL  a statistics pass over fewer chunks than this takes ZS_STATS_SMALL_CPB
 //                   consecutive chunks per block (else one); the reduce passes take one
 //   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
@@ -47,6 +51,9 @@
 #endif
 #ifndef ZS_STATS_NT_BYTES
 #define ZS_STATS_NT_BYTES (256ll << 20)
+#endif
+#ifndef ZS_STATS_TAIL_BYTES
+#define ZS_STATS_TAIL_BYTES (256ll << 20)
 #endif
 #ifndef ZS_STATS_SMALL
 #define ZS_STATS_SMALL 32768
@@ -310,7 +317,7 @@ template <int DT, bool NT>
 struct Stats16Op {
   const uint16_t* g;
   float inv;
-  SumSq ss;
+  SumSq& ss;
   __device__ __forceinline__ void elem(int64_t j) { ss.add(0, dec16<DT>(g[j]) * inv); }
   template <int U>
   __device__ __forceinline__ void groups(int64_t j, int64_t stride) {
@@ -336,6 +343,8 @@ struct StatsArgs {
   int32_t flip;            // 1: the step's first intake (its last block flips sc->cur_slot)
   DevScalars* sc;
   IntakeParts parts;
+  int64_t plain_from;      // NT passes: chunks from this state offset on are read with plain loads
+                           // (the slice's tail, left in the Infinity Cache for the Adam pass)
 };
 
 // The unscale factor of an intake pass: the call's inv, or 1 / the device-resident
@@ -410,12 +419,20 @@ __device__ __forceinline__ void walk_parts(const Chunk* chunks, int64_t n_chunks
 
 template <int DT, bool NT>
 __global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
-  Stats16Op<DT, NT> op{nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc), SumSq{}};
+  SumSq ss;
+  Stats16Op<DT, NT> op{nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc), ss};
+  Stats16Op<DT, false> op_plain{nullptr, op.inv, ss};
   walk_chunks(a.chunks, a.n_chunks, a.cpb, [&](const ChunkRef ch) {
-    op.g = a.flat_g ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
-    run_chunk<ZS_STATS_U, 4>(op, ch.len, head16(op.g), true);
+    const uint16_t* g = a.flat_g ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
+    if (NT && ch.state_off >= a.plain_from) {
+      op_plain.g = g;
+      run_chunk<ZS_STATS_U, 4>(op_plain, ch.len, head16(g), true);
+    } else {
+      op.g = g;
+      run_chunk<ZS_STATS_U, 4>(op, ch.len, head16(g), true);
+    }
   });
-  finish_stats(op.ss.total(), a.sc, a.parts, a.flip);
+  finish_stats(ss.total(), a.sc, a.parts, a.flip);
 }
 
 // ---------------------------------------------------------------------------
@@ -767,6 +784,7 @@ struct AdamArgs {
   float growth, backoff, min_scale;
   int32_t interval;
   SegArgs seg;             // segment completion flags (seg.seg null: none)
+  int32_t reverse;         // walk the work items from the last (the cached tail of the gradient first)
 };
 
 // ---------------------------------------------------------------------------
@@ -909,7 +927,8 @@ __global__ void __launch_bounds__(ZS_ADAM_BLOCK) adam_kernel(AdamArgs a) {
   // Work item i is part i % kSplit of chunk i / kSplit: one short-lived block per part,
   // scheduled by the hardware dispatcher (measured faster than a persistent grid here).
   const int64_t n_items = a.n_chunks * kSplit;
-  for (int64_t i = blockIdx.x; i < n_items; i += gridDim.x) {
+  for (int64_t i0 = blockIdx.x; i0 < n_items; i0 += gridDim.x) {
+    const int64_t i = a.reverse ? n_items - 1 - i0 : i0;
     const Chunk ch = a.chunks[i / kSplit];
     const Part p = chunk_part(ch.len, i % kSplit, kSplit);
     if (p.lo < ch.len) {
@@ -1035,6 +1054,12 @@ static unsigned intake_grid(int64_t n_chunks, int32_t cpb) {
   return clamp_grid((n_chunks + cpb - 1) / cpb, n_chunks);
 }
 
+// Whether the statistics pass over a 16-bit slice of slice_elems elements reads its tail with
+// plain loads (a slice too large for the Infinity Cache, read non-temporally otherwise).
+static bool stats_tail_cached(int64_t slice_elems) {
+  return 2 * slice_elems > (int64_t)ZS_STATS_NT_BYTES && ZS_STATS_TAIL_BYTES > 0;
+}
+
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, int64_t slice_elems,
                           const uint16_t* flat_g, float inv, bool dyn, bool flip, DevScalars* sc,
                           const IntakeParts& parts, hipStream_t st) {
@@ -1043,9 +1068,10 @@ hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, int6
     return hipGetLastError();
   }
   const int32_t cpb = n_chunks < ZS_STATS_SMALL ? ZS_STATS_SMALL_CPB : 1;
-  StatsArgs a{chunks, n_chunks, flat_g, inv, (int32_t)dyn, cpb, (int32_t)flip, sc, parts};
-  const unsigned g = intake_grid(n_chunks, cpb);
   const bool nt = 2 * slice_elems > (int64_t)ZS_STATS_NT_BYTES;
+  const int64_t plain_from = stats_tail_cached(slice_elems) ? slice_elems - (int64_t)ZS_STATS_TAIL_BYTES / 2 : INT64_MAX;
+  StatsArgs a{chunks, n_chunks, flat_g, inv, (int32_t)dyn, cpb, (int32_t)flip, sc, parts, plain_from};
+  const unsigned g = intake_grid(n_chunks, cpb);
   if (dtype == ZERO_BF16) {
     if (nt) hipLaunchKernelGGL((stats16_kernel<ZERO_BF16, true>), dim3(g), dim3(kBlock), 0, st, a);
     else hipLaunchKernelGGL((stats16_kernel<ZERO_BF16, false>), dim3(g), dim3(kBlock), 0, st, a);
@@ -1267,9 +1293,9 @@ hipError_t launch_adam(int dtype, int grad_source, bool cast, const AdamArgs& a,
 }
 
 hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* chunks, int64_t n_chunks,
-                            const uint16_t* flat_g, const float* red, float* master, float* m, float* v,
-                            DevScalars* sc, int32_t other_flag, double other_sumsq, bool sumsq_global, float max_norm,
-                            float inv, const zero_adam_hparams_t* hp, const zero_loss_scaler_t* dyn,
+                            int64_t slice_elems, const uint16_t* flat_g, const float* red, float* master, float* m,
+                            float* v, DevScalars* sc, int32_t other_flag, double other_sumsq, bool sumsq_global,
+                            float max_norm, float inv, const zero_adam_hparams_t* hp, const zero_loss_scaler_t* dyn,
                             const SegArgs* seg, int64_t grid_cap, hipStream_t st) {
   AdamArgs a;
   a.chunks = chunks;
@@ -1296,6 +1322,10 @@ hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* 
   a.min_scale = dyn ? dyn->min_scale : 1.0f;
   a.interval = dyn ? dyn->growth_interval : 1;
   a.seg = seg ? *seg : SegArgs{nullptr, 1, 0, 0, 0};
+  // After a statistics pass that left its slice's tail in the cache, start where it ended --
+  // unless the write-back reports segments, whose consumers wait for them in order.
+  a.reverse = (grad_source == kGradFlat16 || grad_source == kGradChunk16) && stats_tail_cached(slice_elems) &&
+              !(cast && seg);
   return launch_adam(dtype, grad_source, cast, a, grid_cap, st);
 }
 

@@ -576,7 +576,8 @@ zero_status_t zero_adam_step(zero_shard_t h, const zero_adam_hparams_t* hp, int3
   const bool track = h->n_seg > 0 && fuse_cast != 0;
   if (track) ZS_HIP(hipEventRecord(h->wb_event, static_cast<hipStream_t>(stream)));
   hipError_t e = zs::launch_adam_step(h->dtype, h->grad_source, fuse_cast != 0, h->chunks, h->n_chunks,
-                                      h->step_flat_g, h->red, h->master, h->m, h->v, h->sc, h->other_flag,
+                                      h->info.valid_elems, h->step_flat_g, h->red, h->master, h->m, h->v, h->sc,
+                                      h->other_flag,
                                       h->other_sumsq, h->sumsq_global, h->max_norm,
                                       h->inv, hp, h->dynamic ? &h->dyn_cfg : nullptr, h->n_seg ? &seg : nullptr,
                                       h->grid_main, static_cast<hipStream_t>(stream));

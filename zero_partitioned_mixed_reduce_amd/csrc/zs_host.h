@@ -35,8 +35,8 @@ hipError_t launch_export(const Chunk* chunks, int64_t n_chunks, const float* src
                          hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* chunks, int64_t n_chunks,
-                            const uint16_t* flat_g, const float* red, float* master, float* m, float* v,
-                            DevScalars* sc, int32_t other_flag, double other_sumsq, bool sumsq_global, float max_norm,
-                            float inv, const zero_adam_hparams_t* hp, const zero_loss_scaler_t* dyn,
+                            int64_t slice_elems, const uint16_t* flat_g, const float* red, float* master, float* m,
+                            float* v, DevScalars* sc, int32_t other_flag, double other_sumsq, bool sumsq_global,
+                            float max_norm, float inv, const zero_adam_hparams_t* hp, const zero_loss_scaler_t* dyn,
                             const SegArgs* seg, int64_t grid_cap, hipStream_t st);
 }  // namespace zs
