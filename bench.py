@@ -602,6 +602,7 @@ INFINITY_CACHE_BYTES = 256 << 20
 
 
 STATS_TAIL_BYTES = 256 << 20   # a larger slice's tail that the statistics pass leaves in the cache
+REDUCE_TAIL_BYTES = 192 << 20  # the part of the local reduce's output stored to stay in the cache
 
 
 def hbm_side(w, valid, micro_steps, reduce_out16, step_b, adam_b, segments=0):
@@ -610,12 +611,23 @@ def hbm_side(w, valid, micro_steps, reduce_out16, step_b, adam_b, segments=0):
     statistics pass with plain loads and re-read by the Adam pass from the cache, so the
     second read does not reach HBM.  Of a larger slice the statistics pass reads the last
     256 MiB with plain loads and the Adam pass (walking from the end, unless the write-back
-    tracks segments) re-reads those from the cache.  Returns (step, adam, note)."""
+    tracks segments) re-reads those from the cache.  Likewise the local reduce stores the
+    last 192 MiB of its output (all of it if smaller) with plain stores, and the Adam pass
+    reads them from the cache.  Returns (step, adam, note)."""
     slice_bytes = 2 * valid
     fabric = "HBM-side bytes equal the fabric count"
-    if w.grad_mode == "reduce" or micro_steps > 1 or valid == 0:
-        return step_b, adam_b, "no re-read of a 16-bit gradient slice in this step: " + fabric
     unseen = "(no hardware counter separates the two on gfx950)"
+    if micro_steps > 1 or valid == 0:
+        return step_b, adam_b, "the step's re-reads are not counted apart with micro-steps: " + fabric
+    if w.grad_mode == "reduce":
+        out_bytes = (2 if reduce_out16 else 4) * valid
+        if out_bytes > REDUCE_TAIL_BYTES and segments:
+            return step_b, adam_b, ("with tracked segments the Adam pass walks forward and re-reads no cached part of "
+                                    "the reduce output: " + fabric)
+        d = min(out_bytes, REDUCE_TAIL_BYTES) / valid
+        return step_b - d, adam_b - d, (f"{min(out_bytes, REDUCE_TAIL_BYTES) / 2**20:.0f} MiB of the local reduce's "
+                                        f"{out_bytes / 1e6:.0f} MB output stay in the Infinity Cache for the Adam pass: "
+                                        f"HBM moves {d:.4f} B/param less than the fabric count " + unseen)
     if slice_bytes <= INFINITY_CACHE_BYTES:
         return step_b - 2, adam_b - 2, (f"the {slice_bytes / 1e6:.0f} MB gradient slice fits in the 256 MiB Infinity "
                                         "Cache: the Adam pass re-reads it from there, so HBM moves 2 B/param less "

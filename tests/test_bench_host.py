@@ -85,8 +85,8 @@ def test_hbm_side_bytes():
     234 MB), the Adam pass's re-read is not counted as HBM traffic: 28 B/param for the step and
     26 for the Adam pass, against the fabric counts 30 and 28.  Of a larger slice (the GPT-2
     shard's 389 MB, the full state) only the 256 MiB tail left in the cache is taken off, and
-    nothing with tracked segments (the Adam pass then walks forward).  The local reduce and
-    micro-steps keep the fabric count."""
+    nothing with tracked segments (the Adam pass then walks forward).  The same holds for the
+    last 192 MiB of the local reduce's output.  Micro-steps keep the fabric count."""
     approx = pytest.approx
     assert bench.hbm_side(recipes.zero1_7p5b(), 117_187_520, 1, False, 30, 28)[:2] == (28, 26)
     tail = 256 * 2**20
@@ -95,7 +95,14 @@ def test_hbm_side_bytes():
     assert bench.hbm_side(recipes.gpt2_shard(), 194_409_856, 1, False, 30, 28)[:2] == approx(
         (30 - tail / 194_409_856, 28 - tail / 194_409_856))
     assert bench.hbm_side(recipes.gpt2_shard(), 194_409_856, 1, False, 30, 28, segments=64)[:2] == (30, 28)
-    assert bench.hbm_side(recipes.reduce8(), 187_500_032, 1, False, 50, 30)[:2] == (50, 30)
+    # the local reduce's output: its last 192 MiB are re-read from the cache (all of a smaller output)
+    rtail = 192 * 2**20
+    assert bench.hbm_side(recipes.reduce8(), 187_500_032, 1, False, 50, 30)[:2] == approx(
+        (50 - rtail / 187_500_032, 30 - rtail / 187_500_032))
+    assert bench.hbm_side(recipes.reduce8(), 187_500_032, 1, True, 46, 28)[:2] == approx(
+        (46 - rtail / 187_500_032, 28 - rtail / 187_500_032))
+    assert bench.hbm_side(recipes.reduce8(), 187_500_032, 1, False, 50, 30, segments=8)[:2] == (50, 30)
+    assert bench.hbm_side(recipes.tiny(), 262_144, 1, False, 42, 30)[:2] == (38, 26)
     # with micro-steps the accumulator is re-read instead: no adjustment
     assert bench.hbm_side(recipes.zero1_7p5b(), 117_187_520, 2, False, 44, 32)[:2] == (44, 32)
 

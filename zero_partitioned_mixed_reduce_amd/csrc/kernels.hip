@@ -30,6 +30,11 @@
 //                      they stay in the Infinity Cache; the Adam pass then walks the shard from
 //                      its end and re-reads them from there (256 MiB measured 3.8% faster on
 //                      the 389 MB GPT-2 slice than none, 240 and 320 MiB in between)
+//   ZS_REDUCE_TAIL_BYTES  the local reduce stores the last this many bytes of its output (all of
+//                      it if smaller) with plain stores, which stay in the Infinity Cache for
+//                      the Adam pass, the rest non-temporally (128-192 MiB measured 2.7% faster
+//                      with the 16-bit output of the 8-way reduce, 0.6% with fp32 u; the plain
+//                      stores slow the reduce pass itself, so more is not better)
 //   ZS_STATS_SMALL  a statistics pass over fewer chunks than this takes ZS_STATS_SMALL_CPB
 //                   consecutive chunks per block (else one); the reduce passes take one
 //   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
@@ -54,6 +59,9 @@
 #endif
 #ifndef ZS_STATS_TAIL_BYTES
 #define ZS_STATS_TAIL_BYTES (256ll << 20)
+#endif
+#ifndef ZS_REDUCE_TAIL_BYTES
+#define ZS_REDUCE_TAIL_BYTES (192ll << 20)
 #endif
 #ifndef ZS_STATS_SMALL
 #define ZS_STATS_SMALL 32768
@@ -158,6 +166,7 @@ __device__ __forceinline__ u32x2 ld16x4_src(const uint16_t* p) {
   return *reinterpret_cast<const u32x2*>(p);
 #endif
 }
+__device__ __forceinline__ void st16x4(uint16_t* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 __device__ __forceinline__ void st16x4_nt(uint16_t* p, u32x2 v) {
 #if ZS_NT_STORE
   __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
@@ -183,6 +192,7 @@ __device__ __forceinline__ f32x4 ld32x4_nt(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
 #endif
 }
+__device__ __forceinline__ void st32x4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 __device__ __forceinline__ void st32x4_nt(float* p, f32x4 v) {
 #if ZS_NT_STORE
   __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
@@ -450,6 +460,7 @@ struct ReduceArgs {
   int32_t flip;            // as in StatsArgs
   DevScalars* sc;
   IntakeParts parts;
+  int64_t keep_from;       // outputs from this state offset on are stored with plain stores
 };
 
 // Gradient sources of the intake passes.  NR > 0: that many rank buffers
@@ -527,6 +538,7 @@ struct ReduceOp {
   float* red;
   float inv;
   SumSq ss;
+  int32_t keep;  // plain stores: the output stays in the Infinity Cache
   __device__ __forceinline__ void elem(int64_t j) {
     float r;
     if constexpr (NR == kSrcNone) r = red[j];
@@ -558,7 +570,10 @@ struct ReduceOp {
       const f32x4 u = s[k] * inv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) ss.add(k, u[e]);
-      if constexpr (STORE) st32x4_nt(red + j + k * stride, u);
+      if constexpr (STORE) {
+        if (keep) st32x4(red + j + k * stride, u);
+        else st32x4_nt(red + j + k * stride, u);
+      }
     }
   }
 };
@@ -566,8 +581,9 @@ struct ReduceOp {
 template <int DT, int NR, bool ACC, bool R16 = false, bool STORE = true>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(ReduceArgs a) {
   ReduceOp<DT, NR, ACC, R16, STORE> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc),
-                                SumSq{}};
+                                SumSq{}, 0};
   walk_parts(a.chunks, a.n_chunks, a.ppc, [&](const ChunkRef ch) {
+    op.keep = ch.state_off >= a.keep_from;
     op.gs.flat_off = ch.flat_off;
     op.gs.src0 = reinterpret_cast<const uint16_t*>(ch.g16);
     op.red = a.red + ch.state_off;
@@ -586,6 +602,7 @@ struct Reduce16Op {
   uint16_t* red16;
   float inv;
   SumSq ss;
+  int32_t keep;  // plain stores: the output stays in the Infinity Cache
   __device__ __forceinline__ void elem(int64_t j) {
     const uint32_t h = enc16<DT>(gs.one(j));
     red16[j] = (uint16_t)h;
@@ -598,7 +615,8 @@ struct Reduce16Op {
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const u32x2 h = enc16x4<DT>(s[k]);
-      st16x4_nt(red16 + j + k * stride, h);
+      if (keep) st16x4(red16 + j + k * stride, h);
+      else st16x4_nt(red16 + j + k * stride, h);
       const f32x4 u = dec16x4<DT>(h) * inv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) ss.add(k, u[e]);
@@ -608,8 +626,10 @@ struct Reduce16Op {
 
 template <int DT, int NR>
 __global__ void __launch_bounds__(kBlock) reduce16_kernel(ReduceArgs a) {
-  Reduce16Op<DT, NR> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc), SumSq{}};
+  Reduce16Op<DT, NR> op{GradSum<DT, NR>{&a, nullptr, 0}, nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc), SumSq{},
+                        0};
   walk_parts(a.chunks, a.n_chunks, a.ppc, [&](const ChunkRef ch) {
+    op.keep = ch.state_off >= a.keep_from;
     op.gs.flat_off = ch.flat_off;
     op.red16 = reinterpret_cast<uint16_t*>(a.red) + ch.state_off;
     const int head = head16(op.gs.src(0));
@@ -1060,6 +1080,20 @@ static bool stats_tail_cached(int64_t slice_elems) {
   return 2 * slice_elems > (int64_t)ZS_STATS_NT_BYTES && ZS_STATS_TAIL_BYTES > 0;
 }
 
+// The local reduce stores its output of `bytes` per element with plain stores from this
+// state offset on (the last ZS_REDUCE_TAIL_BYTES of it, or all of it when it fits), so
+// that part stays in the Infinity Cache for the Adam pass.
+static int64_t reduce_keep_from(int64_t slice_elems, int bytes) {
+  if (ZS_REDUCE_TAIL_BYTES <= 0) return INT64_MAX;
+  const int64_t keep = (int64_t)ZS_REDUCE_TAIL_BYTES / bytes;
+  return slice_elems > keep ? slice_elems - keep : 0;
+}
+// Whether only a tail of that output is cached (so the Adam pass should start at the end).
+static bool reduce_tail_cached(int64_t slice_elems, int bytes) {
+  const int64_t from = reduce_keep_from(slice_elems, bytes);
+  return from > 0 && from != INT64_MAX;
+}
+
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, int64_t slice_elems,
                           const uint16_t* flat_g, float inv, bool dyn, bool flip, DevScalars* sc,
                           const IntakeParts& parts, hipStream_t st) {
@@ -1172,6 +1206,7 @@ static ReduceArgs make_reduce_args(const Chunk* chunks, int64_t n_chunks, const 
   a.flip = flip;
   a.sc = sc;
   a.parts = parts;
+  a.keep_from = INT64_MAX;
   return a;
 }
 
@@ -1192,7 +1227,7 @@ static int src_code(int32_t n_ranks) {
 // per element), and u is taken from it; with accumulation the rounded sum is added.
 // keep_acc (with accumulation from one source or none, n_ranks 0, 1 or < 0):
 // statistics only, red keeps the accumulator.
-hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
+hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, int64_t slice_elems, const void* const* ranks,
                          int32_t n_ranks, bool accumulate, bool r16, bool keep_acc, float inv, bool dyn, bool flip,
                          float* red, DevScalars* sc, const IntakeParts& parts, hipStream_t st) {
   if (n_chunks == 0) {
@@ -1204,6 +1239,7 @@ hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const
   // Parts of a chunk pay off where a block reads several rank slices; over one
   // 16-bit source (and the accumulator) whole chunks per block measured faster.
   a.ppc = is_rank_reduce(src) ? kIntakeParts : 1;
+  a.keep_from = reduce_keep_from(slice_elems, r16 && !accumulate && is_rank_reduce(src) ? 2 : 4);
   const unsigned g = clamp_grid(n_chunks * a.ppc, n_chunks * a.ppc);
   if (keep_acc) {
     if (!accumulate || !(src == 1 || src == kSrcChunk || src == kSrcNone)) return hipErrorInvalidValue;
@@ -1322,10 +1358,13 @@ hipError_t launch_adam_step(int dtype, int grad_source, bool cast, const Chunk* 
   a.min_scale = dyn ? dyn->min_scale : 1.0f;
   a.interval = dyn ? dyn->growth_interval : 1;
   a.seg = seg ? *seg : SegArgs{nullptr, 1, 0, 0, 0};
-  // After a statistics pass that left its slice's tail in the cache, start where it ended --
-  // unless the write-back reports segments, whose consumers wait for them in order.
-  a.reverse = (grad_source == kGradFlat16 || grad_source == kGradChunk16) && stats_tail_cached(slice_elems) &&
-              !(cast && seg);
+  // After an intake that left the tail of the Adam pass's gradient source in the cache, start
+  // where it ended -- unless the write-back reports segments, whose consumers wait in order.
+  const bool tail = (grad_source == kGradFlat16 || grad_source == kGradChunk16) ? stats_tail_cached(slice_elems)
+                    : grad_source == kGradRed                                    ? reduce_tail_cached(slice_elems, 4)
+                    : grad_source == kGradRed16                                  ? reduce_tail_cached(slice_elems, 2)
+                                                                                 : false;
+  a.reverse = tail && !(cast && seg);
   return launch_adam(dtype, grad_source, cast, a, grid_cap, st);
 }
 

@@ -440,7 +440,7 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
       if (s != ZERO_OK) return s;
     }
     const bool keep_acc = n_ranks == 0 || n_ranks == 1 || n_ranks == ZERO_ACCUMULATED;
-    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, true, h->reduce_out16, keep_acc,
+    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, h->info.valid_elems, rank_grads, n_ranks, true, h->reduce_out16, keep_acc,
                           inv_loss_scale, dyn, flip, h->red, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
     h->grad_source = !keep_acc ? kGradRed : n_ranks == 0 ? kGradAccChunk16 : n_ranks == 1 ? kGradAccFlat16 : kGradAcc;
@@ -467,7 +467,7 @@ zero_status_t zero_reduce_grads(zero_shard_t h, const void* const* rank_grads, i
     zero_status_t sc = check_sources(h, rank_grads, n_ranks);  // n_ranks < -1 or >= 2 here
     if (sc != ZERO_OK) return sc;
     if (!h->red) return fail(ZERO_EINVAL, "reducing N_d >= 2 buffers needs bufs.red");
-    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, rank_grads, n_ranks, false, h->reduce_out16, false,
+    e = zs::launch_reduce(h->dtype, h->chunks, h->n_chunks, h->info.valid_elems, rank_grads, n_ranks, false, h->reduce_out16, false,
                           inv_loss_scale, dyn, flip, h->red, h->sc, h->parts, st);
     if (e != hipSuccess) return hip_fail("reduce kernel", e);
     h->grad_source = h->reduce_out16 ? kGradRed16 : kGradRed;

@@ -19,7 +19,7 @@ namespace zs {
 hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, int64_t slice_elems,
                           const uint16_t* flat_g, float inv, bool dyn, bool flip, DevScalars* sc,
                           const IntakeParts& parts, hipStream_t st);
-hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
+hipError_t launch_reduce(int dtype, const Chunk* chunks, int64_t n_chunks, int64_t slice_elems, const void* const* ranks,
                          int32_t n_ranks, bool accumulate, bool r16, bool keep_acc, float inv, bool dyn, bool flip,
                          float* red, DevScalars* sc, const IntakeParts& parts, hipStream_t st);
 hipError_t launch_accumulate(int dtype, const Chunk* chunks, int64_t n_chunks, const void* const* ranks,
