@@ -29,7 +29,8 @@
 //   ZS_STATS_TAIL_BYTES  ... except for its last ZS_STATS_TAIL_BYTES, read with plain loads so
 //                      they stay in the Infinity Cache; the Adam pass then walks the shard from
 //                      its end and re-reads them from there (256 MiB measured 3.8% faster on
-//                      the 389 MB GPT-2 slice than none, 240 and 320 MiB in between)
+//                      the 389 MB GPT-2 slice than none, 240 and 320 MiB in between); not for
+//                      slices beyond 16 times this, where the gain is within the noise
 //   ZS_REDUCE_TAIL_BYTES  the local reduce stores the last this many bytes of its output (all of
 //                      it if smaller) with plain stores, which stay in the Infinity Cache for
 //                      the Adam pass, the rest non-temporally (128-192 MiB measured 2.7% faster
@@ -427,14 +428,15 @@ __device__ __forceinline__ void walk_parts(const Chunk* chunks, int64_t n_chunks
   body(ch);
 }
 
-template <int DT, bool NT>
+// TAIL (with NT): chunks from a.plain_from on are read with plain loads.
+template <int DT, bool NT, bool TAIL>
 __global__ void __launch_bounds__(kBlock) stats16_kernel(StatsArgs a) {
   SumSq ss;
   Stats16Op<DT, NT> op{nullptr, intake_inv(a.inv, a.dyn, a.flip, a.sc), ss};
   Stats16Op<DT, false> op_plain{nullptr, op.inv, ss};
   walk_chunks(a.chunks, a.n_chunks, a.cpb, [&](const ChunkRef ch) {
     const uint16_t* g = a.flat_g ? a.flat_g + ch.flat_off : reinterpret_cast<const uint16_t*>(ch.g16);
-    if (NT && ch.state_off >= a.plain_from) {
+    if (TAIL && ch.state_off >= a.plain_from) {
       op_plain.g = g;
       run_chunk<ZS_STATS_U, 4>(op_plain, ch.len, head16(g), true);
     } else {
@@ -1075,9 +1077,12 @@ static unsigned intake_grid(int64_t n_chunks, int32_t cpb) {
 }
 
 // Whether the statistics pass over a 16-bit slice of slice_elems elements reads its tail with
-// plain loads (a slice too large for the Infinity Cache, read non-temporally otherwise).
+// plain loads: a slice too large for the Infinity Cache (read non-temporally otherwise) but
+// not so large that the tail's share of the re-read is negligible (beyond 16 times the tail
+// the statistics kernel's extra load path costs about what the tail saves).
 static bool stats_tail_cached(int64_t slice_elems) {
-  return 2 * slice_elems > (int64_t)ZS_STATS_NT_BYTES && ZS_STATS_TAIL_BYTES > 0;
+  return 2 * slice_elems > (int64_t)ZS_STATS_NT_BYTES && ZS_STATS_TAIL_BYTES > 0 &&
+         2 * slice_elems <= 16 * (int64_t)ZS_STATS_TAIL_BYTES;
 }
 
 // The local reduce stores its output of `bytes` per element with plain stores from this
@@ -1103,15 +1108,18 @@ hipError_t launch_stats16(int dtype, const Chunk* chunks, int64_t n_chunks, int6
   }
   const int32_t cpb = n_chunks < ZS_STATS_SMALL ? ZS_STATS_SMALL_CPB : 1;
   const bool nt = 2 * slice_elems > (int64_t)ZS_STATS_NT_BYTES;
-  const int64_t plain_from = stats_tail_cached(slice_elems) ? slice_elems - (int64_t)ZS_STATS_TAIL_BYTES / 2 : INT64_MAX;
+  const bool tail = stats_tail_cached(slice_elems);
+  const int64_t plain_from = tail ? slice_elems - (int64_t)ZS_STATS_TAIL_BYTES / 2 : INT64_MAX;
   StatsArgs a{chunks, n_chunks, flat_g, inv, (int32_t)dyn, cpb, (int32_t)flip, sc, parts, plain_from};
   const unsigned g = intake_grid(n_chunks, cpb);
   if (dtype == ZERO_BF16) {
-    if (nt) hipLaunchKernelGGL((stats16_kernel<ZERO_BF16, true>), dim3(g), dim3(kBlock), 0, st, a);
-    else hipLaunchKernelGGL((stats16_kernel<ZERO_BF16, false>), dim3(g), dim3(kBlock), 0, st, a);
+    if (tail) hipLaunchKernelGGL((stats16_kernel<ZERO_BF16, true, true>), dim3(g), dim3(kBlock), 0, st, a);
+    else if (nt) hipLaunchKernelGGL((stats16_kernel<ZERO_BF16, true, false>), dim3(g), dim3(kBlock), 0, st, a);
+    else hipLaunchKernelGGL((stats16_kernel<ZERO_BF16, false, false>), dim3(g), dim3(kBlock), 0, st, a);
   } else {
-    if (nt) hipLaunchKernelGGL((stats16_kernel<ZERO_F16, true>), dim3(g), dim3(kBlock), 0, st, a);
-    else hipLaunchKernelGGL((stats16_kernel<ZERO_F16, false>), dim3(g), dim3(kBlock), 0, st, a);
+    if (tail) hipLaunchKernelGGL((stats16_kernel<ZERO_F16, true, true>), dim3(g), dim3(kBlock), 0, st, a);
+    else if (nt) hipLaunchKernelGGL((stats16_kernel<ZERO_F16, true, false>), dim3(g), dim3(kBlock), 0, st, a);
+    else hipLaunchKernelGGL((stats16_kernel<ZERO_F16, false, false>), dim3(g), dim3(kBlock), 0, st, a);
   }
   return hipGetLastError();
 }
