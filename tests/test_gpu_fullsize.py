@@ -118,16 +118,22 @@ def gpu_params_at(wl, flat_idx):
     return out
 
 
-@pytest.mark.parametrize("cfg,rank,micro,r16", [
-    ("zero1_7p5b", 0, 1, False), ("zero1_7p5b", 63, 1, False), ("gpt2", 7, 1, False), ("gpt2", 3, 1, False),
-    ("reduce8", 7, 1, False), ("reduce8", 0, 1, False), ("full7p5b", 0, 1, False),
-    ("reduce8", 7, 3, False), ("zero1_7p5b", 0, 2, False), ("reduce8", 7, 1, True), ("reduce8", 0, 2, True),
-    ("big_tensor", 0, 1, False)])
-def test_full_size_sampled(cfg, rank, micro, r16):
+@pytest.mark.parametrize("cfg,rank,micro,r16,seg", [
+    ("zero1_7p5b", 0, 1, False, 0), ("zero1_7p5b", 63, 1, False, 0), ("gpt2", 7, 1, False, 0),
+    ("gpt2", 3, 1, False, 0), ("reduce8", 7, 1, False, 0), ("reduce8", 0, 1, False, 0), ("full7p5b", 0, 1, False, 0),
+    ("reduce8", 7, 3, False, 0), ("zero1_7p5b", 0, 2, False, 0), ("reduce8", 7, 1, True, 0), ("reduce8", 0, 2, True, 0),
+    ("big_tensor", 0, 1, False, 0),
+    # tracked segments: the Adam pass walks forward past the intake's cached tail
+    ("gpt2", 7, 1, False, 16), ("reduce8", 7, 1, True, 16)])
+def test_full_size_sampled(cfg, rank, micro, r16, seg):
+    """The shard's slices beyond the 256 MiB Infinity Cache (GPT-2, the local reduce's output)
+    take the paths where the intake leaves a tail in the cache and the Adam pass starts at the
+    end (or, with tracked segments, walks forward)."""
     import bench
     w = recipes.ALL[cfg]() if cfg in recipes.ALL else getattr(recipes, cfg)()
-    print(f"\n[fullsize] {cfg} rank {rank} micro-steps {micro} 16-bit reduce output {r16}: setting up", flush=True)
-    wl = bench.Workload(w, rank, micro, reduce_out16=r16)
+    print(f"\n[fullsize] {cfg} rank {rank} micro-steps {micro} 16-bit reduce output {r16} segments {seg}: setting up",
+          flush=True)
+    wl = bench.Workload(w, rank, micro, reduce_out16=r16, segments=seg)
     info = wl.info
     b, valid = info.shard_begin, info.valid_elems
     pieces = wl.shard.pieces()
@@ -136,6 +142,8 @@ def test_full_size_sampled(cfg, rank, micro, r16):
     torch.cuda.synchronize()
     q = wl.shard.query()
     assert q["t"] == 2 and not q["skipped"]
+    if seg:
+        assert wl.shard.zero_segment_timeouts() == 0
 
     print(f"[fullsize] {cfg}: oracle sum of squares over {valid} elements", flush=True)
     flag, local = oracle_local_sumsq(w, b, valid, wl.inv, micro, r16)
