@@ -100,6 +100,41 @@ def test_static_workspace_matches_caller_workspace_twice():
     s2.close()
 
 
+def test_static_workspace_at_its_largest_shard():
+    """The largest flat shard whose workspace fits the static array (about 8.2e8 elements at
+    N_d = 1, so its 16-bit slice is larger than the Infinity Cache and the statistics pass
+    leaves a cached tail for an Adam pass that walks from the end): two steps on the static
+    handle and on a caller-workspace handle, compared bit for bit on the device."""
+    from zero_partitioned_mixed_reduce_amd.shard import make_desc
+    probe = torch.empty(1, dtype=torch.int16, device="cuda")
+    lo, hi = 1 << 20, 1 << 31                                  # the plan's workspace grows with psi
+    while hi - lo > 8192:
+        mid = (lo + hi) // 2
+        fits = _abi.zero_shard_plan(make_desc([mid], 1, 0, _abi.ZERO_BF16, probe)).workspace_bytes
+        lo, hi = (mid, hi) if fits <= _abi.ZERO_STATIC_WORKSPACE_BYTES else (lo, mid)
+    psi = lo
+    w = recipes.tiny()
+    print(f"[no-alloc] largest static shard: flat bf16 psi {psi} N_d 1", flush=True)
+    p16 = torch.empty(psi, dtype=torch.int16, device="cuda")
+    synth.gpu_normal_16(p16, _abi.ZERO_BF16, w.seed, synth.stream_id(synth.MASTER), 0, w.master_sigma)
+    pa, pb = p16.clone(), p16
+    a = ZeroShard([psi], 1, 0, _abi.ZERO_BF16, pa)
+    s = ZeroShard([psi], 1, 0, _abi.ZERO_BF16, pb, static_workspace=True)
+    assert a.info.workspace_bytes <= _abi.ZERO_STATIC_WORKSPACE_BYTES and 2 * psi > 256 << 20
+    g = torch.empty(psi, dtype=torch.int16, device="cuda")
+    hp = (1e-3, 0.9, 0.999, 1e-8, 0.01)
+    for step in range(1, 3):
+        synth.gpu_normal_16(g, _abi.ZERO_BF16, w.seed, synth.stream_id(synth.GRAD, 0, step), 0, 1e-4)
+        step_both((a, s), [g], 1.0, 0.0, 1.0, hp)
+        for name in ("master", "m", "v"):
+            assert torch.equal(a.export(name).view(torch.int32), s.export(name).view(torch.int32)), (step, name)
+        assert torch.equal(pa, pb), (step, "16-bit parameters")
+        qa, qs = a.query(), s.query()
+        assert qa == qs and not qa["skipped"] and qa["t"] == step and qa["clip"] < 1.0, (qa, qs)
+    a.close()
+    s.close()
+
+
 def test_static_workspace_size_limit():
     """A shard whose workspace exceeds the static array is refused before any device work
     (and a caller workspace passed to the static call is refused too)."""
