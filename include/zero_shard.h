@@ -188,7 +188,10 @@ zero_status_t zero_shard_init_static(const zero_shard_desc_t* desc, const zero_s
  * complete on the device as soon as its last element is written, and a consumer
  * stream can wait for one segment and then start that segment's all-gather
  * while later segments are still being updated.  A skipped step marks every
- * segment complete at once (nothing is written). */
+ * segment complete at once (nothing is written).  While segments are tracked
+ * the fused write-back walks the shard from its first segment, so segments
+ * complete roughly in order (without them the Adam pass may start at the end
+ * of a large shard, where the intake left part of its input in the cache). */
 
 /* Splits the write-back into min(n_segments, num_chunks) segments of equal
  * chunk counts (0 turns tracking off; the default).  Between steps only
