@@ -327,3 +327,28 @@ def test_offload_others_norm_mode_on_exact_sums():
         assert not any(x["skipped"] for x in res) and res[0]["clip"] < 1.0
         sim.compare()
     sim.close()
+
+
+def test_offload_random_configurations():
+    """Random small descriptions (1-5 ragged tensors, N_d 1-9, either dtype, a thread count
+    per rank, clipping on or off), two steps each, against the oracle bit for bit."""
+    from hypothesis import HealthCheck, given, settings, strategies as st
+
+    @settings(max_examples=40, deadline=None, derandomize=True,
+              suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+    @given(numel=st.lists(st.integers(0, 40000), min_size=1, max_size=5), nd=st.integers(1, 9),
+           bf16=st.booleans(), threads=st.lists(st.integers(0, 4), min_size=1, max_size=3),
+           clip_on=st.booleans())
+    def run(numel, nd, bf16, threads, clip_on):
+        dtype = BF16 if bf16 else F16
+        seed = 0x5EED0900 + nd + len(numel)
+        sim = HostSim(numel, nd, dtype, seed, threads=tuple(threads))
+        scale = 1.0 if bf16 else 1024.0
+        sigma = (0.5 if clip_on else 1e-4) * scale
+        for step in (1, 2):
+            res = sim.step(grads(sim.psi, dtype, seed, step, sigma), 1.0 / scale, 1.0)
+            assert not any(x["skipped"] for x in res)
+            sim.compare()
+        sim.close()
+
+    run()
