@@ -188,6 +188,30 @@ def test_degenerate_hyperparameters(hp):
                     master[b:b + valid].view(np.uint32)).all()
 
 
+def test_eps_zero_with_exact_zero_gradients():
+    """eps = 0 where the reduced gradient is exactly zero: m = v = 0 there, so the update is
+    0/0 = NaN, the master turns NaN and the 16-bit write-back takes the canonical NaN, on the
+    GPU as in the oracle (elsewhere the step is ordinary)."""
+    w = recipes.tiny()
+    psi = 100_003
+    master, p16 = master_of(w, psi)
+    sim = Sim([psi], w.nd, w.dtype, p16, master, "reduce")
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=0.0, weight_decay=0.01)
+    zeros = np.arange(5, psi, 97)
+    for step in range(1, 3):
+        g = grads_for(w, step, psi, w.nd)
+        for x in g:
+            x[zeros] = 0                                   # +0.0 in every rank: an exact zero sum
+        sim.step(g, 1.0 / w.loss_scale, w.max_norm, hp_of(hp))
+        sim.compare()
+    for r in sim.ranks:
+        _, _, b, valid = sim.plans[r]
+        got = sim.shards[r].export("master").cpu().numpy()
+        mine = zeros[(zeros >= b) & (zeros < b + valid)] - b
+        # (other elements whose four fp16 terms cancel exactly are NaN too, on both sides)
+        assert np.isnan(got[mine]).all() and (np.isnan(got) == np.isnan(sim.ostates[r].w)).all()
+
+
 @pytest.mark.parametrize("cap", ["1", "3"])
 def test_capped_grid(cap, monkeypatch):
     """ZERO_SHARD_BLOCKS_PER_CU caps the streaming grids (init, accumulation, Adam, cast,
