@@ -683,7 +683,10 @@ def probe_ceiling(wl, adam_gbps, stats_gbps):
     p16 = flat16(wl.params)
     out = {"unit": "GB/s", "elements": n,
            "buffers": "the benchmark's own fp32 state arrays and the shard's 16-bit slices (ragged tensor lists: a "
-                      "flat 16-bit stand-in of the slice's size), after the timed steps"}
+                      "flat 16-bit stand-in of the slice's size), after the timed steps",
+           "note": "each probe streams all its bytes through memory: an Adam pass that starts on the part of its "
+                   "gradient input the intake left in the Infinity Cache (a slice between 256 MiB and 4 GiB, or "
+                   "a local reduce's output) can run above its probe"}
     reduce_mode = w.grad_mode == "reduce"
     if reduce_mode:
         g, g32, mix_b = sh.red.data_ptr(), True, 30             # the Adam pass reads fp32 u after a local reduce
