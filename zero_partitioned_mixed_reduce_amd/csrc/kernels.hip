@@ -47,7 +47,8 @@
 //   ZS_ADAM_SPLIT    parts per chunk in the Adam pass (one block per part)
 //   ZS_ADAM_SPLIT_RED  the same when the gradient is the fp32 u of a local reduce (30 B per
 //                      element): 1024-element parts measured 3.5% faster there, and slower
-//                      for the 16-bit gradient sources
+//                      for the 16-bit gradient sources (re-measured later: 3.7% faster on one
+//                      box, 1.1% slower on another)
 //   ZS_ADAM_BLOCK    threads per block of the Adam pass
 #ifndef ZS_ADAM_U
 #define ZS_ADAM_U 2
