@@ -37,7 +37,8 @@
 //                      with the 16-bit output of the 8-way reduce, 0.6% with fp32 u; the plain
 //                      stores slow the reduce pass itself, so more is not better)
 //   ZS_STATS_SMALL  a statistics pass over fewer chunks than this takes ZS_STATS_SMALL_CPB
-//                   consecutive chunks per block (else one); the reduce passes take one
+//                   consecutive chunks per block (else one); the reduce passes take one chunk,
+//                   or one part of it (ZS_REDUCE_PARTS, over several rank slices)
 //   ZS_REDUCE_U quads per lane in flight in the local-reduce pass
 //   ZS_REDUCE_NT non-temporal loads of the local reduce's and accumulation's sources
 //   ZS_STATS_PF request the next chunk's table entry before streaming the current chunk
