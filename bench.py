@@ -32,8 +32,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=30,
-                   help="untimed steps first; on the full state the step settles over its first ~30 "
-                        "back-to-back steps (about a second of streaming)")
+                   help="untimed steps first; on the full state a process's step time can shift once "
+                        "by about 0.5%% within its first ~30 back-to-back steps")
     p.add_argument("--config", default="full7p5b", choices=["tiny", "gpt2", "zero1_7p5b", "reduce8", "full7p5b"])
     p.add_argument("--rank", type=int, default=None, help="data-parallel rank whose shard is stepped")
     p.add_argument("--micro-steps", type=int, default=1,
