@@ -66,7 +66,8 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="also time the step captured into a HIP graph and replayed (after the timed steps)")
     p.add_argument("--no-cold-cache", action="store_true",
-                   help="skip the per-step timing after a cache-evicting write (after the timed steps)")
+                   help="skip the per-step timing after a cache-evicting read, and after a write "
+                        "(after the timed steps)")
     p.add_argument("--no-copy-ceiling", action="store_true",
                    help="skip the device-to-device copy measurement after the timed steps")
     p.add_argument("--copy-calibration", action="store_true",
